@@ -1,0 +1,172 @@
+"""fp64 CPU oracle for the Simple GLA mixer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  The product path (the HIP library and its Python
+binding) never imports, links or calls it, and this package imports nothing
+from the product.
+
+The arithmetic lives in ``gla_oracle.c`` (plain per-token recurrence in fp64,
+see its header for the passages of the Laplace 3B post it follows).  This
+module only builds that file with the host C compiler and marshals numpy
+arrays to it.
+
+Parity status of each function (what pins it is in tests/test_oracle.py):
+  fwd     pinned: lambda=1 causal linear attention, lambda=0 (q.k)v, the
+          quadratic decay-masked form, chunked == recurrent, split/resume.
+  bwd     pinned: central finite differences, fp64 autograd of the quadratic
+          form, and the (t+1)(q.dq - k.dk) identity for dlambda.
+  decode  pinned: k decode steps == forward over the same k tokens, and the
+          lambda=0 / lambda=1 closed forms.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgla_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = False) -> str:
+    """Compile gla_oracle.c into oracle/libgla_oracle.so with gcc + OpenMP."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(lib):
+    i = ctypes.c_int
+    lib.gla_oracle_fwd.argtypes = [i, i, i, i, i, _D, _D, _D, _D, _D,
+                                   ctypes.c_double, _D, _D, i]
+    lib.gla_oracle_bwd.argtypes = [i, i, i, i, i, _D, _D, _D, _D, _D,
+                                   ctypes.c_double, _D, _D, _D, _D, _D,
+                                   _D, _D, i]
+    lib.gla_oracle_decode.argtypes = [i, i, i, i, _D, _D, _D, _D, _D,
+                                      ctypes.c_double, _D, i]
+    for f in (lib.gla_oracle_fwd, lib.gla_oracle_bwd, lib.gla_oracle_decode):
+        f.restype = ctypes.c_int
+    lib.gla_oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+            ):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def compile_variant(src_text: str, out_path: str):
+    """Compile an edited copy of the oracle source (used by the tests that plant
+    a mistake in the oracle to show the pins catch it) and return its functions
+    as an object with fwd/bwd/decode methods."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                    "-o", out_path, src], check=True)
+    return _Variant(_bind(ctypes.CDLL(out_path)))
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _f64(x):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def max_threads() -> int:
+    return int(_load().gla_oracle_max_threads())
+
+
+def fwd(q, k, v, lam, S0=None, scale=1.0, nthreads=0, _lib_=None):
+    """q,k [B,T,H,dk], v [B,T,H,dv], lam [H] -> (o [B,T,H,dv], S_final [B,H,dk,dv])."""
+    q, k, v, lam, S0 = map(_f64, (q, k, v, lam, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    assert k.shape == q.shape and v.shape[:3] == (B, T, H) and lam.shape == (H,)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.zeros((B, T, H, dv))
+    S = np.zeros((B, H, dk, dv))
+    rc = (_lib_ or _load()).gla_oracle_fwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(lam),
+                                _p(S0), float(scale), _p(o), _p(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_fwd failed")
+    return o, S
+
+
+def bwd(q, k, v, lam, d_o, S0=None, dS_T=None, scale=1.0, nthreads=0, _lib_=None):
+    """Gradients of <do,o> + <dS_T,S_final>: returns dq, dk, dv, dlambda[H], dS0."""
+    q, k, v, lam, d_o, S0, dS_T = map(_f64, (q, k, v, lam, d_o, S0, dS_T))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    assert d_o.shape == v.shape
+    dq = np.zeros_like(q)
+    dkk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    dlam = np.zeros(H)
+    dS0 = np.zeros((B, H, dk, dv))
+    rc = (_lib_ or _load()).gla_oracle_bwd(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(lam),
+                                _p(S0), float(scale), _p(d_o), _p(dS_T), _p(dq),
+                                _p(dkk), _p(dvv), _p(dlam), _p(dS0), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_bwd failed")
+    return dq, dkk, dvv, dlam, dS0
+
+
+def decode(q, k, v, lam, S, scale=1.0, nthreads=0, _lib_=None):
+    """One decode step: q,k [N,H,dk], v [N,H,dv], S [N,H,dk,dv] -> (o, S_new)."""
+    q, k, v, lam = map(_f64, (q, k, v, lam))
+    S = np.array(S, dtype=np.float64, copy=True, order="C")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((N, H, dv))
+    rc = (_lib_ or _load()).gla_oracle_decode(N, H, dk, dv, _p(q), _p(k), _p(v), _p(lam),
+                                   _p(S), float(scale), _p(o), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_decode failed")
+    return o, S
+
+
+class _Variant:
+    def __init__(self, lib):
+        self.lib = lib
+
+    def fwd(self, *a, **kw):
+        return fwd(*a, _lib_=self.lib, **kw)
+
+    def bwd(self, *a, **kw):
+        return bwd(*a, _lib_=self.lib, **kw)
+
+    def decode(self, *a, **kw):
+        return decode(*a, _lib_=self.lib, **kw)
