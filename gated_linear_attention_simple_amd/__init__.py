@@ -1,0 +1,144 @@
+"""Python binding of libgla (include/gla.h): argument marshalling only.
+
+Every step of the mixer runs in the HIP kernels of libgla.so; this module only
+checks tensor metadata, allocates outputs/workspace with torch, and passes raw
+device pointers plus torch's current HIP stream through ctypes.  There is no
+fallback: if libgla.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgla.so")
+
+GLA_OK, GLA_ERR_INVALID_ARG, GLA_ERR_UNSUPPORTED, GLA_ERR_WORKSPACE, GLA_ERR_DEVICE = range(5)
+GLA_F32, GLA_BF16 = 0, 1
+
+SYMBOLS = (
+    "gla_abi_version",
+    "gla_status_str",
+    "gla_fwd_workspace_bytes",
+    "gla_fwd_chunked",
+    "gla_decode_step",
+)
+
+_lib = None
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+def load():
+    """Load libgla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgla.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.gla_abi_version.restype = i
+        lib.gla_status_str.restype = ctypes.c_char_p
+        lib.gla_status_str.argtypes = [i]
+        lib.gla_fwd_workspace_bytes.restype = sz
+        lib.gla_fwd_workspace_bytes.argtypes = [i] * 7
+        lib.gla_fwd_chunked.restype = i
+        lib.gla_fwd_chunked.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
+        lib.gla_decode_step.restype = i
+        lib.gla_decode_step.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, f, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load().gla_status_str(int(status)).decode()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    if t.dtype == torch.float32:
+        return GLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def fwd_workspace_bytes(dtype: int, B, T, H, dk, dv, chunk) -> int:
+    return int(load().gla_fwd_workspace_bytes(dtype, B, T, H, dk, dv, chunk))
+
+
+def fwd_chunked(q, k, v, lam, S0=None, scale=1.0, chunk=128, o=None, S_final=True,
+                workspace=None, stream=None):
+    """o, S_final = gla_fwd_chunked(...).  S_final=False skips the final state;
+    a tensor passed as `o`/`S_final` is written in place."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (B, T, H, dv), q.dtype, dev)
+    if S_final is True:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_final is False:
+        S_final = None
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    dt = _dt(q)
+    need = lib.gla_fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gla_fwd_chunked(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                             _ptr(S0), float(scale), _ptr(o), _ptr(S_final), _ptr(workspace),
+                             ws_bytes, _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_fwd_chunked")
+    return o, S_final
+
+
+def decode_step(q, k, v, lam, S, scale=1.0, o=None, stream=None):
+    """In place on S: S <- lam S + k v^T, o = scale S^T q.  Returns o."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    _check(q, "q", (N, H, dk), q.dtype, dev)
+    _check(k, "k", (N, H, dk), q.dtype, dev)
+    _check(v, "v", (N, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (N, H, dv), q.dtype, dev)
+    st = lib.gla_decode_step(_dt(q), N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S),
+                             float(scale), _ptr(o), _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_decode_step")
+    return o

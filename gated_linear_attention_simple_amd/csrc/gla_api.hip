@@ -1,0 +1,87 @@
+// gla_api.hip -- the extern "C" boundary of libgla (declared in include/gla.h).
+//
+// Host-side validation runs to completion before any HIP call, so an error
+// return enqueues nothing.  The library allocates nothing and keeps no state.
+#include "gla.h"
+#include "gla_internal.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+// gfx950 parts (MI350X / MI355X) have 256 compute units; the launch plan is
+// sized for that fixed count so workspace sizes never depend on a device query.
+constexpr int kPlanCUs = 256;
+constexpr long kMaxGridY = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+bool ok_dtype(int dt) { return dt == GLA_F32 || dt == GLA_BF16; }
+
+// Element counts must stay addressable; 2^40 elements is far above any HBM size.
+bool sane_count(long a, long b, long c, long d) {
+    const double n = (double)a * (double)b * (double)c * (double)d;
+    return n < 1.0e12;
+}
+
+int fwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    if (!ok_dtype(dtype) || B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(B, T, H, dk > dv ? dk : dv)) return GLA_ERR_INVALID_ARG;
+    if (!gla::fwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+    if ((long)B * H > kMaxGridY) return GLA_ERR_UNSUPPORTED;
+    return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return 1; }
+
+const char* gla_status_str(int status) {
+    switch (status) {
+        case GLA_OK: return "GLA_OK";
+        case GLA_ERR_INVALID_ARG: return "GLA_ERR_INVALID_ARG: null/misaligned pointer or invalid size";
+        case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: no kernel for this dtype/dk/dv/chunk";
+        case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
+        case GLA_ERR_DEVICE: return "GLA_ERR_DEVICE: HIP launch failed";
+        default: return "GLA_ERR_UNKNOWN";
+    }
+}
+
+size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
+    return gla::fwd_plan(B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
+}
+
+int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                    const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                    void* ws, size_t ws_bytes, void* stream) {
+    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (st != GLA_OK) return st;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
+    const gla::FwdPlan plan = gla::fwd_plan(B, T, H, dk, dv, chunk, kPlanCUs);
+    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
+                                           scale, o, S_final, ws, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_decode_step(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                    const float* lambda, float* S, float scale, void* o, void* stream) {
+    if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(N, H, dk, dv)) return GLA_ERR_INVALID_ARG;
+    if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
+    if ((long)N * H > 2147483647L) return GLA_ERR_UNSUPPORTED;
+    if (N == 0) return GLA_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(S) || !ok_ptr(o))
+        return GLA_ERR_INVALID_ARG;
+    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, scale, o,
+                                              static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// gla_decode.hip -- batched single-token decode step (one fused launch).
+//
+// Laplace 3B post, section "Optimizing inference on Trainium2": every sequence
+// owns one fixed state page that each decode step reads and writes; section
+// "GLA mixer": S <- lambda_h S + k v^T, then o = scale S^T q on the new state.
+//
+// The step moves 2 * dk * dv * 4 bytes of fp32 state per (sequence, head) and
+// does 4 * dk * dv flops on it (0.5 flop/byte), so it is bound by HBM: no
+// MFMA, just wide coalesced non-temporal loads/stores, fp32 FMAs, and an LDS
+// reduction of the per-thread column partial sums.
+//
+// One workgroup per (sequence, head).  Thread t owns float4 column group
+// cg = t % (DV/4) and rows r = rg, rg + RG, ... with rg = t / (DV/4); its
+// loads of one row sweep are contiguous across the workgroup.
+#include "gla_common.hpp"
+#include "gla_internal.hpp"
+
+namespace gla {
+
+template <typename E, int DK, int DV, int RG>
+__global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
+    int H, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ lambda, float* __restrict__ S, float scale, E* __restrict__ o) {
+    constexpr int NCG = DV / 4;          // float4 column groups per row
+    constexpr int NT = NCG * RG;         // threads
+    constexpr int RPT = DK / RG;         // rows per thread
+    static_assert(DK % RG == 0, "rows must split evenly");
+
+    __shared__ float qs[DK];
+    __shared__ float ks[DK];
+    __shared__ f32x4 part[RG][NCG];
+
+    const int unit = blockIdx.x;         // n * H + h
+    const int h = unit % H;
+    const int t = threadIdx.x;
+    const int cg = t % NCG;
+    const int rg = t / NCG;
+
+    for (int i = t; i < DK; i += NT) {
+        qs[i] = to_f32(q[(size_t)unit * DK + i]);
+        ks[i] = to_f32(k[(size_t)unit * DK + i]);
+    }
+    const float lam = lambda[h];
+    float vc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[(size_t)unit * DV + cg * 4 + e]);
+
+    f32x4* Sp = reinterpret_cast<f32x4*>(S + (size_t)unit * DK * DV);
+    f32x4 st[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + i * RG) * NCG + cg);
+    __syncthreads();
+
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        const float kr = ks[r], qr = qs[r];
+        f32x4 s = st[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[e] = fmaf(lam, s[e], kr * vc[e]);
+            acc[e] = fmaf(s[e], qr, acc[e]);
+        }
+        __builtin_nontemporal_store(s, Sp + (size_t)r * NCG + cg);
+    }
+    part[rg][cg] = acc;
+    __syncthreads();
+    for (int c = t; c < DV; c += NT) {
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < RG; ++j) sum += part[j][c / 4][c % 4];
+        o[(size_t)unit * DV + c] = from_f32<E>(scale * sum);
+    }
+}
+
+template <typename E, int DK, int DV, int RG>
+static hipError_t launch_decode_t(int N, int H, const void* q, const void* k, const void* v,
+                                  const float* lambda, float* S, float scale, void* o,
+                                  hipStream_t stream) {
+    const int units = N * H;
+    hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG>), dim3(units), dim3((DV / 4) * RG), 0, stream,
+                       H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+                       lambda, S, scale, static_cast<E*>(o));
+    return hipGetLastError();
+}
+
+bool decode_supported(int dk, int dv) {
+    return (dk == 96 && dv == 192) || (dk == 16 && dv == 32);
+}
+
+hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* lambda, float* S, float scale, void* o,
+                         hipStream_t stream) {
+    if (dk == 96 && dv == 192) {
+        return bf16_io ? launch_decode_t<bf16, 96, 192, 4>(N, H, q, k, v, lambda, S, scale, o, stream)
+                       : launch_decode_t<float, 96, 192, 4>(N, H, q, k, v, lambda, S, scale, o, stream);
+    }
+    return bf16_io ? launch_decode_t<bf16, 16, 32, 16>(N, H, q, k, v, lambda, S, scale, o, stream)
+                   : launch_decode_t<float, 16, 32, 16>(N, H, q, k, v, lambda, S, scale, o, stream);
+}
+
+}  // namespace gla

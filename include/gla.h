@@ -1,0 +1,118 @@
+/*
+ * gla.h -- C ABI of libgla, the MI355X (gfx950) Simple GLA mixer library.
+ *
+ * The method is the "GLA mixer" of the Laplace 3B post (AWS ML blog "Beyond the
+ * KV cache: training and serving i14's Laplace 3B linear attention model on
+ * AWS Trainium2 with native PyTorch"), section "i14 and the Laplace 3B
+ * architecture", paragraph "GLA mixer".  Per head h, with a fixed decay
+ * lambda_h shared by all sequences, a dk x dv matrix state evolves per token as
+ *       S_t = lambda_h * S_{t-1} + k_t v_t^T          (rank-1 write)
+ *       o_t = scale * S_t^T q_t                       (readout after the write)
+ * `scale` multiplies the readout only; the state never depends on it.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers (HIP global memory on the current
+ *   device); `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   Sizes are host ints.  The library never allocates or frees device memory:
+ *   the caller owns every buffer, including the workspace.
+ * - Layouts are dense row-major, last index fastest:
+ *     q, k  [B][T][H][dk]     v, o  [B][T][H][dv]      (token-major, as the fused
+ *                                                        QKVG projection emits them)
+ *     S0, S_final, dS_T, dS0   [B][H][dk][dv] fp32
+ *     lambda, dlambda          [H] fp32
+ * - dtype selects the element type of q, k, v, o, do, dq, dk, dv: GLA_F32 (fp32)
+ *   or GLA_BF16 (bfloat16).  States, lambda and every accumulation are fp32.
+ *   bf16 outputs are rounded to nearest even.
+ * - Supported shapes (instantiated kernels), (dk, dv, chunk):
+ *     bf16: (96, 192, 128), (96, 192, 64);   fp32: (96, 192, 64), (16, 32, 32);
+ *     decode, either dtype: (dk, dv) = (96, 192) or (16, 32).
+ *   Anything else returns GLA_ERR_UNSUPPORTED.  T need not be a multiple of
+ *   chunk (the last chunk is partial).
+ * - Validation is host-only and finishes before any HIP call: on any error
+ *   nothing is enqueued and no output is touched.  Pointers must be 16-byte
+ *   aligned.  lambda in [0, 1] is a precondition (device data is not read on
+ *   the host).  Outputs must not alias inputs (decode's S is in/out by design).
+ * - Calls are asynchronous: GLA_OK means "validated and enqueued on `stream`".
+ *   GLA_ERR_DEVICE reports a launch failure; device faults surface at the
+ *   caller's next synchronisation.  Results are deterministic (no float
+ *   atomics): the same inputs and sizes give the same bits, and a sequence's
+ *   bits do not depend on its position in the batch.  (The forward's launch
+ *   plan depends on B*H and T, so changing B may change rounding, not results
+ *   beyond it; decode is independent of N.)
+ * - No exception or abort crosses this ABI.  Calls are thread-safe.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GLA_OK = 0,
+    GLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, ... */
+    GLA_ERR_UNSUPPORTED = 2,   /* no kernel instantiated for (dtype, dk, dv, chunk) */
+    GLA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace_bytes */
+    GLA_ERR_DEVICE = 4         /* a HIP launch or query failed */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+/* Version of this ABI (bumped on any signature or semantic change). */
+int gla_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gla_status_str(int status);
+
+/*
+ * Workspace needed by gla_fwd_chunked for these sizes, in bytes (0 if none).
+ * The launch plan assumes the 256 compute units of gfx950 parts, so the size
+ * depends only on the arguments (no device query).
+ * Returns 0 as well for unsupported or invalid sizes; the call then reports it.
+ */
+size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+/*
+ * Chunked-parallel forward (Laplace 3B post, section "Challenge 1": per chunk
+ * of `chunk` tokens, a decay-masked causal linear attention inside the chunk
+ * plus the running state's contribution; the state then advances by the decay
+ * compounded over the chunk).  Equal, up to rounding, to the per-token
+ * recurrence above run from S0.
+ *   q, k, v     inputs (dtype), layouts above
+ *   lambda      [H] fp32 per-head decay
+ *   S0          optional initial state (NULL = zero)
+ *   scale       readout scale
+ *   o           output [B][T][H][dv] (dtype)
+ *   S_final     optional output: state after token T-1 (NULL = not written);
+ *               with T == 0 it receives S0 (or zeros)
+ *   ws, ws_bytes  caller-owned device workspace, at least
+ *               gla_fwd_workspace_bytes(...) bytes (may be NULL when that is 0)
+ */
+int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                    const void* q, const void* k, const void* v,
+                    const float* lambda, const float* S0, float scale,
+                    void* o, float* S_final,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Batched single-token decode step (Laplace 3B post, section "Optimizing
+ * inference on Trainium2": one fixed state page per sequence, read and written
+ * once per generated token).  For every sequence n and head h, in place:
+ *       S[n,h] <- lambda_h S[n,h] + k[n,h] v[n,h]^T ;  o[n,h] = scale S[n,h]^T q[n,h]
+ *   q, k   [N][H][dk] (dtype)      v, o  [N][H][dv] (dtype)
+ *   S      [N][H][dk][dv] fp32, updated in place (the sequence's state page)
+ * No workspace.  One kernel launch per call.
+ */
+int gla_decode_step(int dtype, int N, int H, int dk, int dv,
+                    const void* q, const void* k, const void* v,
+                    const float* lambda, float* S, float scale, void* o,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,87 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/gla.h declares, and rejects invalid arguments on the host before any
+HIP call (no device is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_attention_simple_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gla_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = gla.load()
+    decl = declared_functions()
+    assert "gla_fwd_chunked" in decl and "gla_decode_step" in decl
+    for name in decl:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(gla.SYMBOLS) <= set(decl)
+    assert lib.gla_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert gla.status_str(s).startswith("GLA_")
+    assert "UNKNOWN" in gla.status_str(99)
+
+
+P = ctypes.c_void_p(16)  # non-null, 16-byte aligned dummy (never dereferenced: validation fails first)
+MIS = ctypes.c_void_p(18)
+
+
+def fwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, o=P, Sf=None,
+        ws=None, wsb=0):
+    return gla.load().gla_fwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, o, Sf, ws, wsb, None)
+
+
+def test_fwd_rejects_bad_arguments_before_touching_the_device():
+    E = gla
+    assert fwd(dtype=7) == E.GLA_ERR_INVALID_ARG
+    assert fwd(B=0) == E.GLA_ERR_INVALID_ARG
+    assert fwd(T=-1) == E.GLA_ERR_INVALID_ARG
+    assert fwd(H=0) == E.GLA_ERR_INVALID_ARG
+    assert fwd(dk=64) == E.GLA_ERR_UNSUPPORTED
+    assert fwd(C=32) == E.GLA_ERR_UNSUPPORTED
+    assert fwd(dtype=0, C=128) == E.GLA_ERR_UNSUPPORTED          # fp32 stops at chunk 64
+    assert fwd(dtype=1, dk=16, dv=32, C=32) == E.GLA_ERR_UNSUPPORTED
+    assert fwd(q=None) == E.GLA_ERR_INVALID_ARG
+    assert fwd(v=MIS) == E.GLA_ERR_INVALID_ARG
+    assert fwd(lam=None) == E.GLA_ERR_INVALID_ARG
+    assert fwd(S0=MIS) == E.GLA_ERR_INVALID_ARG
+    assert fwd(B=70000, T=1) == E.GLA_ERR_UNSUPPORTED               # grid limit on B*H
+
+
+def test_fwd_workspace_contract():
+    lib = gla.load()
+    need = lib.gla_fwd_workspace_bytes(1, 1, 2048, 16, 96, 192, 128)
+    assert need > 0 and need % (96 * 192 * 4) == 0
+    assert fwd(T=2048) == gla.GLA_ERR_WORKSPACE
+    assert fwd(T=2048, ws=P, wsb=need - 1) == gla.GLA_ERR_WORKSPACE
+    assert lib.gla_fwd_workspace_bytes(1, 1, 2048, 16, 64, 192, 128) == 0   # unsupported -> 0
+    # a large batch fills the GPU without splitting the sequence: no workspace
+    assert lib.gla_fwd_workspace_bytes(1, 32, 2048, 16, 96, 192, 128) == 0
+
+
+def test_decode_rejects_bad_arguments():
+    lib = gla.load()
+    d = lambda dtype=1, N=4, H=16, dk=96, dv=192, q=P, S=P: lib.gla_decode_step(
+        dtype, N, H, dk, dv, q, P, P, P, S, 1.0, P, None)
+    assert d(dtype=5) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(dk=80) == gla.GLA_ERR_UNSUPPORTED
+    assert d(q=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(S=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=0, q=None) == gla.GLA_OK        # nothing to do, nothing enqueued
