@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the Simple GLA mixer hot path on one MI355X.
+
+A step is one pass of the hot path on synthetic inputs already resident in HBM:
+  * forward: one gla_fwd_chunked call on the Laplace-layer workload
+    (B=1, H=16, T=2048, dk=96, dv=192, chunk 128, bf16, fp32 state);
+  * decode: one decode step of the 1,280-sequence x 24-layer serving workload
+    (24 gla_decode_step launches over a 36 GB fp32 state pool).
+Each leg is timed over K steps after W warm-up steps, bracketed by device
+synchronisation; per-launch durations come from HIP events recorded on the
+stream the library launches on.  The headline value is forward tokens/s; the
+decode leg reports state-update GB/s and output tokens/s in the same line.
+
+The CPU baseline leg times the fp64 oracle on a bounded sample of the same
+workloads (rank 0, one GPU only).  Usage: python bench.py [--gpus 1] [--steps K]
+[--warmup W] [--no-cpu-baseline] [--counters]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "GLA chunked fwd tokens/s (H16,dk96,dv192,T2048) + decode GB/s at 1280 seqs"
+
+# Algorithmic work (per token-head for the forward, per sequence-head for decode)
+FWD_BYTES_PER_TOKEN_HEAD = {"bf16": 2 * 96 + 2 * 96 + 2 * 192 + 2 * 192, "f32": 4 * (96 + 96 + 192 + 192)}
+
+
+def fwd_flops_per_token_head(C, dk=96, dv=192):
+    """Tile-issued MFMA work: 2C(dk+dv) for QK^T and AV over a full CxC tile, plus 4 dk dv for QS and K^T V."""
+    return 2 * C * (dk + dv) + 4 * dk * dv
+
+
+DEC_BYTES_PER_SEQ_HEAD = 2 * 96 * 192 * 4 + 2 * (96 + 96 + 192 + 192)   # state R+W + q,k,v,o bf16
+DEC_FLOPS_PER_SEQ_HEAD = 4 * 96 * 192
+
+
+def src_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_linear_attention_simple_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, bytes_per_launch_alg: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get("kernels", {}).get(kernel)
+    if not rec or rec.get("src_digest") != src_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (debugging only)")
+    ap.add_argument("--counters", action="store_true",
+                    help="run a short fixed sequence (copy kernel + each hot kernel) for rocprofv3 --pmc")
+    ap.add_argument("--chunk", type=int, default=128)
+    return ap.parse_args()
+
+
+class FwdLeg:
+    """Pre-marshalled gla_fwd_chunked call on one workload (no per-call allocation)."""
+
+    def __init__(self, gla, gi, torch, w, seed, chunk):
+        self.torch = torch
+        dev = torch.device("cuda:0")
+        x = gi.fwd_inputs(w, dev, seed)
+        self.x = x
+        B, T, H, dk = x["q"].shape
+        dv = x["v"].shape[3]
+        self.tokens = B * T
+        self.token_heads = B * T * H
+        self.o = torch.empty((B, T, H, dv), dtype=x["q"].dtype, device=dev)
+        self.S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        dt = gla.GLA_BF16 if x["q"].dtype == torch.bfloat16 else gla.GLA_F32
+        need = gla.fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+        p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        self.fn = gla.load().gla_fwd_chunked
+        self.args = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]),
+                     p(x["S0"]), ctypes.c_float(x["scale"]), p(self.o), p(self.S), p(self.ws),
+                     ctypes.c_size_t(need), ctypes.c_void_p(self.stream.cuda_stream))
+        self.gla = gla
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"gla_fwd_chunked: {self.gla.status_str(st)}")
+
+
+class DecodeLeg:
+    """The 1,280-sequence x 24-layer decode workload with its fp32 state pool on the GPU."""
+
+    def __init__(self, gla, gi, torch, w, seed, n_inputs=4):
+        dev = torch.device("cuda:0")
+        self.torch = torch
+        self.w = w
+        L = w.decode_layers
+        self.pool = torch.empty((L, w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+        for layer in range(L):
+            gi.decode_state(w, dev, seed, layer, out=self.pool[layer])
+        self.inputs = [[gi.decode_token_inputs(w, dev, seed, layer, s) for s in range(n_inputs)]
+                       for layer in range(L)]
+        self.lam = torch.tensor(w.lambdas, dtype=torch.float32, device=dev)
+        self.o = torch.empty((w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.fn = gla.load().gla_decode_step
+        self.gla = gla
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.args = [[(gla.GLA_BF16, w.B, w.H, w.dk, w.dv, p(d["q"]), p(d["k"]), p(d["v"]), p(self.lam),
+                       p(self.pool[layer]), ctypes.c_float(w.scale), p(self.o),
+                       ctypes.c_void_p(self.stream.cuda_stream)) for d in self.inputs[layer]]
+                     for layer in range(L)]
+        self.layers = L
+        self.n_inputs = n_inputs
+
+    def launch(self, layer, step):
+        st = self.fn(*self.args[layer][step % self.n_inputs])
+        if st != 0:
+            raise RuntimeError(f"gla_decode_step: {self.gla.status_str(st)}")
+
+
+def time_fwd(torch, leg, K, W):
+    for _ in range(W):
+        leg()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(leg.stream)
+        leg()
+        b.record(leg.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    return wall, per
+
+
+def time_decode(torch, leg, K, W):
+    for s in range(W):
+        for layer in range(leg.layers):
+            leg.launch(layer, s)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(leg.layers)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for s in range(K):
+        for layer in range(leg.layers):
+            a, b = evs[s][layer]
+            a.record(leg.stream)
+            leg.launch(layer, W + s)
+            b.record(leg.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) * 1e-3 for row in evs for a, b in row]
+    return wall, per
+
+
+def cpu_baseline_fwd(gi, w, seed, budget_s=12.0):
+    """fp64 oracle on the same workload's inputs (drawn on the CPU), repeated until ~budget_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    x = gi.fwd_inputs(w, "cpu", seed)
+    f = lambda t: t.double().numpy()
+    q, k, v, lam = f(x["q"]), f(x["k"]), f(x["v"]), f(x["lam"])
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fwd(q, k, v, lam, scale=x["scale"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    tokens = reps * w.B * w.T
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 per-token recurrence, full Laplace-layer forward (B=1,H=16,T=2048) x {reps} "
+                      f"repetitions, {el:.1f} s, OpenMP over the 16 (batch, head) units"}
+
+
+def cpu_baseline_decode(gi, w, seed, budget_s=8.0):
+    import numpy as np
+
+    import oracle
+
+    n = 64
+    x = gi.decode_token_inputs(w, "cpu", seed, 0, 0, N=n)
+    S = gi.decode_state(w, "cpu", seed, 0, N=n).double().numpy()
+    f = lambda t: t.double().numpy()
+    q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
+    lam = np.array(w.lambdas)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        _, S = oracle.decode(q, k, v, lam, S, scale=w.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10000:
+            break
+    seq_heads = reps * n * w.H
+    return {"value": seq_heads * DEC_BYTES_PER_SEQ_HEAD / el / 1e9, "unit": "GB/s",
+            "tokens_per_s": reps * n / el / w.decode_layers, "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"fp64 decode steps of 64 sequences x 16 heads (one layer), {reps} steps in {el:.1f} s; "
+                      f"GB/s counts the fp32 workload's algorithmic bytes"}
+
+
+def counters_pass(torch, gla, gi, chunk):
+    """Fixed launch sequence for rocprofv3 --pmc: a 1 GiB device copy (calibration), then
+    3 forward calls and 3 decode launches on the bench workloads (decode at one layer)."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    ws = gi.workloads()
+    f = FwdLeg(gla, gi, torch, ws[1], 1, chunk)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    w4 = ws[4]
+    w1 = gi.Workload(w4.name, w4.B, w4.T, w4.H, w4.dk, w4.dv, 0, w4.dtype, w4.lambdas, w4.scale, w4.s0_var, 1)
+    d = DecodeLeg(gla, gi, torch, w1, 4, n_inputs=1)
+    for s in range(3):
+        d.launch(0, s)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_pass": "done", "copy_bytes_each": 2 * (1 << 30)}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the mixer's hot path is single-GPU here); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gated_linear_attention_simple_amd as gla
+    import gla_inputs as gi
+
+    gla.load()
+    if args.counters:
+        counters_pass(torch, gla, gi, args.chunk)
+        return
+    K, W = args.steps, args.warmup
+    ws = gi.workloads()
+
+    # ---- forward leg (Laplace layer)
+    w1 = ws[1]
+    fleg = FwdLeg(gla, gi, torch, w1, 1, args.chunk)
+    f_wall, f_per = time_fwd(torch, fleg, K, W)
+    f_ms = f_wall / K * 1e3
+    f_avg = sum(f_per) / len(f_per)
+    f_bytes = FWD_BYTES_PER_TOKEN_HEAD[w1.dtype] * fleg.token_heads
+    f_flops = fwd_flops_per_token_head(args.chunk) * fleg.token_heads
+    f_ach = f_bytes / f_avg / 1e9
+    fwd_tokens_per_s = K * fleg.tokens / f_wall
+
+    result = {
+        "metric": METRIC, "value": fwd_tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "laplace-layer-fwd B=1 H=16 T=2048 dk=96 dv=192 C=%d bf16 + "
+                               "decode 1280 seqs x 24 layers x H=16 fp32 state" % args.chunk,
+                   "global_batch": 1, "seq_len": 2048, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": f_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": f_ach / HBM_PEAK_GBS, "traffic": stored_traffic("fwd", f_bytes),
+                     "kernel": "gla_fwd_chunked (segment prologue + main)",
+                     "alg_bytes_per_launch": f_bytes, "avg_launch_us": f_avg * 1e6,
+                     "mfma_tflops": f_flops / f_avg / 1e12,
+                     "mfma_frac": f_flops / f_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "fwd": {"ms_per_call_wall": f_ms, "avg_launch_us": f_avg * 1e6, "min_launch_us": min(f_per) * 1e6},
+    }
+
+    # ---- decode leg (1,280 sequences x 24 layers)
+    d_ms = 0.0
+    if not args.no_decode:
+        w4 = ws[4]
+        dleg = DecodeLeg(gla, gi, torch, w4, 4)
+        d_wall, d_per = time_decode(torch, dleg, K, W)
+        d_ms = d_wall / K * 1e3
+        per_launch_bytes = DEC_BYTES_PER_SEQ_HEAD * w4.B * w4.H
+        d_avg = sum(d_per) / len(d_per)
+        d_ach = per_launch_bytes / d_avg / 1e9
+        result["decode"] = {
+            "value": per_launch_bytes * w4.decode_layers * K / d_wall / 1e9, "unit": "GB/s",
+            "tokens_per_s": w4.B * K / d_wall, "ms_per_step": d_ms,
+            "launches_per_step": w4.decode_layers,
+            "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_ach / HBM_PEAK_GBS,
+                         "traffic": stored_traffic("decode", per_launch_bytes),
+                         "kernel": "gla_decode_step", "alg_bytes_per_launch": per_launch_bytes,
+                         "avg_launch_us": d_avg * 1e6},
+        }
+        del dleg
+        torch.cuda.empty_cache()
+    result["ms_per_step"] = f_ms + d_ms
+
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline_fwd(gi, w1, 1)
+        result["cpu_baseline"] = cb
+        if not args.no_decode:
+            result["decode"]["cpu_baseline"] = cpu_baseline_decode(gi, ws[4], 4)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
