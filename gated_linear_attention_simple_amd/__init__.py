@@ -23,6 +23,8 @@ SYMBOLS = (
     "gla_status_str",
     "gla_fwd_workspace_bytes",
     "gla_fwd_chunked",
+    "gla_bwd_workspace_bytes",
+    "gla_bwd_chunked",
     "gla_decode_step",
 )
 
@@ -50,6 +52,10 @@ def load():
         lib.gla_fwd_workspace_bytes.argtypes = [i] * 7
         lib.gla_fwd_chunked.restype = i
         lib.gla_fwd_chunked.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
+        lib.gla_bwd_workspace_bytes.restype = sz
+        lib.gla_bwd_workspace_bytes.argtypes = [i] * 7
+        lib.gla_bwd_chunked.restype = i
+        lib.gla_bwd_chunked.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.gla_decode_step.restype = i
         lib.gla_decode_step.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, f, vp, vp]
         _lib = lib
@@ -121,6 +127,43 @@ def fwd_chunked(q, k, v, lam, S0=None, scale=1.0, chunk=128, o=None, S_final=Tru
     if st != GLA_OK:
         raise GlaError(st, "gla_fwd_chunked")
     return o, S_final
+
+
+def bwd_workspace_bytes(dtype: int, B, T, H, dk, dv, chunk) -> int:
+    return int(load().gla_bwd_workspace_bytes(dtype, B, T, H, dk, dv, chunk))
+
+
+def bwd_chunked(q, k, v, lam, d_o, S0=None, dS_final=None, scale=1.0, chunk=128,
+                dlambda=True, dS0=True, workspace=None, stream=None):
+    """dq, dk, dv, dlambda ([H] or None), dS0 ([B,H,dk,dv] or None) = gla_bwd_chunked(...)."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(d_o, "do", (B, T, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    for t, name in ((S0, "S0"), (dS_final, "dS_final")):
+        if t is not None:
+            _check(t, name, (B, H, dk, dv), torch.float32, dev)
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dl = torch.empty(H, dtype=torch.float32, device=dev) if dlambda else None
+    ds0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if dS0 else None
+    dt = _dt(q)
+    need = lib.gla_bwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gla_bwd_chunked(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S0),
+                             float(scale), _ptr(d_o), _ptr(dS_final), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                             _ptr(dl), _ptr(ds0), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_bwd_chunked")
+    return dq, dkk, dvv, dl, ds0
 
 
 def decode_step(q, k, v, lam, S, scale=1.0, o=None, stream=None):

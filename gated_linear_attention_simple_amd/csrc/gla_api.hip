@@ -33,6 +33,14 @@ int fwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     return GLA_OK;
 }
 
+int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    if (!ok_dtype(dtype) || B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(B, T, H, dk > dv ? dk : dv)) return GLA_ERR_INVALID_ARG;
+    if (!gla::bwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+    if ((long)B * H > kMaxGridY) return GLA_ERR_UNSUPPORTED;
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +75,29 @@ int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, c
     if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
     const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
                                            scale, o, S_final, ws, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+size_t gla_bwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    if (bwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
+    return gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
+}
+
+int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                    const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
+                    const float* dS_final, void* dq, void* dk_out, void* dv_out, float* dlambda, float* dS0,
+                    void* ws, size_t ws_bytes, void* stream) {
+    int st = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (st != GLA_OK) return st;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(d_o) || !ok_ptr(dq) ||
+                  !ok_ptr(dk_out) || !ok_ptr(dv_out)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(dS_final) || !ok_opt(dlambda) || !ok_opt(dS0)) return GLA_ERR_INVALID_ARG;
+    const gla::BwdPlan plan = gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
+    if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    const hipError_t err =
+        gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final,
+                        dq, dk_out, dv_out, dlambda, dS0, ws, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 

@@ -1,0 +1,774 @@
+// gla_bwd.hip -- chunked GLA backward on gfx950 MFMA.
+//
+// Gradients of a scalar loss L with upstream do = dL/do and dS_T = dL/dS_final
+// through the recurrence S_t = lam S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t
+// (Laplace 3B post, section "GLA mixer"), regrouped by chunks as in section
+// "Challenge 1" and the backward through the sequential chunk chain of
+// section "Challenge 3".  For chunk c with start state Sbar = S_{c-1},
+// end-of-chunk state gradient Gbar = dL/dS_c (from later chunks and dS_T),
+// chunk-local positions i, j < C and b_i = lam^(i+1), c_j = lam^(C-1-j),
+// D_ij = lam^(i-j) (i >= j), Lam = lam^C:
+//   dP   = (dO V^T) (.) D,   Abar = (Q K^T) (.) D
+//   dQ   = scale (dP K + diag(b) dO Sbar^T)
+//   dK   = scale dP^T Q + diag(c) V Gbar^T
+//   dV   = scale Abar^T dO + diag(c) K Gbar
+//   dS_{c-1} = Lam Gbar + scale Q^T diag(b) dO       (the chain, run in reverse)
+//   dlam = sum over chunks of
+//          Lam' <Gbar, Sbar> + sum_j c'_j k_j^T Gbar v_j
+//        + scale sum_i b'_i q_i^T Sbar do_i + scale sum_{i>j} D'_ij (q_i.k_j)(do_i.v_j)
+// where ' is d/dlam of the decay factor (n lam^(n-1) for lam^n): the chunk's
+// explicit dependence on lam, with Sbar held fixed; summed over chunks and the
+// batch this is the total derivative.  A partial last chunk uses its length.
+//
+// Launches (one stream):
+//   1-3  forward state pass: per-chunk start states Sbar_c (segment prologue,
+//        scan, emit pass -- the forward's segment scheme);
+//   4-6  reverse state pass: per-chunk Gbar_c, dS0 and the <Gbar, Sbar> term;
+//   7    dK/dV per (chunk, 64-key tile), looping over the chunk's query tiles;
+//   8    dQ per (chunk, 64-query tile), looping over the chunk's key tiles;
+//   9    deterministic sum of the dlam partials per head.
+// Snapshots are stored in the input dtype (they are MFMA operands); the chains
+// themselves accumulate in fp32 registers.
+#include "gla_common.hpp"
+#include "gla_internal.hpp"
+#include "gla_tile.hpp"
+
+namespace gla {
+
+constexpr int kNPart = 8;  // dlam partial slots per (batch*head, chunk)
+
+// ---------------------------------------------------------------- state passes
+
+struct StateArgs {
+    int T, H;
+    const void* x;        // [B][T][H][DK]: keys (forward pass) or queries (reverse pass)
+    const void* y;        // [B][T][H][DV]: values (forward pass) or output gradients (reverse pass)
+    const float* lambda;
+    float xscale;         // extra row factor on x: 1 (forward) or the readout scale (reverse)
+    const float* S_edge;  // state entering the pass: S0 (forward) or dS_T (reverse); nullable
+    float* U;             // [BH][nseg-1][DK][DV]: segment-local states, then segment start states
+    void* snap;           // [BH][NC][DK][DV] (E): per-chunk snapshots written by the emit pass
+    float* S_out;         // reverse emit pass: dS0 (nullable)
+    const void* sbar;     // reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
+    float* part;          // reverse emit pass: dlam partials, slot 0
+    int nseg, seg_chunks, nc;
+};
+
+// One workgroup runs one (batch*head, segment) of the chain
+//   forward:  S <- lam^ceff S + (diag(lam^(ceff-1-j)) K)^T V    over chunks upward
+//   reverse:  G <- lam^ceff G + (diag(scale lam^(i+1)) Q)^T dO  over chunks downward
+// LOCAL passes start from zero and write the segment's local result to U; EMIT
+// passes start from the scanned segment start state and write, before each
+// chunk's update, the state as that chunk's snapshot.
+template <typename E, int DK, int DV, int C, int NW, bool REV, bool EMIT>
+__global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
+    constexpr bool BF = sizeof(E) == 2;
+    constexpr int NT = NW * 64;
+    constexpr int NCW = DV / NW, NCB = NCW / 16, NDB = DK / 16;
+    constexpr int PAD = BF ? 8 : 4;
+    constexpr int LDK = DK + PAD, LDV = DV + PAD;
+    constexpr int NP = BF ? C / 32 : 1;
+    __shared__ __align__(16) E Xc[C * LDK];
+    __shared__ __align__(16) E Ys[C * LDV];
+    __shared__ float pw[C + 1];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int seg = blockIdx.x + ((!EMIT && REV) ? 1 : 0);
+    const int bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int h = bh % H, b = bh / H;
+    const int c_begin = seg * a.seg_chunks;
+    const int c_end = min(a.nc, c_begin + a.seg_chunks);
+    const int colbase = wave * NCW;
+    const float lam = a.lambda[h];
+    for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
+
+    const size_t tokX = (size_t)H * DK, tokY = (size_t)H * DV;
+    const size_t tok0 = (size_t)b * T * H + h;
+    const E* xb = static_cast<const E*>(a.x) + tok0 * DK;
+    const E* yb = static_cast<const E*>(a.y) + tok0 * DV;
+
+    f32x4 Sacc[NDB][NCB];  // Sacc[db][cb][r] = S[db*16 + 4g + r][colbase + cb*16 + n]
+    auto sidx = [&](int db, int cb, int r) -> size_t {
+        return (size_t)(db * 16 + 4 * g + r) * DV + colbase + cb * 16 + n;
+    };
+    const float* Sin = nullptr;
+    if constexpr (EMIT) {
+        if (!REV) Sin = seg == 0 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg - 1) * DK * DV;
+        else Sin = seg == a.nseg - 1 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg) * DK * DV;
+        if (Sin && Sin == a.S_edge) Sin += (size_t)bh * DK * DV;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[db][cb][r] = Sin ? Sin[sidx(db, cb, r)] : 0.f;
+
+    TileStage<E, C, DK, NT> tx;
+    TileStage<E, C, DV, NT> ty;
+    const int nchunks = c_end - c_begin;
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int c = REV ? c_end - 1 - ci : c_begin + ci;
+        const int t0 = c * C;
+        const int ceff = min(C, T - t0);
+        tx.load(xb + (size_t)t0 * tokX, tokX, ceff, tid);
+        ty.load(yb + (size_t)t0 * tokY, tokY, ceff, tid);
+        __syncthreads();  // previous chunk's LDS reads are done (and pw is visible)
+        tx.template store_scaled<LDK>(Xc, tid, [&](int row) {
+            if (row >= ceff) return 0.f;
+            return REV ? a.xscale * pw[row + 1] : pw[ceff - 1 - row];
+        });
+        ty.template store<LDV>(Ys, tid);
+        __syncthreads();
+
+        if constexpr (EMIT) {
+            E* snap = static_cast<E*>(a.snap) + ((size_t)bh * a.nc + c) * DK * DV;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) snap[sidx(db, cb, r)] = from_f32<E>(Sacc[db][cb][r]);
+            if constexpr (REV) {
+                // <Gbar_c, Sbar_c> weighted by d(lam^ceff)/dlam = ceff lam^(ceff-1)
+                const E* sb = static_cast<const E*>(a.sbar) + ((size_t)bh * a.nc + c) * DK * DV;
+                float acc = 0.f;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc = fmaf(Sacc[db][cb][r], to_f32(sb[sidx(db, cb, r)]), acc);
+                acc = wave_sum(acc);
+                if (lane == 0) red[wave] = acc;
+                __syncthreads();
+                if (tid == 0) {
+                    float s = 0.f;
+                    for (int w = 0; w < NW; ++w) s += red[w];
+                    a.part[((size_t)bh * a.nc + c) * kNPart] = (float)ceff * pw[ceff - 1] * s;
+                }
+            }
+        }
+
+        const float Lam = pw[ceff];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[db][cb][r] *= Lam;
+        if constexpr (BF) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                bf16x8 yop[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) yop[cb] = op_col8(Ys, LDV, 32 * p, colbase + cb * 16, n, g);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 xop = op_col8(Xc, LDK, 32 * p, db * 16, n, g);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) Sacc[db][cb] = mfma(xop, yop[cb], Sacc[db][cb]);
+                }
+            }
+        } else {
+#pragma unroll 2
+            for (int p = 0; p < C / 4; ++p)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        Sacc[db][cb] = mfma(Xc[(4 * p + g) * LDK + db * 16 + n],
+                                            Ys[(4 * p + g) * LDV + colbase + cb * 16 + n], Sacc[db][cb]);
+        }
+    }
+
+    float* dst = nullptr;
+    if (!EMIT) dst = a.U + ((size_t)bh * (a.nseg - 1) + (REV ? seg - 1 : seg)) * DK * DV;
+    else if (REV && seg == 0 && a.S_out) dst = a.S_out + (size_t)bh * DK * DV;
+    if (dst) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[sidx(db, cb, r)] = Sacc[db][cb][r];
+    }
+}
+
+// Reverse segment scan: slot s-1 holds the local reverse state dU_s of segment
+// s (from zero at its end), s = 1..nseg-1.  In place it becomes the state
+// gradient at the end of segment s-1:
+//   G_end(nseg-1) = dS_T,   G_end(s-1) = lam^(L_s) G_end(s) + dU_s,
+// with L_s the token count of segment s (the last one may be short).
+__global__ __launch_bounds__(256) void rev_scan_kernel(const float* __restrict__ dST, float* __restrict__ U,
+                                                       const float* __restrict__ lambda, int H, int nseg,
+                                                       int seg_tokens, int T, int dkdv) {
+    const int bh = blockIdx.y;
+    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 * 4 >= dkdv) return;
+    const float lam = lambda[bh % H];
+    f32x4 run = dST ? *reinterpret_cast<const f32x4*>(dST + (size_t)bh * dkdv + 4 * e4) : zero4();
+    f32x4* u = reinterpret_cast<f32x4*>(U + (size_t)bh * (nseg - 1) * dkdv) + e4;
+    const size_t step = (size_t)dkdv / 4;
+    f32x4 x[kMaxSegments - 1];
+#pragma unroll
+    for (int s = 0; s < kMaxSegments - 1; ++s)
+        if (s < nseg - 1) x[s] = u[s * step];
+#pragma unroll
+    for (int s = kMaxSegments - 1; s >= 1; --s) {
+        if (s <= nseg - 1) {
+            const int Ls = min(seg_tokens, T - s * seg_tokens);
+            const float f = pow_int(lam, Ls);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) run[e] = fmaf(f, run[e], x[s - 1][e]);
+            u[(s - 1) * step] = run;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- gradient kernels
+
+struct GradArgs {
+    int T, H;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* d_o;
+    const float* lambda;
+    float scale;
+    const void* sbar;  // [BH][NC][DK][DV] (E): chunk start states
+    const void* gbar;  // [BH][NC][DK][DV] (E): chunk end state gradients
+    void* dq;
+    void* dk;
+    void* dv;
+    float* part;       // [BH][NC][kNPart]
+    int nc;
+};
+
+template <typename E, int DK, int DV, int C>
+struct GradShape {
+    static constexpr bool BF = sizeof(E) == 2;
+    static constexpr int ST = C > 64 ? 64 : C;  // token tile
+    static constexpr int NSUB = C / ST;
+    static constexpr int NW = ST / 16;          // one 16-token block per wave
+    static constexpr int NT = NW * 64;
+    static constexpr int PAD = BF ? 8 : 4;
+    static constexpr int LDK = DK + PAD, LDV = DV + PAD;
+    static constexpr int NDB = DK / 16, NVB = DV / 16;
+    static constexpr int NPAIR = BF ? ST / 32 : ST / 16;  // k-steps of the tile (pairs of blocks for bf16)
+    static_assert(1 + 2 * NSUB <= kNPart, "partial slots");
+};
+
+// Decay factor and its lam-derivative for a non-negative distance d:
+// lam^d and d lam^(d-1) (0 for d = 0).
+__device__ __forceinline__ void decay_pair(const float* pw, int d, float& f, float& df) {
+    f = d >= 0 ? pw[d] : 0.f;
+    df = d >= 1 ? (float)d * pw[d - 1] : 0.f;
+}
+
+__device__ __forceinline__ void block_partial(float x, float* red, int nw, float* dst) {
+    const int tid = threadIdx.x;
+    x = wave_sum(x);
+    if ((tid & 63) == 0) red[tid >> 6] = x;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += red[w];
+        *dst = s;
+    }
+}
+
+// dK, dV of one 64-key tile (jt) of one chunk; wave w owns key block w.
+template <typename E, int DK, int DV, int C>
+__global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dkdv_kernel(GradArgs a) {
+    using G = GradShape<E, DK, DV, C>;
+    constexpr bool BF = G::BF;
+    constexpr int ST = G::ST, NSUB = G::NSUB, NW = G::NW, NT = G::NT;
+    constexpr int LDK = G::LDK, LDV = G::LDV, NDB = G::NDB, NVB = G::NVB;
+    __shared__ __align__(16) E Ks[ST * LDK];
+    __shared__ __align__(16) E Vs[ST * LDV];
+    __shared__ __align__(16) E Qs[ST * LDK];
+    __shared__ __align__(16) E Ds[ST * LDV];
+    __shared__ __align__(16) E Gs[DK * LDV];
+    __shared__ float pw[C + 1];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int cid = blockIdx.x / NSUB, jt = blockIdx.x % NSUB, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int h = bh % H, b = bh / H;
+    const int t0 = cid * C;
+    const int ceff = min(C, T - t0);
+    const int kt0 = jt * ST;  // chunk-local first key of the tile
+    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + 1 + jt;
+    if (kt0 >= ceff) {
+        if (tid == 0) *part = 0.f;
+        return;
+    }
+    const float lam = a.lambda[h];
+    for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
+
+    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
+    const size_t tok0 = (size_t)b * T * H + h;
+    const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
+    const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
+    const E* vb = static_cast<const E*>(a.v) + tok0 * DV;
+    const E* db_ = static_cast<const E*>(a.d_o) + tok0 * DV;
+    {
+        TileStage<E, ST, DK, NT> tk;
+        TileStage<E, ST, DV, NT> tv;
+        TileStage<E, DK, DV, NT> tg;
+        tk.load(kb + (size_t)(t0 + kt0) * tokK, tokK, ceff - kt0, tid);
+        tv.load(vb + (size_t)(t0 + kt0) * tokV, tokV, ceff - kt0, tid);
+        tg.load(static_cast<const E*>(a.gbar) + ((size_t)bh * a.nc + cid) * DK * DV, DV, DK, tid);
+        tk.template store<LDK>(Ks, tid);
+        tv.template store<LDV>(Vs, tid);
+        tg.template store<LDV>(Gs, tid);
+    }
+    __syncthreads();
+
+    const int jb = wave;
+    const int jl = kt0 + jb * 16 + n;  // chunk-local key index of this lane's column
+    const float cj = jl < ceff ? pw[ceff - 1 - jl] : 0.f;
+    const float dcj = (jl < ceff && ceff - 2 - jl >= 0) ? (float)(ceff - 1 - jl) * pw[ceff - 2 - jl] : 0.f;
+
+    // Inter-chunk terms.  dK^T[d][j] = c_j sum_c Gbar[d][c] v_j[c];
+    // dV^T[c][j] = c_j X[c][j], X = sum_d Gbar[d][c] k_j[d]; c'_j v_j . X_j feeds dlam.
+    f32x4 dKT[NDB], dVT[NVB];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+        dKT[d] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int p = 0; p < DV / 32; ++p)
+                dKT[d] = mfma(op_row8(Gs, LDV, d * 16 + n, 32 * p + 8 * g), op_row8(Vs, LDV, jb * 16 + n, 32 * p + 8 * g),
+                              dKT[d]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < DV / 4; ++p)
+                dKT[d] = mfma(Gs[(d * 16 + n) * LDV + 4 * p + g], Vs[(jb * 16 + n) * LDV + 4 * p + g], dKT[d]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dKT[d][r] *= cj;
+    }
+    float t2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < NVB; ++c) {
+        dVT[c] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int p = 0; p < DK / 32; ++p)
+                dVT[c] = mfma(op_col8(Gs, LDV, 32 * p, c * 16, n, g), op_row8(Ks, LDK, jb * 16 + n, 32 * p + 8 * g),
+                              dVT[c]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < DK / 4; ++p)
+                dVT[c] = mfma(Gs[(4 * p + g) * LDV + c * 16 + n], Ks[(jb * 16 + n) * LDK + 4 * p + g], dVT[c]);
+        }
+        const f32x4 vj = load4<E>(Vs + (jb * 16 + n) * LDV + c * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            t2 = fmaf(dcj * vj[r], dVT[c][r], t2);
+            dVT[c][r] *= cj;
+        }
+    }
+
+    // Intra-chunk terms over the query tiles at or after this key tile.
+    float t4 = 0.f;
+    for (int it = jt; it < NSUB; ++it) {
+        const int qt0 = it * ST;
+        if (qt0 >= ceff) break;
+        {
+            TileStage<E, ST, DK, NT> tq;
+            TileStage<E, ST, DV, NT> td;
+            tq.load(qb + (size_t)(t0 + qt0) * tokK, tokK, ceff - qt0, tid);
+            td.load(db_ + (size_t)(t0 + qt0) * tokV, tokV, ceff - qt0, tid);
+            __syncthreads();  // previous tile's reads of Qs / Ds are done
+            tq.template store<LDK>(Qs, tid);
+            td.template store<LDV>(Ds, tid);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pr = 0; pr < G::NPAIR; ++pr) {
+            constexpr int BPP = BF ? 2 : 1;  // query blocks per k-step
+            f32x4 Ab[BPP], Pb[BPP];
+#pragma unroll
+            for (int u = 0; u < BPP; ++u) {
+                const int ib = pr * BPP + u;
+                const int il0 = qt0 + ib * 16;  // chunk-local first query of the block
+                Ab[u] = zero4();
+                Pb[u] = zero4();
+                if (il0 + 15 < kt0 + jb * 16) continue;  // block entirely above the diagonal
+                if constexpr (BF) {
+#pragma unroll
+                    for (int p = 0; p < DK / 32; ++p)
+                        Ab[u] = mfma(op_row8(Qs, LDK, ib * 16 + n, 32 * p + 8 * g),
+                                     op_row8(Ks, LDK, jb * 16 + n, 32 * p + 8 * g), Ab[u]);
+#pragma unroll
+                    for (int p = 0; p < DV / 32; ++p)
+                        Pb[u] = mfma(op_row8(Ds, LDV, ib * 16 + n, 32 * p + 8 * g),
+                                     op_row8(Vs, LDV, jb * 16 + n, 32 * p + 8 * g), Pb[u]);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < DK / 4; ++p)
+                        Ab[u] = mfma(Qs[(ib * 16 + n) * LDK + 4 * p + g], Ks[(jb * 16 + n) * LDK + 4 * p + g], Ab[u]);
+#pragma unroll
+                    for (int p = 0; p < DV / 4; ++p)
+                        Pb[u] = mfma(Ds[(ib * 16 + n) * LDV + 4 * p + g], Vs[(jb * 16 + n) * LDV + 4 * p + g], Pb[u]);
+                }
+                // Ab[u][r] = q_i . k_j, Pb[u][r] = do_i . v_j for i = il0 + 4g + r, j = jl
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float f, df;
+                    decay_pair(pw, il0 + 4 * g + r - jl, f, df);
+                    t4 = fmaf(df * Ab[u][r], Pb[u][r], t4);
+                    Ab[u][r] *= a.scale * f;
+                    Pb[u][r] *= a.scale * f;
+                }
+            }
+            if constexpr (BF) {
+                const bf16x8 ab = pack_acc(Ab[0], Ab[1]);
+                const bf16x8 pb = pack_acc(Pb[0], Pb[1]);
+#pragma unroll
+                for (int c = 0; c < NVB; ++c) dVT[c] = mfma(op_col_pair(Ds, LDV, 32 * pr, c * 16, n, g), ab, dVT[c]);
+#pragma unroll
+                for (int d = 0; d < NDB; ++d) dKT[d] = mfma(op_col_pair(Qs, LDK, 32 * pr, d * 16, n, g), pb, dKT[d]);
+            } else {
+                const int ib = pr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                    for (int c = 0; c < NVB; ++c)
+                        dVT[c] = mfma(Ds[(ib * 16 + 4 * g + r) * LDV + c * 16 + n], Ab[0][r], dVT[c]);
+#pragma unroll
+                    for (int d = 0; d < NDB; ++d)
+                        dKT[d] = mfma(Qs[(ib * 16 + 4 * g + r) * LDK + d * 16 + n], Pb[0][r], dKT[d]);
+                }
+            }
+        }
+    }
+
+    if (jl < ceff) {
+        E* dkr = static_cast<E*>(a.dk) + tok0 * DK + (size_t)(t0 + jl) * tokK;
+        E* dvr = static_cast<E*>(a.dv) + tok0 * DV + (size_t)(t0 + jl) * tokV;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) store4<E>(dkr + d * 16 + 4 * g, dKT[d]);
+#pragma unroll
+        for (int c = 0; c < NVB; ++c) store4<E>(dvr + c * 16 + 4 * g, dVT[c]);
+    }
+    block_partial(t2 + a.scale * t4, red, NW, part);
+}
+
+// dQ of one 64-query tile (it) of one chunk; wave w owns query block w.
+template <typename E, int DK, int DV, int C>
+__global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(GradArgs a) {
+    using G = GradShape<E, DK, DV, C>;
+    constexpr bool BF = G::BF;
+    constexpr int ST = G::ST, NSUB = G::NSUB, NW = G::NW, NT = G::NT;
+    constexpr int LDK = G::LDK, LDV = G::LDV, NDB = G::NDB;
+    __shared__ __align__(16) E Qs[ST * LDK];
+    __shared__ __align__(16) E Ds[ST * LDV];
+    __shared__ __align__(16) E Ks[ST * LDK];
+    __shared__ __align__(16) E Vs[ST * LDV];
+    __shared__ __align__(16) E Ss[DK * LDV];
+    __shared__ float pw[C + 1];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int cid = blockIdx.x / NSUB, it = blockIdx.x % NSUB, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int h = bh % H, b = bh / H;
+    const int t0 = cid * C;
+    const int ceff = min(C, T - t0);
+    const int qt0 = it * ST;
+    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + 1 + NSUB + it;
+    if (qt0 >= ceff) {
+        if (tid == 0) *part = 0.f;
+        return;
+    }
+    const float lam = a.lambda[h];
+    for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
+
+    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
+    const size_t tok0 = (size_t)b * T * H + h;
+    const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
+    const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
+    const E* vb = static_cast<const E*>(a.v) + tok0 * DV;
+    const E* db_ = static_cast<const E*>(a.d_o) + tok0 * DV;
+    {
+        TileStage<E, ST, DK, NT> tq;
+        TileStage<E, ST, DV, NT> td;
+        TileStage<E, DK, DV, NT> ts;
+        tq.load(qb + (size_t)(t0 + qt0) * tokK, tokK, ceff - qt0, tid);
+        td.load(db_ + (size_t)(t0 + qt0) * tokV, tokV, ceff - qt0, tid);
+        ts.load(static_cast<const E*>(a.sbar) + ((size_t)bh * a.nc + cid) * DK * DV, DV, DK, tid);
+        tq.template store<LDK>(Qs, tid);
+        td.template store<LDV>(Ds, tid);
+        ts.template store<LDV>(Ss, tid);
+    }
+    __syncthreads();
+
+    const int ib = wave;
+    const int il = qt0 + ib * 16 + n;  // chunk-local query index of this lane's column
+    const float bi = pw[il + 1];
+    const float dbi = (float)(il + 1) * pw[il];
+
+    // Inter-chunk term: Y^T[d][i] = sum_c Sbar[d][c] do_i[c]; dQ += scale b_i Y; scale b'_i q_i . Y_i feeds dlam.
+    f32x4 dQT[NDB];
+    float t3 = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+        dQT[d] = zero4();
+        if constexpr (BF) {
+#pragma unroll
+            for (int p = 0; p < DV / 32; ++p)
+                dQT[d] = mfma(op_row8(Ss, LDV, d * 16 + n, 32 * p + 8 * g), op_row8(Ds, LDV, ib * 16 + n, 32 * p + 8 * g),
+                              dQT[d]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < DV / 4; ++p)
+                dQT[d] = mfma(Ss[(d * 16 + n) * LDV + 4 * p + g], Ds[(ib * 16 + n) * LDV + 4 * p + g], dQT[d]);
+        }
+        const f32x4 qi = load4<E>(Qs + (ib * 16 + n) * LDK + d * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            t3 = fmaf(dbi * qi[r], dQT[d][r], t3);
+            dQT[d][r] *= a.scale * bi;
+        }
+    }
+
+    // Intra-chunk term over the key tiles at or before this query tile.
+    for (int jt = 0; jt <= it; ++jt) {
+        const int kt0 = jt * ST;
+        {
+            TileStage<E, ST, DK, NT> tk;
+            TileStage<E, ST, DV, NT> tv;
+            tk.load(kb + (size_t)(t0 + kt0) * tokK, tokK, ceff - kt0, tid);
+            tv.load(vb + (size_t)(t0 + kt0) * tokV, tokV, ceff - kt0, tid);
+            __syncthreads();  // previous tile's reads of Ks / Vs are done
+            tk.template store<LDK>(Ks, tid);
+            tv.template store<LDV>(Vs, tid);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pr = 0; pr < G::NPAIR; ++pr) {
+            constexpr int BPP = BF ? 2 : 1;  // key blocks per k-step
+            f32x4 Pt[BPP];
+#pragma unroll
+            for (int u = 0; u < BPP; ++u) {
+                const int jb = pr * BPP + u;
+                const int jl0 = kt0 + jb * 16;  // chunk-local first key of the block
+                Pt[u] = zero4();
+                if (jl0 > qt0 + ib * 16 + 15) continue;  // block entirely above the diagonal
+                if constexpr (BF) {
+#pragma unroll
+                    for (int p = 0; p < DV / 32; ++p)
+                        Pt[u] = mfma(op_row8(Vs, LDV, jb * 16 + n, 32 * p + 8 * g),
+                                     op_row8(Ds, LDV, ib * 16 + n, 32 * p + 8 * g), Pt[u]);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < DV / 4; ++p)
+                        Pt[u] = mfma(Vs[(jb * 16 + n) * LDV + 4 * p + g], Ds[(ib * 16 + n) * LDV + 4 * p + g], Pt[u]);
+                }
+                // Pt[u][r] = v_j . do_i for j = jl0 + 4g + r, i = il
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = il - (jl0 + 4 * g + r);
+                    Pt[u][r] *= d >= 0 ? a.scale * pw[d] : 0.f;
+                }
+            }
+            if constexpr (BF) {
+                const bf16x8 pt = pack_acc(Pt[0], Pt[1]);
+#pragma unroll
+                for (int d = 0; d < NDB; ++d) dQT[d] = mfma(op_col_pair(Ks, LDK, 32 * pr, d * 16, n, g), pt, dQT[d]);
+            } else {
+                const int jb = pr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int d = 0; d < NDB; ++d)
+                        dQT[d] = mfma(Ks[(jb * 16 + 4 * g + r) * LDK + d * 16 + n], Pt[0][r], dQT[d]);
+            }
+        }
+    }
+
+    if (il < ceff) {
+        E* dqr = static_cast<E*>(a.dq) + tok0 * DK + (size_t)(t0 + il) * tokK;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) store4<E>(dqr + d * 16 + 4 * g, dQT[d]);
+    }
+    block_partial(a.scale * t3, red, NW, part);
+}
+
+// dlam[h] = sum over batch, chunks and partial slots, in a fixed order (double).
+__global__ __launch_bounds__(256) void dlambda_reduce_kernel(const float* __restrict__ part, int B, int H, int nc,
+                                                             int nslots, float* __restrict__ dlambda) {
+    __shared__ double red[256];
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const long per_b = (long)nc * nslots;
+    double s = 0.0;
+    for (long e = tid; e < (long)B * per_b; e += 256) {
+        const long bb = e / per_b, rest = e % per_b;
+        const long c = rest / nslots, slot = rest % nslots;
+        s += (double)part[(((size_t)bb * H + h) * nc + c) * kNPart + slot];
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int m = 128; m >= 1; m >>= 1) {
+        if (tid < m) red[tid] += red[tid + m];
+        __syncthreads();
+    }
+    if (tid == 0) dlambda[h] = (float)red[0];
+}
+
+// T == 0: no tokens -- dS0 = dS_T (or 0), dlam = 0.
+__global__ void bwd_empty_kernel(const float* __restrict__ dST, float* __restrict__ dS0, size_t n,
+                                 float* __restrict__ dlambda, int H) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        if (dS0) dS0[i] = dST ? dST[i] : 0.f;
+    if (blockIdx.x == 0 && dlambda)
+        for (int i = threadIdx.x; i < H; i += blockDim.x) dlambda[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- host side
+
+bool bwd_supported(bool bf16_io, int dk, int dv, int chunk) {
+    return bf16_io ? (dk == 96 && dv == 192 && (chunk == 128 || chunk == 64))
+                   : (dk == 16 && dv == 32 && chunk == 32);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
+    BwdPlan p{};
+    const FwdPlan f = fwd_plan(B, T, H, dk, dv, chunk, num_cu);
+    p.nc = f.nc;
+    p.nseg = f.nseg;
+    p.seg_chunks = f.seg_chunks;
+    const size_t units = (size_t)B * H;
+    const size_t esz = bf16_io ? 2 : 4;
+    p.snap_bytes = align256(units * p.nc * dk * dv * esz);
+    p.u_bytes = align256(units * (p.nseg - 1) * dk * dv * sizeof(float));
+    p.part_bytes = align256(units * (p.nc > 0 ? p.nc : 1) * kNPart * sizeof(float));
+    p.ws_bytes = 2 * p.snap_bytes + p.u_bytes + p.part_bytes;
+    return p;
+}
+
+template <typename E, int DK, int DV, int C>
+static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const void* q, const void* k,
+                               const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
+                               const float* dST, void* dq, void* dk, void* dv, float* dlambda, float* dS0,
+                               void* ws, hipStream_t stream) {
+    constexpr int NW = DV / 16 >= 4 ? 4 : DV / 16;
+    constexpr int dkdv = DK * DV;
+    char* w = static_cast<char*>(ws);
+    void* sbar = w;
+    void* gbar = w + plan.snap_bytes;
+    float* U = reinterpret_cast<float*>(w + 2 * plan.snap_bytes);
+    float* part = reinterpret_cast<float*>(w + 2 * plan.snap_bytes + plan.u_bytes);
+    const unsigned units = (unsigned)B * H;
+    const int nseg = plan.nseg;
+    hipError_t err;
+
+    StateArgs s{};
+    s.T = T;
+    s.H = H;
+    s.lambda = lambda;
+    s.U = U;
+    s.nseg = nseg;
+    s.seg_chunks = plan.seg_chunks;
+    s.nc = plan.nc;
+    // forward chain: snapshots Sbar
+    s.x = k;
+    s.y = v;
+    s.xscale = 1.f;
+    s.S_edge = S0;
+    s.snap = sbar;
+    if (nseg > 1) {
+        hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, false>), dim3(nseg - 1, units), dim3(NW * 64), 0,
+                           stream, s);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) != hipSuccess)
+            return err;
+    }
+    hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, true>), dim3(nseg, units), dim3(NW * 64), 0, stream, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // reverse chain: snapshots Gbar, dS0, <Gbar, Sbar> partials
+    s.x = q;
+    s.y = d_o;
+    s.xscale = scale;
+    s.S_edge = dST;
+    s.snap = gbar;
+    s.S_out = dS0;
+    s.sbar = sbar;
+    s.part = part;
+    if (nseg > 1) {
+        hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, false>), dim3(nseg - 1, units), dim3(NW * 64), 0,
+                           stream, s);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(rev_scan_kernel, dim3((dkdv / 4 + 255) / 256, units), dim3(256), 0, stream, dST, U, lambda,
+                           H, nseg, plan.seg_chunks * C, T, dkdv);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, true>), dim3(nseg, units), dim3(NW * 64), 0, stream, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    GradArgs ga{};
+    ga.T = T;
+    ga.H = H;
+    ga.q = q;
+    ga.k = k;
+    ga.v = v;
+    ga.d_o = d_o;
+    ga.lambda = lambda;
+    ga.scale = scale;
+    ga.sbar = sbar;
+    ga.gbar = gbar;
+    ga.dq = dq;
+    ga.dk = dk;
+    ga.dv = dv;
+    ga.part = part;
+    ga.nc = plan.nc;
+    using GS = GradShape<E, DK, DV, C>;
+    const dim3 ggrid(plan.nc * GS::NSUB, units);
+    hipLaunchKernelGGL((grad_dkdv_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((grad_dq_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (dlambda) {
+        hipLaunchKernelGGL(dlambda_reduce_kernel, dim3(H), dim3(256), 0, stream, part, B, H, plan.nc,
+                           1 + 2 * GS::NSUB, dlambda);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
+                      const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                      const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
+                      float* dS0, void* ws, hipStream_t stream) {
+    if (T == 0) {
+        const size_t n = (size_t)B * H * dk * dv;
+        hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                           dim3(256), 0, stream, dST, dS0, n, dlambda, H);
+        return hipGetLastError();
+    }
+    if (bf16_io && dk == 96 && dv == 192 && chunk == 128)
+        return launch_bwd_t<bf16, 96, 192, 128>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
+                                                dv_out, dlambda, dS0, ws, stream);
+    if (bf16_io && dk == 96 && dv == 192 && chunk == 64)
+        return launch_bwd_t<bf16, 96, 192, 64>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
+                                               dv_out, dlambda, dS0, ws, stream);
+    if (!bf16_io && dk == 16 && dv == 32 && chunk == 32)
+        return launch_bwd_t<float, 16, 32, 32>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
+                                               dv_out, dlambda, dS0, ws, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -13,24 +13,30 @@
 // Work decomposition (one workgroup of NW waves per (batch, head, segment)):
 //  * the fp32 state lives in MFMA accumulator registers for the whole chunk
 //    loop; wave w owns state columns [w*DV/NW, (w+1)*DV/NW) and the output
-//    columns with them, so the state is never written to LDS or HBM;
+//    columns with them, so the state is never written to LDS or HBM inside a
+//    segment;
 //  * per chunk the q, k, v tiles are staged global -> registers (prefetched one
-//    chunk ahead) -> LDS, as row-major Q and K plus transposed copies K'^T
-//    (pre-scaled by c_j) and V^T, so every MFMA operand is a contiguous LDS
-//    read along its contraction dimension;
-//  * A^T = K Q^T is computed per 16-row output block with its decay mask in
-//    fp32, rounded to bf16 and fed straight back from the accumulator
-//    registers as the B operand of O^T += V^T A^T (the accumulator's row index
-//    is the contraction index, so no LDS round trip is needed);
-//  * O^T = S^T Q^T (the inter-chunk term) likewise takes S from its
-//    accumulators; outputs leave as 4 consecutive columns per lane.
+//    chunk ahead) -> LDS, row-major as they sit in HBM, plus a copy of k
+//    pre-scaled by c_j; operands contracted over features are plain LDS reads,
+//    operands contracted over tokens use the gfx950 transpose read;
+//  * the decay-masked score blocks A = (Q K^T) (.) D are computed once per
+//    workgroup (blocks dealt round-robin to the waves, mask applied in fp32
+//    with per-lane precomputed powers) and shared through LDS in bf16;
+//  * each wave reads its value columns once per chunk as MFMA fragments and
+//    uses them twice: as V^T for the intra-chunk output O^T += V^T A^T and as
+//    V for the state update;
+//  * O^T = S^T Q^T (the inter-chunk term) takes S straight from its
+//    accumulator registers (the accumulator's row index is the contraction
+//    index); outputs leave as 4 consecutive columns per lane.
 //  * Long sequences are cut into segments run by separate workgroups: a
 //    prologue launch (STATE_ONLY) computes each segment's local end state U_s
-//    from zero; the main launch starts segment s from
-//    lam^(sL) S0 + sum_{s'<s} lam^((s-1-s')L) U_s' (Horner, L tokens per
-//    segment), which is the same recurrence regrouped by segments.
+//    from zero, a scan launch turns them into segment start states
+//    S_in(s+1) = lam^L S_in(s) + U_s (L tokens per segment), and the main
+//    launch runs every segment from its start state -- the same recurrence
+//    regrouped by segments.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
+#include "gla_tile.hpp"
 
 #include <stdlib.h>
 
@@ -46,138 +52,67 @@ struct FwdArgs {
     float scale;
     void* o;
     float* S_final;
-    float* U;          // [B*H][nseg-1][DK][DV] segment-local end states
+    float* U;          // [B*H][nseg-1][DK][DV]: segment-local end states, then segment start states
     int nseg, seg_chunks, nc;
 };
 
-// Loads one chunk tile (C rows of D elements, token stride `tok_stride`) into
-// registers as 16-byte pieces.  Piece p covers RP consecutive rows (2 for bf16
-// so a transposed LDS store writes one dword = two tokens) and one 16-byte
-// column group; rows at or past T read as zeros.
-template <typename E, int D, int C, int NT>
-struct TileLoader {
-    static constexpr int VEC = 16 / sizeof(E);
-    static constexpr int RP = 4 / sizeof(E);
-    static constexpr int KC = D / VEC;
-    static constexpr int NRG = C / RP;
-    static constexpr int NP = NRG * KC;
-    static constexpr int PER = (NP + NT - 1) / NT;
-    uint4 r[PER][RP];
+// Workgroups per CU the register budget is sized for: two whenever both fit in
+// LDS (everything but the full 128-token main tile set).
+// Row of block t of a lower triangle of 16x16 blocks numbered row by row
+// (block (ib, jb) is t = ib(ib+1)/2 + jb), for t < 136 (up to 16 block rows).
+__device__ __forceinline__ int tri_row(int t) {
+    int ib = static_cast<int>((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+    ib -= (ib * (ib + 1) / 2 > t);        // guard against sqrt rounding either way
+    ib += ((ib + 1) * (ib + 2) / 2 <= t);
+    return ib;
+}
 
-    __device__ __forceinline__ void load(const E* base, size_t tok_stride, int t0, int T, int tid) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int p = tid + NT * i;
-            const int rgp = p % NRG, kc = p / NRG;
-#pragma unroll
-            for (int j = 0; j < RP; ++j) {
-                const int t = t0 + rgp * RP + j;
-                if ((NP % NT == 0 || p < NP) && t < T)
-                    r[i][j] = *reinterpret_cast<const uint4*>(base + (size_t)t * tok_stride + kc * VEC);
-                else
-                    r[i][j] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    }
-
-    // Row-major copy dst[row * LD + col].
-    template <int LD>
-    __device__ __forceinline__ void store_rows(E* dst, int tid) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int p = tid + NT * i;
-            if (NP % NT != 0 && p >= NP) continue;
-            const int rgp = p % NRG, kc = p / NRG;
-#pragma unroll
-            for (int j = 0; j < RP; ++j)
-                *reinterpret_cast<uint4*>(dst + (rgp * RP + j) * LD + kc * VEC) = r[i][j];
-        }
-    }
-
-    // Transposed copy dst[col * LDT + row]; with SCALED, row j is multiplied by
-    // lam^(ceff-1-j) (0 past the chunk end) before rounding to E.
-    template <int LDT, bool SCALED>
-    __device__ __forceinline__ void store_cols(E* dst, int tid, const float* pw, int ceff) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int p = tid + NT * i;
-            if (NP % NT != 0 && p >= NP) continue;
-            const int rgp = p % NRG, kc = p / NRG;
-            const int row0 = rgp * RP;
-            if constexpr (sizeof(E) == 2) {
-                const bf16* x0 = reinterpret_cast<const bf16*>(&r[i][0]);
-                const bf16* x1 = reinterpret_cast<const bf16*>(&r[i][1]);
-                float c0 = 1.f, c1 = 1.f;
-                if constexpr (SCALED) {
-                    c0 = row0 < ceff ? pw[ceff - 1 - row0] : 0.f;
-                    c1 = row0 + 1 < ceff ? pw[ceff - 2 - row0] : 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16 a0 = x0[e], a1 = x1[e];
-                    if constexpr (SCALED) {
-                        a0 = to_bf16(to_f32(a0) * c0);
-                        a1 = to_bf16(to_f32(a1) * c1);
-                    }
-                    const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-                    *reinterpret_cast<uint32_t*>(dst + (kc * 8 + e) * LDT + row0) = w;
-                }
-            } else {
-                const float* x = reinterpret_cast<const float*>(&r[i][0]);
-                float c0 = 1.f;
-                if constexpr (SCALED) c0 = row0 < ceff ? pw[ceff - 1 - row0] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(kc * 4 + e) * LDT + row0] = x[e] * c0;
-            }
-        }
-    }
+// LDS layout of one workgroup (elements of E unless noted):
+//   Qs, Ks, Kc  [C][DK + PAD]   queries, keys, keys scaled by c_j   (main only: Qs, Ks)
+//   Vs          [C][DV + PAD]   values
+//   As          lower-triangular 16x16 blocks of the decay-masked scores
+//               A[i][j] = (q_i . k_j) lam^(i-j), block (ib, jb) at
+//               (ib(ib+1)/2 + jb) * 16 * ALD, row i - 16 ib, column j - 16 jb
+//   pw          [C + 1] fp32 powers lam^n
+template <typename E, int DK, int DV, int C, bool STATE_ONLY>
+struct FwdLds {
+    static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
+    static constexpr int LDK = DK + PAD;
+    static constexpr int LDV = DV + PAD;
+    static constexpr int ALD = sizeof(E) == 2 ? 24 : 20;  // padded 16-wide score block rows
+    static constexpr int NIB = C / 16;
+    static constexpr int NTRI = NIB * (NIB + 1) / 2;
+    static constexpr int QK = STATE_ONLY ? 8 : C * LDK;
+    static constexpr int AS = STATE_ONLY ? 8 : NTRI * 16 * ALD;
+    static constexpr int bytes =
+        (int)sizeof(E) * (2 * QK + C * LDK + C * LDV + AS) + 4 * (C + 1);
+    // Two workgroups per CU whenever two fit in LDS (160 KB) and the register
+    // half-file (256 per lane) holds a staged chunk next to the state: the
+    // prologue's 128-row bf16 / 64-row fp32 tiles do not, and would spill.
+    static constexpr int min_blocks =
+        (2 * bytes <= 160 * 1024 && !(STATE_ONLY && (int)sizeof(E) * C >= 256)) ? 2 : 1;
 };
 
-__device__ __forceinline__ bf16x8 lds_k8(const bf16* base, int ld, int row, int k0) {
-    return *reinterpret_cast<const bf16x8*>(base + row * ld + k0);
-}
-// k0..k0+3 and k0+16..k0+19: the k-set of two stacked accumulator blocks.
-__device__ __forceinline__ bf16x8 lds_k4x2(const bf16* base, int ld, int row, int k0) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + row * ld + k0);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + row * ld + k0 + 16);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ bf16x8 pack_acc(f32x4 a, f32x4 b) {
-    return bf16x8{to_bf16(a[0]), to_bf16(a[1]), to_bf16(a[2]), to_bf16(a[3]),
-                  to_bf16(b[0]), to_bf16(b[1]), to_bf16(b[2]), to_bf16(b[3])};
-}
-
-template <typename E>
-__device__ __forceinline__ void store4(E* dst, f32x4 x);
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, f32x4 x) {
-    *reinterpret_cast<f32x4*>(dst) = x;
-}
-template <>
-__device__ __forceinline__ void store4<bf16>(bf16* dst, f32x4 x) {
-    *reinterpret_cast<bf16x4*>(dst) = bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
-}
-
 template <typename E, int DK, int DV, int C, int NW, bool STATE_ONLY>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blocks)) void fwd_kernel(FwdArgs a) {
+    using L = FwdLds<E, DK, DV, C, STATE_ONLY>;
     constexpr bool BF = sizeof(E) == 2;
     constexpr int NT = NW * 64;
     constexpr int NCW = DV / NW;   // state / output columns per wave
     constexpr int NCB = NCW / 16;
     constexpr int NDB = DK / 16;
     constexpr int NIB = C / 16;
-    constexpr int PAD = BF ? 8 : 4;
-    constexpr int LDK = DK + PAD;  // row stride of Qs, Ks
-    constexpr int LDC = C + PAD;   // row stride of KTs, VTs
+    constexpr int LDK = L::LDK, LDV = L::LDV, ALD = L::ALD;
+    constexpr int NP = BF ? C / 32 : 1;  // bf16 token k-steps per chunk
     static_assert(NCW % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
     static_assert(!BF || (DK % 32 == 0 && C % 32 == 0), "bf16 k-steps of 32");
 
-    __shared__ __align__(16) E KTs[DK * LDC];
-    __shared__ __align__(16) E VTs[DV * LDC];
-    __shared__ __align__(16) E Qs[STATE_ONLY ? 8 : C * LDK];
-    __shared__ __align__(16) E Ks[STATE_ONLY ? 8 : C * LDK];
-    __shared__ float pw[C + 1];
+    __shared__ __align__(16) E Qs[L::QK];
+    __shared__ __align__(16) E Ks[L::QK];
+    __shared__ __align__(16) E Kc[C * LDK];  // keys scaled by c_j = lam^(ceff-1-j)
+    __shared__ __align__(16) E Vs[C * LDV];
+    __shared__ __align__(16) E As[L::AS];
+    __shared__ float pw[C + 1];              // lam^n, n = 0..C
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, n = lane % 16, g = lane / 16;
@@ -190,6 +125,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const float lam = a.lambda[h];
 
     for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
+    DecayLane dl;
+    float hlane = 1.f;   // lam^(n+1): b_i = lam^(16 ib) * lam^(n+1) for query i = 16 ib + n
+    if constexpr (!STATE_ONLY) {
+        dl.init(lam, n, g);
+        hlane = pow_int(lam, n + 1);
+    }
 
     const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
     const size_t tok0 = (size_t)b * T * H + h;
@@ -203,117 +144,166 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     auto sidx = [&](int db, int cb, int r) -> size_t {
         return (size_t)(db * 16 + 4 * g + r) * DV + colbase + cb * 16 + n;
     };
-    const float* S0 = STATE_ONLY ? nullptr : a.S0;
+    const float* Sin = nullptr;  // segment start state (nullptr = zero)
+    if constexpr (!STATE_ONLY) {
+        if (seg == 0) Sin = a.S0 ? a.S0 + (size_t)bh * DK * DV : nullptr;
+        else Sin = a.U + ((size_t)bh * (a.nseg - 1) + (seg - 1)) * DK * DV;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sacc[db][cb][r] = S0 ? S0[(size_t)bh * DK * DV + sidx(db, cb, r)] : 0.f;
-    if (!STATE_ONLY && seg > 0) {
-        const float lamL = pow_int(lam, a.seg_chunks * C);
-        const float* U = a.U + (size_t)bh * (a.nseg - 1) * DK * DV;
-        for (int s = 0; s < seg; ++s) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Sacc[db][cb][r] = fmaf(lamL, Sacc[db][cb][r], U[(size_t)s * DK * DV + sidx(db, cb, r)]);
-        }
-    }
+            for (int r = 0; r < 4; ++r) Sacc[db][cb][r] = Sin ? Sin[sidx(db, cb, r)] : 0.f;
 
-    TileLoader<E, DK, C, NT> lq, lk;
-    TileLoader<E, DV, C, NT> lv;
-    if (c_begin < c_end) {
-        if (!STATE_ONLY) lq.load(qb, tokK, c_begin * C, T, tid);
-        lk.load(kb, tokK, c_begin * C, T, tid);
-        lv.load(vb, tokV, c_begin * C, T, tid);
-    }
+    // With one workgroup per CU the next chunk's tiles are prefetched into
+    // registers during the current chunk's math; with two, the other
+    // workgroup's math covers the load and the registers go to the MFMA loop.
+    constexpr bool PREFETCH = L::min_blocks == 1;
+    TileStage<E, C, DK, NT> tq, tk;
+    TileStage<E, C, DV, NT> tv;
+    auto load_chunk = [&](int t) {
+        if (!STATE_ONLY) tq.load(qb + (size_t)t * tokK, tokK, T - t, tid);
+        tk.load(kb + (size_t)t * tokK, tokK, T - t, tid);
+        tv.load(vb + (size_t)t * tokV, tokV, T - t, tid);
+    };
+    if (PREFETCH && c_begin < c_end) load_chunk(c_begin * C);
 
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         const int ceff = min(C, T - t0);
+        if (!PREFETCH) load_chunk(t0);
         __syncthreads();  // previous chunk's LDS reads are done (and pw is visible)
         if (!STATE_ONLY) {
-            lq.template store_rows<LDK>(Qs, tid);
-            lk.template store_rows<LDK>(Ks, tid);
+            tq.template store<LDK>(Qs, tid);
+            tk.template store<LDK>(Ks, tid);
         }
-        lk.template store_cols<LDC, true>(KTs, tid, pw, ceff);
-        lv.template store_cols<LDC, false>(VTs, tid, pw, ceff);
+        tk.template store_scaled<LDK>(Kc, tid, [&](int row) { return row < ceff ? pw[ceff - 1 - row] : 0.f; });
+        tv.template store<LDV>(Vs, tid);
         __syncthreads();
-        if (c + 1 < c_end) {
-            if (!STATE_ONLY) lq.load(qb, tokK, t0 + C, T, tid);
-            lk.load(kb, tokK, t0 + C, T, tid);
-            lv.load(vb, tokV, t0 + C, T, tid);
-        }
+        if (PREFETCH && c + 1 < c_end) load_chunk(t0 + C);
 
         if constexpr (!STATE_ONLY) {
+            // Decay-masked score blocks, each computed by one wave and shared:
+            // A[i][j] = (q_i . k_j) lam^(i-j) for j <= i (block (ib, jb), jb <= ib).
+            // Block t = NW*k + wave of the triangle; the blocks of a wave are
+            // independent, so their MFMA chains are interleaved k-step by k-step.
+            constexpr int NBW = (L::NTRI + NW - 1) / NW;  // blocks per wave
+            constexpr int GRP = NBW < 3 ? NBW : 3;           // blocks interleaved at a time
+            const int nib = (ceff + 15) / 16;
+            const int ntri = nib * (nib + 1) / 2;
 #pragma unroll
+            for (int k0 = 0; k0 < NBW; k0 += GRP) {
+                if (wave + NW * k0 >= ntri) break;
+                f32x4 AT[GRP];
+                int bib[GRP], bjb[GRP];
+#pragma unroll
+                for (int k = 0; k < GRP; ++k) {
+                    const int t = wave + NW * (k0 + k);  // slots past the triangle point at block 0 (unused)
+                    bib[k] = t < L::NTRI ? tri_row(t) : 0;
+                    bjb[k] = t < L::NTRI ? t - bib[k] * (bib[k] + 1) / 2 : 0;
+                    AT[k] = zero4();
+                }
+                if constexpr (BF) {
+#pragma unroll
+                    for (int p = 0; p < DK / 32; ++p)
+#pragma unroll
+                        for (int k = 0; k < GRP; ++k)
+                            if (k0 + k < NBW && wave + NW * (k0 + k) < ntri)
+                                AT[k] = mfma(op_row8(Ks, LDK, bjb[k] * 16 + n, 32 * p + 8 * g),
+                                             op_row8(Qs, LDK, bib[k] * 16 + n, 32 * p + 8 * g), AT[k]);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < DK / 4; ++p)
+#pragma unroll
+                        for (int k = 0; k < GRP; ++k)
+                            if (k0 + k < NBW && wave + NW * (k0 + k) < ntri)
+                                AT[k] = mfma(Ks[(bjb[k] * 16 + n) * LDK + 4 * p + g],
+                                             Qs[(bib[k] * 16 + n) * LDK + 4 * p + g], AT[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < GRP; ++k) {
+                    const int t = wave + NW * (k0 + k);
+                    if (k0 + k >= NBW || t >= ntri) break;
+                    const int ib = bib[k], jb = bjb[k];
+                    const float blk = jb == ib ? 1.f : pw[16 * (ib - jb - 1)];  // lam^(16(ib-jb-1))
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) AT[k][r] *= (jb == ib) ? dl.diag[r] : blk * dl.off[r];
+                    store4<E>(As + t * 16 * ALD + n * ALD + 4 * g, AT[k]);
+                }
+            }
+        }
+        // This wave's value columns as MFMA fragments, shared by the intra-chunk
+        // output (as V^T, A operand) and the state update (as V, B operand):
+        // vf[cb][p] holds V[32p + 8g + e][colbase + 16 cb + n], e = 0..7.
+        bf16x8 vf[NCB][NP];
+        if constexpr (BF) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int p = 0; p < NP; ++p) vf[cb][p] = op_col8(Vs, LDV, 32 * p, colbase + cb * 16, n, g);
+        }
+        if constexpr (!STATE_ONLY) {
+            __syncthreads();  // score blocks complete
+#pragma unroll 1
             for (int ib = 0; ib < NIB; ++ib) {
                 if (ib * 16 >= ceff) break;
-                const int irow = ib * 16 + n;  // this lane's output row (token) in the chunk
-                // A^T blocks (jb, ib): AT[jb][r] = (k_j . q_i) * lam^(i-j), j = jb*16+4g+r.
-                f32x4 AT[NIB];
+                const int irow = ib * 16 + n;  // this lane's query row in the chunk
+                const float bi = pw[16 * ib] * hlane;
+                // O^T = b_i S^T Q^T (inter-chunk, S^T from its accumulators)
+                //      + V^T A^T     (intra-chunk, A from the shared score blocks)
+                f32x4 OT[NCB];
 #pragma unroll
-                for (int jb = 0; jb <= ib; ++jb) {
-                    AT[jb] = zero4();
-                    if constexpr (BF) {
+                for (int cb = 0; cb < NCB; ++cb) OT[cb] = zero4();
+                if constexpr (BF) {
+                    bf16x8 qop[DK / 32];
 #pragma unroll
-                        for (int p = 0; p < DK / 32; ++p)
-                            AT[jb] = mfma(lds_k8(Ks, LDK, jb * 16 + n, 32 * p + 8 * g),
-                                          lds_k8(Qs, LDK, irow, 32 * p + 8 * g), AT[jb]);
-                    } else {
+                    for (int p = 0; p < DK / 32; ++p) qop[p] = op_row_pair(Qs, LDK, irow, 32 * p + 4 * g);
 #pragma unroll
-                        for (int p = 0; p < DK / 4; ++p)
-                            AT[jb] = mfma(Ks[(jb * 16 + n) * LDK + 4 * p + g], Qs[irow * LDK + 4 * p + g], AT[jb]);
-                    }
+                    for (int p = 0; p < DK / 32; ++p)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int d = irow - (jb * 16 + 4 * g + r);
-                        AT[jb][r] *= d >= 0 ? pw[d] : 0.f;
-                    }
-                }
-                const float bi = pw[irow + 1];
+                        for (int cb = 0; cb < NCB; ++cb)
+                            OT[cb] = mfma(pack_acc(Sacc[2 * p][cb], Sacc[2 * p + 1][cb]), qop[p], OT[cb]);
+                } else {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const int vrow = colbase + cb * 16 + n;  // this lane's column as a V^T row
-                    f32x4 OT = zero4();
-                    // inter-chunk: O^T += S^T Q^T
-                    if constexpr (BF) {
-#pragma unroll
-                        for (int p = 0; p < DK / 32; ++p)  // S^T from its accumulators, pairs of dk blocks
-                            OT = mfma(pack_acc(Sacc[2 * p][cb], Sacc[2 * p + 1][cb]),
-                                      lds_k4x2(Qs, LDK, irow, 32 * p + 4 * g), OT);
-                    } else {
+                    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                         for (int db = 0; db < NDB; ++db)
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                OT = mfma(Sacc[db][cb][r], Qs[irow * LDK + db * 16 + 4 * g + r], OT);
+                                OT[cb] = mfma(Sacc[db][cb][r], Qs[irow * LDK + db * 16 + 4 * g + r], OT[cb]);
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) OT[cb][r] *= bi;
+                if constexpr (BF) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        if (2 * p > ib) break;
+                        const int jb = 2 * p + (g >> 1);  // this lane's key block
+                        bf16x8 aop = bf16x8{};
+                        if (jb <= ib)
+                            aop = op_row8(As + (ib * (ib + 1) / 2 + jb) * 16 * ALD, ALD, n, 8 * (g & 1));
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf[cb][p], aop, OT[cb]);
                     }
+                } else {
+                    for (int jb = 0; jb <= ib; ++jb) {
+                        const E* blk = As + (ib * (ib + 1) / 2 + jb) * 16 * ALD + n * ALD + 4 * g;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) OT[r] *= bi;
-                    // intra-chunk: O^T += V^T A^T
-                    if constexpr (BF) {
-#pragma unroll
-                        for (int p = 0; 2 * p <= ib; ++p) {
-                            const f32x4 hi = (2 * p + 1 <= ib) ? AT[2 * p + 1] : zero4();
-                            OT = mfma(lds_k4x2(VTs, LDC, vrow, 32 * p + 4 * g), pack_acc(AT[2 * p], hi), OT);
-                        }
-                    } else {
-#pragma unroll
-                        for (int jb = 0; jb <= ib; ++jb)
+                        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                OT = mfma(VTs[vrow * LDC + jb * 16 + 4 * g + r], AT[jb][r], OT);
+                                OT[cb] = mfma(Vs[(jb * 16 + 4 * g + r) * LDV + colbase + cb * 16 + n], blk[r], OT[cb]);
                     }
-                    if (irow < ceff) {
+                }
+                if (irow < ceff) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) OT[r] *= a.scale;
-                        store4<E>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT);
+                    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) OT[cb][r] *= a.scale;
+                        store4<E>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT[cb]);
                     }
                 }
             }
@@ -329,23 +319,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
                 for (int r = 0; r < 4; ++r) Sacc[db][cb][r] *= Lam;
         if constexpr (BF) {
 #pragma unroll
-            for (int p = 0; p < C / 32; ++p)
+            for (int p = 0; p < NP; ++p)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 ka = lds_k8(KTs, LDC, db * 16 + n, 32 * p + 8 * g);
+                    const bf16x8 kop = op_col8(Kc, LDK, 32 * p, db * 16, n, g);
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        Sacc[db][cb] = mfma(ka, lds_k8(VTs, LDC, colbase + cb * 16 + n, 32 * p + 8 * g), Sacc[db][cb]);
+                    for (int cb = 0; cb < NCB; ++cb) Sacc[db][cb] = mfma(kop, vf[cb][p], Sacc[db][cb]);
                 }
         } else {
-#pragma unroll
+#pragma unroll 2
             for (int p = 0; p < C / 4; ++p)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
-                        Sacc[db][cb] = mfma(KTs[(db * 16 + n) * LDC + 4 * p + g],
-                                            VTs[(colbase + cb * 16 + n) * LDC + 4 * p + g], Sacc[db][cb]);
+                        Sacc[db][cb] = mfma(Kc[(4 * p + g) * LDK + db * 16 + n],
+                                            Vs[(4 * p + g) * LDV + colbase + cb * 16 + n], Sacc[db][cb]);
         }
     }
 
@@ -360,6 +349,42 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[sidx(db, cb, r)] = Sacc[db][cb][r];
     }
+}
+
+// Segment start states: turns the segment-local end states U_0..U_{nseg-2} (from
+// zero) into the start states of segments 1..nseg-1, in place:
+//   S_in(s+1) = lam^L S_in(s) + U_s,   S_in(0) = S0 (or 0),   L = tokens per segment.
+// One thread per 4 consecutive state elements; all loads are issued before the
+// (short, sequential) multiply-add chain.
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ S0, float* __restrict__ U,
+                                                       const float* __restrict__ lambda, int H, int nseg,
+                                                       int seg_tokens, int dkdv) {
+    const int bh = blockIdx.y;
+    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 * 4 >= dkdv) return;
+    const float lamL = pow_int(lambda[bh % H], seg_tokens);
+    f32x4 run = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)bh * dkdv + 4 * e4) : zero4();
+    f32x4* u = reinterpret_cast<f32x4*>(U + (size_t)bh * (nseg - 1) * dkdv) + e4;
+    const size_t step = (size_t)dkdv / 4;
+    f32x4 x[kMaxSegments - 1];
+#pragma unroll
+    for (int s = 0; s < kMaxSegments - 1; ++s)
+        if (s < nseg - 1) x[s] = u[s * step];
+#pragma unroll
+    for (int s = 0; s < kMaxSegments - 1; ++s) {
+        if (s < nseg - 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) run[e] = fmaf(lamL, run[e], x[s][e]);
+            u[s * step] = run;
+        }
+    }
+}
+
+hipError_t launch_seg_scan(const float* S0, float* U, const float* lambda, int H, int nseg, int seg_tokens,
+                           int dkdv, unsigned units, hipStream_t stream) {
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((dkdv / 4 + 255) / 256, units), dim3(256), 0, stream, S0, U, lambda, H,
+                       nseg, seg_tokens, dkdv);
+    return hipGetLastError();
 }
 
 // T == 0: the final state is the initial one (or zeros).
@@ -380,12 +405,12 @@ FwdPlan fwd_plan(int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
     p.nc = T > 0 ? (T + chunk - 1) / chunk : 0;
     const long units = (long)B * H;
     int nseg = 1;
-    // Split the sequence until the grid covers every compute unit, keeping at
-    // least two chunks per segment for the Horner start-up of later segments.
-    while (units * nseg < num_cu && nseg * 4 <= p.nc && nseg < 16) nseg *= 2;
-    if (const char* e = getenv("GLA_FWD_SEGMENTS")) {
+    // Split the sequence until the grid covers every compute unit (segments of
+    // at least one chunk, at most kMaxSegments of them).
+    while (units * nseg < num_cu && nseg * 2 <= p.nc && nseg < kMaxSegments) nseg *= 2;
+    if (const char* e = getenv("GLA_FWD_SEGMENTS")) {  // tuning override (sweeps, tests)
         const int forced = atoi(e);
-        if (forced >= 1) nseg = forced;
+        if (forced >= 1) nseg = forced < kMaxSegments ? forced : kMaxSegments;
     }
     if (p.nc == 0) nseg = 1;
     nseg = nseg > p.nc && p.nc > 0 ? p.nc : nseg;
@@ -419,6 +444,8 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, int B, int T, int H, const v
         hipLaunchKernelGGL((fwd_kernel<E, DK, DV, C, NW, true>), dim3(plan.nseg - 1, units), dim3(NW * 64), 0,
                            stream, a);
         hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        err = launch_seg_scan(S0, a.U, lambda, H, plan.nseg, plan.seg_chunks * C, DK * DV, units, stream);
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL((fwd_kernel<E, DK, DV, C, NW, false>), dim3(plan.nseg, units), dim3(NW * 64), 0, stream, a);

@@ -20,6 +20,28 @@ hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, in
                       const float* S0, float scale, void* o, float* S_final, void* ws,
                       hipStream_t stream);
 
+// Sequence segments run in parallel (at most this many per sequence).
+constexpr int kMaxSegments = 16;
+
+// Turns segment-local end states U_0..U_{nseg-2} into start states of
+// segments 1..nseg-1 in place (forward order), starting from S0 (or 0).
+hipError_t launch_seg_scan(const float* S0, float* U, const float* lambda, int H, int nseg, int seg_tokens,
+                           int dkdv, unsigned units, hipStream_t stream);
+
+struct BwdPlan {
+    int nc, nseg, seg_chunks;
+    size_t snap_bytes;  // per-chunk snapshots (one array for states, one for state gradients)
+    size_t u_bytes;     // segment states (fp32)
+    size_t part_bytes;  // dlambda partials
+    size_t ws_bytes;    // total
+};
+bool bwd_supported(bool bf16_io, int dk, int dv, int chunk);
+BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
+                      const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                      const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
+                      float* dS0, void* ws, hipStream_t stream);
+
 bool decode_supported(int dk, int dv);
 hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
                          const void* v, const float* lambda, float* S, float scale, void* o,

@@ -98,6 +98,36 @@ int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Workspace needed by gla_bwd_chunked (bytes; 0 for unsupported/invalid sizes).
+ * Holds the per-chunk state snapshots (2 * B*H*ceil(T/chunk)*dk*dv elements of
+ * the input dtype), segment states and the dlambda partials.
+ */
+size_t gla_bwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+/*
+ * Chunked backward: gradients of a scalar loss L given do = dL/do and the
+ * optional dS_final = dL/dS_final, through the forward defined above (Laplace
+ * 3B post, section "Challenge 3": the backward differentiates through the
+ * sequential chunk-to-chunk state chain, run here in reverse chunk order).
+ * Supported shapes: bf16 (96, 192, 128), (96, 192, 64); fp32 (16, 32, 32).
+ *   q, k, v, lambda, S0, scale, chunk   as in gla_fwd_chunked (S0 nullable)
+ *   d_o        [B][T][H][dv] (dtype) upstream gradient of o
+ *   dS_final   [B][H][dk][dv] fp32 upstream gradient of S_final (NULL = 0)
+ *   dq, dk_out [B][T][H][dk] (dtype) outputs;  dv_out [B][T][H][dv] (dtype) output
+ *   dlambda    [H] fp32 output, summed over the batch (NULL = not computed)
+ *   dS0        [B][H][dk][dv] fp32 output, gradient of the initial state (NULL = skip)
+ *   ws, ws_bytes  caller-owned workspace of at least gla_bwd_workspace_bytes(...)
+ * With T == 0: dS0 = dS_final (or 0) and dlambda = 0.
+ */
+int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                    const void* q, const void* k, const void* v,
+                    const float* lambda, const float* S0, float scale,
+                    const void* d_o, const float* dS_final,
+                    void* dq, void* dk_out, void* dv_out,
+                    float* dlambda, float* dS0,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Batched single-token decode step (Laplace 3B post, section "Optimizing
  * inference on Trainium2": one fixed state page per sequence, read and written
  * once per generated token).  For every sequence n and head h, in place:
