@@ -4,6 +4,9 @@
 A step is one pass of the hot path on synthetic inputs already resident in HBM:
   * forward: one gla_fwd_chunked call on the Laplace-layer workload
     (B=1, H=16, T=2048, dk=96, dv=192, chunk 128, bf16, fp32 state);
+  * training step: gla_fwd_chunked + gla_bwd_chunked (dq, dk, dv, dlambda) on
+    the mixer-train workload (B=8, H=16, T=2048, do ~ N(0,1)), at chunk 128
+    (part of the step) and chunk 64 (timed alongside, reported separately);
   * decode: one decode step of the 1,280-sequence x 24-layer serving workload
     (24 gla_decode_step launches over a 36 GB fp32 state pool).
 Each leg is timed over K steps after W warm-up steps, bracketed by device
@@ -42,6 +45,18 @@ def fwd_flops_per_token_head(C, dk=96, dv=192):
     return 2 * C * (dk + dv) + 4 * dk * dv
 
 
+def train_bytes_per_token_head(C, dk=96, dv=192):
+    """Forward I/O + backward I/O (q,k,v,do in; dq,dk,dv out, bf16) + one fp32
+    state write+read per chunk: 1152 + 1920 + 2*4*dk*dv/C."""
+    return 1152 + 1920 + 2 * 4 * dk * dv // C
+
+
+def train_flops_per_token_head(C, dk=96, dv=192):
+    """Tile-issued MFMA work of forward + backward: 2C(dk+dv) + 4dk dv for the
+    forward, 2C(2dv + 3dk) + 10 dk dv for the backward (state recompute included)."""
+    return fwd_flops_per_token_head(C, dk, dv) + 2 * C * (2 * dv + 3 * dk) + 10 * dk * dv
+
+
 DEC_BYTES_PER_SEQ_HEAD = 2 * 96 * 192 * 4 + 2 * (96 + 96 + 192 + 192)   # state R+W + q,k,v,o bf16
 DEC_FLOPS_PER_SEQ_HEAD = 4 * 96 * 192
 
@@ -77,9 +92,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (debugging only)")
+    ap.add_argument("--no-train", action="store_true", help="skip the training legs (debugging only)")
     ap.add_argument("--counters", action="store_true",
                     help="run a short fixed sequence (copy kernel + each hot kernel) for rocprofv3 --pmc")
     ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files of the --counters pass "
+                         "(FETCH_SIZE, WRITE_SIZE) into profiles/counters.json")
     return ap.parse_args()
 
 
@@ -112,6 +131,45 @@ class FwdLeg:
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError(f"gla_fwd_chunked: {self.gla.status_str(st)}")
+
+
+class TrainLeg:
+    """Pre-marshalled forward + backward (dq, dk, dv, dlambda) on the mixer-train workload."""
+
+    def __init__(self, gla, gi, torch, w, seed, chunk):
+        dev = torch.device("cuda:0")
+        x = gi.fwd_inputs(w, dev, seed, with_do=True)
+        self.x = x
+        B, T, H, dk = x["q"].shape
+        dv = x["v"].shape[3]
+        self.tokens = B * T
+        self.token_heads = B * T * H
+        dt = gla.GLA_BF16
+        self.o = torch.empty_like(x["v"])
+        self.dq, self.dk, self.dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+        self.dl = torch.empty(H, dtype=torch.float32, device=dev)
+        nf = gla.fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+        nb = gla.bwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+        self.wsf = torch.empty(max(nf, 16), dtype=torch.uint8, device=dev)
+        self.wsb = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+        p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        st = ctypes.c_void_p(self.stream.cuda_stream)
+        lib = gla.load()
+        self.f, self.b = lib.gla_fwd_chunked, lib.gla_bwd_chunked
+        sc = ctypes.c_float(x["scale"])
+        self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                      p(self.o), None, p(self.wsf), ctypes.c_size_t(nf), st)
+        self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                      p(x["do"]), None, p(self.dq), p(self.dk), p(self.dv), p(self.dl), None, p(self.wsb),
+                      ctypes.c_size_t(nb), st)
+        self.gla = gla
+
+    def __call__(self):
+        for fn, args, name in ((self.f, self.fargs, "gla_fwd_chunked"), (self.b, self.bargs, "gla_bwd_chunked")):
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(f"{name}: {self.gla.status_str(st)}")
 
 
 class DecodeLeg:
@@ -255,8 +313,47 @@ def counters_pass(torch, gla, gi, chunk):
     print(json.dumps({"counters_pass": "done", "copy_bytes_each": 2 * (1 << 30)}), flush=True)
 
 
+def ingest_counters(fetch_csv, write_csv):
+    """Per-dispatch HBM traffic of the hot kernels from the --counters pass, scaled by
+    what the same counters read for the 1 GiB device copy (2 GiB moved) of that pass."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        by = {}
+        for r in rows:
+            by.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), 0.0)
+            by[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+        return by
+
+    out = {"src_digest": src_digest(), "kernels": {}}
+    fac = {}
+    vals = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        by = per_kernel(path, counter)
+        copies = [v for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
+        ref = max(copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
+        fac[counter] = (1 << 30) / (ref * 1024.0)
+        groups = {"fwd": ["fwd_kernel", "seg_scan"], "decode": ["decode_kernel"]}
+        for key, pats in groups.items():
+            # per call: sum over the kernels one call launches, averaged over the 3 calls
+            tot = sum(v for (d, name), v in by.items() if any(pt in name for pt in pats))
+            vals.setdefault(key, {})[counter] = tot / 3.0 * 1024.0 * fac[counter]
+    for key, v in vals.items():
+        out["kernels"][key] = {"src_digest": out["src_digest"], "fetch_bytes_per_launch": v["FETCH_SIZE"],
+                               "write_bytes_per_launch": v["WRITE_SIZE"],
+                               "hbm_bytes_per_launch": v["FETCH_SIZE"] + v["WRITE_SIZE"]}
+    out["copy_calibration"] = {"fetch_factor": fac["FETCH_SIZE"], "write_factor": fac["WRITE_SIZE"]}
+    with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the mixer's hot path is single-GPU here); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -300,6 +397,27 @@ def main():
         "fwd": {"ms_per_call_wall": f_ms, "avg_launch_us": f_avg * 1e6, "min_launch_us": min(f_per) * 1e6},
     }
 
+    # ---- training-step legs (mixer-train workload, chunk 128 and 64)
+    w2 = ws[2]
+    t_ms = 0.0
+    result["train"] = {}
+    for C in (() if args.no_train else (128, 64)):
+        tleg = TrainLeg(gla, gi, torch, w2, 2, C)
+        t_wall, t_per = time_fwd(torch, tleg, K, W)
+        t_avg = sum(t_per) / len(t_per)
+        tb = train_bytes_per_token_head(C) * tleg.token_heads
+        tf = train_flops_per_token_head(C) * tleg.token_heads
+        leg = {"value": K * tleg.tokens / t_wall, "unit": "tokens/s", "ms_per_step": t_wall / K * 1e3,
+               "workload": f"mixer-train B=8 H=16 T=2048 dk=96 dv=192 C={C} bf16, fwd + bwd (dq,dk,dv,dlambda)",
+               "avg_step_us": t_avg * 1e6, "alg_bytes_per_step": tb, "alg_flops_per_step": tf,
+               "hbm_gbs": tb / t_avg / 1e9, "hbm_frac": tb / t_avg / 1e9 / HBM_PEAK_GBS,
+               "mfma_tflops": tf / t_avg / 1e12, "mfma_frac": tf / t_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        result["train"][f"chunk{C}"] = leg
+        if C == 128:
+            t_ms = leg["ms_per_step"]
+        del tleg
+        torch.cuda.empty_cache()
+
     # ---- decode leg (1,280 sequences x 24 layers)
     d_ms = 0.0
     if not args.no_decode:
@@ -322,7 +440,7 @@ def main():
         }
         del dleg
         torch.cuda.empty_cache()
-    result["ms_per_step"] = f_ms + d_ms
+    result["ms_per_step"] = f_ms + t_ms + d_ms
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline_fwd(gi, w1, 1)

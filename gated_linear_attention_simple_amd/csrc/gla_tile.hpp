@@ -149,8 +149,8 @@ struct TileStage {
 // (queries), i.e. element (j = jb*16 + 4g + r, i = ib*16 + n):
 //   diagonal block (ib == jb): lam^(n - 4g - r) if n >= 4g + r, else 0
 //   below (ib > jb):           lam^(16(ib - jb - 1)) * lam^(16 + n - 4g - r)
-// Every factor is a product of at most two exp2-evaluated powers with
-// non-negative exponents (no ratio of powers is formed).
+// Every factor is a product of at most two powers with non-negative exponents
+// (no ratio of powers is formed).
 struct DecayLane {
     float diag[4];
     float off[4];

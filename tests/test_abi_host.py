@@ -85,3 +85,34 @@ def test_decode_rejects_bad_arguments():
     assert d(q=None) == gla.GLA_ERR_INVALID_ARG
     assert d(S=MIS) == gla.GLA_ERR_INVALID_ARG
     assert d(N=0, q=None) == gla.GLA_OK        # nothing to do, nothing enqueued
+
+
+def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,
+        dq=P, dk_=P, dv_=P, dl=None, dS0=None, ws=None, wsb=0):
+    return gla.load().gla_bwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, do, dST, dq, dk_, dv_,
+                                      dl, dS0, ws, wsb, None)
+
+
+def test_bwd_rejects_bad_arguments_before_touching_the_device():
+    E = gla
+    assert bwd(dtype=3) == E.GLA_ERR_INVALID_ARG
+    assert bwd(T=-5) == E.GLA_ERR_INVALID_ARG
+    assert bwd(dk=64) == E.GLA_ERR_UNSUPPORTED
+    assert bwd(dtype=0) == E.GLA_ERR_UNSUPPORTED                  # fp32 backward: tiny shape only
+    assert bwd(dtype=0, dk=16, dv=32, C=64) == E.GLA_ERR_UNSUPPORTED
+    assert bwd(do=None) == E.GLA_ERR_INVALID_ARG
+    assert bwd(dv_=MIS) == E.GLA_ERR_INVALID_ARG
+    assert bwd(dl=MIS) == E.GLA_ERR_INVALID_ARG
+    assert bwd(dST=MIS) == E.GLA_ERR_INVALID_ARG
+    need = gla.load().gla_bwd_workspace_bytes(1, 1, 256, 16, 96, 192, 128)
+    assert need > 0
+    assert bwd() == E.GLA_ERR_WORKSPACE
+    assert bwd(ws=P, wsb=need - 1) == E.GLA_ERR_WORKSPACE
+
+
+def test_bwd_workspace_holds_both_snapshot_sets():
+    lib = gla.load()
+    B, T, H, C = 8, 2048, 16, 128
+    need = lib.gla_bwd_workspace_bytes(1, B, T, H, 96, 192, C)
+    snaps = 2 * B * H * (T // C) * 96 * 192 * 2
+    assert snaps <= need <= snaps + 16 * 1024 * 1024
