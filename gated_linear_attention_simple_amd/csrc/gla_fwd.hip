@@ -1,4 +1,5 @@
-// gla_fwd.hip -- chunked-parallel GLA forward on gfx950 MFMA.
+// gla_fwd.hip -- chunked-parallel GLA forward for fp32 q/k/v, plus the launch
+// plan, segment scan and dispatch shared with the bf16 kernel (gla_fwd_bf16.hip).
 //
 // Method: Laplace 3B post, section "Challenge 1" (chunked GLA).  For chunk c
 // of C tokens with start state S (positions i, j in [0, C) inside the chunk,
@@ -10,30 +11,18 @@
 // o_t = scale S_t^T q_t regrouped exactly (only rounding differs).  A partial
 // last chunk uses its own length in place of C.
 //
-// Work decomposition (one workgroup of NW waves per (batch, head, segment)):
-//  * the fp32 state lives in MFMA accumulator registers for the whole chunk
-//    loop; wave w owns state columns [w*DV/NW, (w+1)*DV/NW) and the output
-//    columns with them, so the state is never written to LDS or HBM inside a
-//    segment;
-//  * per chunk the q, k, v tiles are staged global -> registers (prefetched one
-//    chunk ahead) -> LDS, row-major as they sit in HBM, plus a copy of k
-//    pre-scaled by c_j; operands contracted over features are plain LDS reads,
-//    operands contracted over tokens use the gfx950 transpose read;
-//  * the decay-masked score blocks A = (Q K^T) (.) D are computed once per
-//    workgroup (blocks dealt round-robin to the waves, mask applied in fp32
-//    with per-lane precomputed powers) and shared through LDS in bf16;
-//  * each wave reads its value columns once per chunk as MFMA fragments and
-//    uses them twice: as V^T for the intra-chunk output O^T += V^T A^T and as
-//    V for the state update;
-//  * O^T = S^T Q^T (the inter-chunk term) takes S straight from its
-//    accumulator registers (the accumulator's row index is the contraction
-//    index); outputs leave as 4 consecutive columns per lane.
-//  * Long sequences are cut into segments run by separate workgroups: a
-//    prologue launch (STATE_ONLY) computes each segment's local end state U_s
-//    from zero, a scan launch turns them into segment start states
-//    S_in(s+1) = lam^L S_in(s) + U_s (L tokens per segment), and the main
-//    launch runs every segment from its start state -- the same recurrence
-//    regrouped by segments.
+// fp32 kernel (16x16x4 fp32 MFMA; one workgroup of NW waves per (batch, head,
+// segment)): the fp32 state lives in accumulator registers across the chunk
+// loop, wave w owning state/output columns [w*DV/NW, (w+1)*DV/NW); q, k, a
+// c_j-scaled copy of k and v are staged row-major in LDS; decay-masked score
+// blocks are computed once per workgroup and shared through LDS; O^T = S^T Q^T
+// takes S straight from its accumulators.
+//
+// Long sequences are cut into segments run by separate workgroups: a prologue
+// launch (STATE_ONLY) computes each segment's local end state U_s from zero, a
+// scan launch turns them into segment start states
+// S_in(s+1) = lam^L S_in(s) + U_s (L tokens per segment), and the main launch
+// runs every segment from its start state -- the same recurrence regrouped.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
@@ -42,22 +31,7 @@
 
 namespace gla {
 
-struct FwdArgs {
-    int T, H;
-    const void* q;
-    const void* k;
-    const void* v;
-    const float* lambda;
-    const float* S0;
-    float scale;
-    void* o;
-    float* S_final;
-    float* U;          // [B*H][nseg-1][DK][DV]: segment-local end states, then segment start states
-    int nseg, seg_chunks, nc;
-};
 
-// Workgroups per CU the register budget is sized for: two whenever both fit in
-// LDS (everything but the full 128-token main tile set).
 // Row of block t of a lower triangle of 16x16 blocks numbered row by row
 // (block (ib, jb) is t = ib(ib+1)/2 + jb), for t < 136 (up to 16 block rows).
 __device__ __forceinline__ int tri_row(int t) {
@@ -67,45 +41,35 @@ __device__ __forceinline__ int tri_row(int t) {
     return ib;
 }
 
-// LDS layout of one workgroup (elements of E unless noted):
-//   Qs, Ks, Kc  [C][DK + PAD]   queries, keys, keys scaled by c_j   (main only: Qs, Ks)
-//   Vs          [C][DV + PAD]   values
+// LDS layout of one fp32 workgroup:
+//   Qs, Ks, Kc  [C][DK + 4]   queries, keys, keys scaled by c_j   (main only: Qs, Ks)
+//   Vs          [C][DV + 4]   values
 //   As          lower-triangular 16x16 blocks of the decay-masked scores
 //               A[i][j] = (q_i . k_j) lam^(i-j), block (ib, jb) at
 //               (ib(ib+1)/2 + jb) * 16 * ALD, row i - 16 ib, column j - 16 jb
-//   pw          [C + 1] fp32 powers lam^n
-template <typename E, int DK, int DV, int C, bool STATE_ONLY>
+//   pw          [C + 1] powers lam^n
+template <int DK, int DV, int C, bool STATE_ONLY>
 struct FwdLds {
-    static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-    static constexpr int LDK = DK + PAD;
-    static constexpr int LDV = DV + PAD;
-    static constexpr int ALD = sizeof(E) == 2 ? 24 : 20;  // padded 16-wide score block rows
+    static constexpr int LDK = DK + 4;
+    static constexpr int LDV = DV + 4;
+    static constexpr int ALD = 20;  // padded 16-wide score block rows
     static constexpr int NIB = C / 16;
     static constexpr int NTRI = NIB * (NIB + 1) / 2;
     static constexpr int QK = STATE_ONLY ? 8 : C * LDK;
     static constexpr int AS = STATE_ONLY ? 8 : NTRI * 16 * ALD;
-    static constexpr int bytes =
-        (int)sizeof(E) * (2 * QK + C * LDK + C * LDV + AS) + 4 * (C + 1);
-    // Two workgroups per CU whenever two fit in LDS (160 KB) and the register
-    // half-file (256 per lane) holds a staged chunk next to the state: the
-    // prologue's 128-row bf16 / 64-row fp32 tiles do not, and would spill.
-    static constexpr int min_blocks =
-        (2 * bytes <= 160 * 1024 && !(STATE_ONLY && (int)sizeof(E) * C >= 256)) ? 2 : 1;
 };
 
-template <typename E, int DK, int DV, int C, int NW, bool STATE_ONLY>
-__global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blocks)) void fwd_kernel(FwdArgs a) {
-    using L = FwdLds<E, DK, DV, C, STATE_ONLY>;
-    constexpr bool BF = sizeof(E) == 2;
+template <int DK, int DV, int C, int NW, bool STATE_ONLY>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_f32_kernel(FwdArgs a) {
+    using L = FwdLds<DK, DV, C, STATE_ONLY>;
+    using E = float;
     constexpr int NT = NW * 64;
     constexpr int NCW = DV / NW;   // state / output columns per wave
     constexpr int NCB = NCW / 16;
     constexpr int NDB = DK / 16;
     constexpr int NIB = C / 16;
     constexpr int LDK = L::LDK, LDV = L::LDV, ALD = L::ALD;
-    constexpr int NP = BF ? C / 32 : 1;  // bf16 token k-steps per chunk
     static_assert(NCW % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
-    static_assert(!BF || (DK % 32 == 0 && C % 32 == 0), "bf16 k-steps of 32");
 
     __shared__ __align__(16) E Qs[L::QK];
     __shared__ __align__(16) E Ks[L::QK];
@@ -132,7 +96,7 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
         hlane = pow_int(lam, n + 1);
     }
 
-    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
+    const int tokK = H * DK, tokV = H * DV;
     const size_t tok0 = (size_t)b * T * H + h;
     const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
     const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
@@ -156,23 +120,14 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sacc[db][cb][r] = Sin ? Sin[sidx(db, cb, r)] : 0.f;
 
-    // With one workgroup per CU the next chunk's tiles are prefetched into
-    // registers during the current chunk's math; with two, the other
-    // workgroup's math covers the load and the registers go to the MFMA loop.
-    constexpr bool PREFETCH = L::min_blocks == 1;
     TileStage<E, C, DK, NT> tq, tk;
     TileStage<E, C, DV, NT> tv;
-    auto load_chunk = [&](int t) {
-        if (!STATE_ONLY) tq.load(qb + (size_t)t * tokK, tokK, T - t, tid);
-        tk.load(kb + (size_t)t * tokK, tokK, T - t, tid);
-        tv.load(vb + (size_t)t * tokV, tokV, T - t, tid);
-    };
-    if (PREFETCH && c_begin < c_end) load_chunk(c_begin * C);
-
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         const int ceff = min(C, T - t0);
-        if (!PREFETCH) load_chunk(t0);
+        if (!STATE_ONLY) tq.load(qb + (size_t)t0 * tokK, tokK, T - t0, tid);
+        tk.load(kb + (size_t)t0 * tokK, tokK, T - t0, tid);
+        tv.load(vb + (size_t)t0 * tokV, tokV, T - t0, tid);
         __syncthreads();  // previous chunk's LDS reads are done (and pw is visible)
         if (!STATE_ONLY) {
             tq.template store<LDK>(Qs, tid);
@@ -181,7 +136,6 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
         tk.template store_scaled<LDK>(Kc, tid, [&](int row) { return row < ceff ? pw[ceff - 1 - row] : 0.f; });
         tv.template store<LDV>(Vs, tid);
         __syncthreads();
-        if (PREFETCH && c + 1 < c_end) load_chunk(t0 + C);
 
         if constexpr (!STATE_ONLY) {
             // Decay-masked score blocks, each computed by one wave and shared:
@@ -204,23 +158,13 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
                     bjb[k] = t < L::NTRI ? t - bib[k] * (bib[k] + 1) / 2 : 0;
                     AT[k] = zero4();
                 }
-                if constexpr (BF) {
 #pragma unroll
-                    for (int p = 0; p < DK / 32; ++p)
+                for (int p = 0; p < DK / 4; ++p)
 #pragma unroll
-                        for (int k = 0; k < GRP; ++k)
-                            if (k0 + k < NBW && wave + NW * (k0 + k) < ntri)
-                                AT[k] = mfma(op_row8(Ks, LDK, bjb[k] * 16 + n, 32 * p + 8 * g),
-                                             op_row8(Qs, LDK, bib[k] * 16 + n, 32 * p + 8 * g), AT[k]);
-                } else {
-#pragma unroll
-                    for (int p = 0; p < DK / 4; ++p)
-#pragma unroll
-                        for (int k = 0; k < GRP; ++k)
-                            if (k0 + k < NBW && wave + NW * (k0 + k) < ntri)
-                                AT[k] = mfma(Ks[(bjb[k] * 16 + n) * LDK + 4 * p + g],
-                                             Qs[(bib[k] * 16 + n) * LDK + 4 * p + g], AT[k]);
-                }
+                    for (int k = 0; k < GRP; ++k)
+                        if (k0 + k < NBW && wave + NW * (k0 + k) < ntri)
+                            AT[k] = mfma(Ks[(bjb[k] * 16 + n) * LDK + 4 * p + g],
+                                         Qs[(bib[k] * 16 + n) * LDK + 4 * p + g], AT[k]);
 #pragma unroll
                 for (int k = 0; k < GRP; ++k) {
                     const int t = wave + NW * (k0 + k);
@@ -232,18 +176,6 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
                     store4<E>(As + t * 16 * ALD + n * ALD + 4 * g, AT[k]);
                 }
             }
-        }
-        // This wave's value columns as MFMA fragments, shared by the intra-chunk
-        // output (as V^T, A operand) and the state update (as V, B operand):
-        // vf[cb][p] holds V[32p + 8g + e][colbase + 16 cb + n], e = 0..7.
-        bf16x8 vf[NCB][NP];
-        if constexpr (BF) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int p = 0; p < NP; ++p) vf[cb][p] = op_col8(Vs, LDV, 32 * p, colbase + cb * 16, n, g);
-        }
-        if constexpr (!STATE_ONLY) {
             __syncthreads();  // score blocks complete
 #pragma unroll 1
             for (int ib = 0; ib < NIB; ++ib) {
@@ -255,48 +187,24 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
                 f32x4 OT[NCB];
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) OT[cb] = zero4();
-                if constexpr (BF) {
-                    bf16x8 qop[DK / 32];
 #pragma unroll
-                    for (int p = 0; p < DK / 32; ++p) qop[p] = op_row_pair(Qs, LDK, irow, 32 * p + 4 * g);
+                for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                    for (int p = 0; p < DK / 32; ++p)
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb)
-                            OT[cb] = mfma(pack_acc(Sacc[2 * p][cb], Sacc[2 * p + 1][cb]), qop[p], OT[cb]);
-                } else {
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                OT[cb] = mfma(Sacc[db][cb][r], Qs[irow * LDK + db * 16 + 4 * g + r], OT[cb]);
-                }
+                        for (int r = 0; r < 4; ++r)
+                            OT[cb] = mfma(Sacc[db][cb][r], Qs[irow * LDK + db * 16 + 4 * g + r], OT[cb]);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) OT[cb][r] *= bi;
-                if constexpr (BF) {
+                for (int jb = 0; jb <= ib; ++jb) {
+                    const E* blk = As + (ib * (ib + 1) / 2 + jb) * 16 * ALD + n * ALD + 4 * g;
 #pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        if (2 * p > ib) break;
-                        const int jb = 2 * p + (g >> 1);  // this lane's key block
-                        bf16x8 aop = bf16x8{};
-                        if (jb <= ib)
-                            aop = op_row8(As + (ib * (ib + 1) / 2 + jb) * 16 * ALD, ALD, n, 8 * (g & 1));
+                    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf[cb][p], aop, OT[cb]);
-                    }
-                } else {
-                    for (int jb = 0; jb <= ib; ++jb) {
-                        const E* blk = As + (ib * (ib + 1) / 2 + jb) * 16 * ALD + n * ALD + 4 * g;
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                OT[cb] = mfma(Vs[(jb * 16 + 4 * g + r) * LDV + colbase + cb * 16 + n], blk[r], OT[cb]);
-                    }
+                        for (int r = 0; r < 4; ++r)
+                            OT[cb] = mfma(Vs[(jb * 16 + 4 * g + r) * LDV + colbase + cb * 16 + n], blk[r], OT[cb]);
                 }
                 if (irow < ceff) {
 #pragma unroll
@@ -317,25 +225,14 @@ __global__ __launch_bounds__(NW * 64, (FwdLds<E, DK, DV, C, STATE_ONLY>::min_blo
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Sacc[db][cb][r] *= Lam;
-        if constexpr (BF) {
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 kop = op_col8(Kc, LDK, 32 * p, db * 16, n, g);
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) Sacc[db][cb] = mfma(kop, vf[cb][p], Sacc[db][cb]);
-                }
-        } else {
 #pragma unroll 2
-            for (int p = 0; p < C / 4; ++p)
+        for (int p = 0; p < C / 4; ++p)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        Sacc[db][cb] = mfma(Kc[(4 * p + g) * LDK + db * 16 + n],
-                                            Vs[(4 * p + g) * LDV + colbase + cb * 16 + n], Sacc[db][cb]);
-        }
+                for (int cb = 0; cb < NCB; ++cb)
+                    Sacc[db][cb] = mfma(Kc[(4 * p + g) * LDK + db * 16 + n],
+                                        Vs[(4 * p + g) * LDV + colbase + cb * 16 + n], Sacc[db][cb]);
     }
 
     float* dst = nullptr;
@@ -420,10 +317,10 @@ FwdPlan fwd_plan(int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
     return p;
 }
 
-template <typename E, int DK, int DV, int C, int NW>
-static hipError_t launch_fwd_t(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k,
-                               const void* v, const float* lambda, const float* S0, float scale, void* o,
-                               float* S_final, void* ws, hipStream_t stream) {
+template <int DK, int DV, int C, int NW>
+static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k,
+                                 const void* v, const float* lambda, const float* S0, float scale, void* o,
+                                 float* S_final, void* ws, hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
     a.H = H;
@@ -441,14 +338,14 @@ static hipError_t launch_fwd_t(const FwdPlan& plan, int B, int T, int H, const v
     a.nc = plan.nc;
     const unsigned units = (unsigned)B * H;
     if (plan.nseg > 1) {
-        hipLaunchKernelGGL((fwd_kernel<E, DK, DV, C, NW, true>), dim3(plan.nseg - 1, units), dim3(NW * 64), 0,
+        hipLaunchKernelGGL((fwd_f32_kernel<DK, DV, C, NW, true>), dim3(plan.nseg - 1, units), dim3(NW * 64), 0,
                            stream, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         err = launch_seg_scan(S0, a.U, lambda, H, plan.nseg, plan.seg_chunks * C, DK * DV, units, stream);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((fwd_kernel<E, DK, DV, C, NW, false>), dim3(plan.nseg, units), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<DK, DV, C, NW, false>), dim3(plan.nseg, units), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -463,14 +360,17 @@ hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, in
                            dim3(256), 0, stream, S0, S_final, n);
         return hipGetLastError();
     }
-#define GLA_FWD_CASE(E_, DK_, DV_, C_, NW_)                                                            \
-    if ((sizeof(E_) == 2) == bf16_io && dk == DK_ && dv == DV_ && chunk == C_)                          \
-        return launch_fwd_t<E_, DK_, DV_, C_, NW_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, \
-                                                    ws, stream);
-    GLA_FWD_CASE(bf16, 96, 192, 128, 4)
-    GLA_FWD_CASE(bf16, 96, 192, 64, 4)
-    GLA_FWD_CASE(float, 96, 192, 64, 4)
-    GLA_FWD_CASE(float, 16, 32, 32, 2)
+    if (bf16_io) {
+        if (dk == 96 && dv == 192)
+            return launch_fwd_bf16(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, o, S_final, ws, stream);
+        return hipErrorInvalidValue;
+    }
+#define GLA_FWD_CASE(DK_, DV_, C_, NW_)                                                                   \
+    if (dk == DK_ && dv == DV_ && chunk == C_)                                                             \
+        return launch_fwd_f32<DK_, DV_, C_, NW_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, \
+                                                 stream);
+    GLA_FWD_CASE(96, 192, 64, 4)
+    GLA_FWD_CASE(16, 32, 32, 2)
 #undef GLA_FWD_CASE
     return hipErrorInvalidValue;
 }

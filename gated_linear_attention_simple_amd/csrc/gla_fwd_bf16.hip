@@ -1,0 +1,424 @@
+// gla_fwd_bf16.hip -- chunked-parallel GLA forward for bf16 q/k/v on gfx950
+// (dk = 96, dv = 192, chunks of 64 or 128 tokens).
+//
+// Method: Laplace 3B post, section "Challenge 1" (chunked GLA).  For chunk c
+// of C tokens with start state S (positions i, j in [0, C); b_i = lam^(i+1),
+// c_j = lam^(C-1-j), D_ij = lam^(i-j) for i >= j else 0):
+//     O_c   = scale * ( (Q K^T (.) D) V  +  diag(b) Q S )
+//     S_new = lam^C S + K^T diag(c) V
+// -- the per-token recurrence S_t = lam S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t
+// regrouped exactly.  A partial last chunk uses its own length in place of C.
+//
+// One workgroup per (batch, head, segment) of NW = 2 * NCG waves, NCG column
+// groups of 16 * NCB state/output columns (NCB = 3: 8 waves, two per SIMD;
+// NCB = 2: 12 waves, three per SIMD).  Waves w and w + NCG form a pair owning
+// columns [16 NCB (w % NCG), +16 NCB); inside a pair, wave h = w / NCG keeps the
+// 16-row state blocks db = 2i + h (i = 0..2) in fp32 accumulator registers for
+// the whole chunk loop.  Per chunk:
+//  * q, k, v tiles (prefetched into registers during the previous chunk) go to
+//    LDS row-major, as they sit in HBM;
+//  * each wave publishes a bf16 copy of its state half and reads its partner's,
+//    so both hold S^T for their 48 columns as MFMA operands (the accumulator's
+//    row index is the contraction index) for the inter-chunk term b (.) S^T Q^T;
+//  * the decay-masked score blocks A = (Q K^T) (.) D (16x16, lower triangle)
+//    are dealt to the waves in sets that share query fragments, masked in fp32
+//    and shared through LDS in bf16;
+//  * the pair splits the query strips for the output (h = 0 takes strip pairs
+//    whose intra-chunk work sums to the same as h = 1's) and writes O^T blocks,
+//    one strip at a time, as 4 consecutive columns per lane;
+//  * the value fragments each wave loaded for O^T += V^T A^T are reused, scaled
+//    by c_j in registers, for the state update S += K^T diag(c) V (K^T read with
+//    the gfx950 LDS transpose read).
+// Long sequences with few (batch, head) units are cut into segments exactly as
+// in the fp32 kernel: a state-only prologue, a segment scan, then this kernel.
+#include "gla_common.hpp"
+#include "gla_internal.hpp"
+#include "gla_tile.hpp"
+
+#include <stdlib.h>
+#include <type_traits>
+
+namespace gla {
+namespace {
+
+constexpr int kDK = 96, kDV = 192;
+
+template <int C, int LDK_, int NCB_>
+struct F8 {
+    static constexpr int NCB = NCB_;              // 16-column blocks per wave
+    static constexpr int NCG = kDV / (16 * NCB);  // column groups (wave pairs)
+    static constexpr int NW = 2 * NCG, NT = 64 * NW;
+    static constexpr int NIB = C / 16, NP = C / 32, NTRI = NIB * (NIB + 1) / 2;
+    static constexpr int NDW = 3;                 // 16-row state blocks per wave
+    static constexpr int LDK = LDK_, LDV = kDV + 8;
+    static constexpr int Q_BYTES = C * LDK * 2, V_BYTES = C * LDV * 2;
+    static constexpr int XS_BYTES = NW * NDW * NCB * 64 * 8;   // bf16 state halves
+    static constexpr int AS_BYTES = NTRI * 16 * 16 * 2;        // score blocks, unpadded (swizzled)
+    static constexpr int TAIL_BYTES = (C + 2) * 4 + 2 * C * 4;
+    static constexpr int XA_BYTES = XS_BYTES + AS_BYTES;   // exchange area, then score blocks
+    static constexpr int AS_OFF = XS_BYTES;
+    static_assert(2 * Q_BYTES + V_BYTES + XA_BYTES + TAIL_BYTES <= 160 * 1024, "LDS budget");
+    static constexpr int NSLOT = (NTRI + NW - 1) / NW;   // score blocks per wave
+    static_assert(kDV % (16 * NCB) == 0, "column groups");
+};
+
+// Score blocks of wave w (slot k), packed 16 * ib + jb, or -1 for an empty slot.
+// Each wave's blocks lie in at most two query strips, so per k-step it reads
+// at most two query fragments; the sets balance the 36 (C = 128) or 10
+// (C = 64) blocks of the lower triangle over the NW waves.  The first
+// score_lead<C, NW>() slots of every wave lie in its first strip.
+template <int C, int NW>
+__device__ __forceinline__ int score_block(int w, int k) {
+    if constexpr (C == 128 && NW == 8) {
+        constexpr signed char t[8][5] = {{0x70, 0x71, 0x72, 0x73, -1}, {0x74, 0x75, 0x76, 0x77, -1},
+                                         {0x60, 0x61, 0x62, 0x63, -1}, {0x64, 0x65, 0x66, 0x00, -1},
+                                         {0x50, 0x51, 0x52, 0x53, 0x54}, {0x40, 0x41, 0x42, 0x43, 0x55},
+                                         {0x30, 0x31, 0x32, 0x33, 0x44}, {0x20, 0x21, 0x22, 0x10, 0x11}};
+        return t[w][k];
+    } else if constexpr (C == 64 && NW == 8) {
+        constexpr signed char t[8][2] = {{0x30, 0x31}, {0x32, 0x33}, {0x20, 0x21}, {0x22, 0x10},
+                                         {0x11, 0x00}, {-1, -1},     {-1, -1},     {-1, -1}};
+        return t[w][k];
+    } else if constexpr (C == 128 && NW == 12) {
+        constexpr signed char t[12][3] = {{0x70, 0x71, 0x72}, {0x73, 0x74, 0x75}, {0x76, 0x77, 0x00},
+                                          {0x60, 0x61, 0x62}, {0x63, 0x64, 0x65}, {0x10, 0x11, 0x66},
+                                          {0x50, 0x51, 0x52}, {0x53, 0x54, 0x55}, {0x40, 0x41, 0x42},
+                                          {0x43, 0x44, 0x20}, {0x21, 0x22, 0x30}, {0x31, 0x32, 0x33}};
+        return t[w][k];
+    } else {
+        static_assert(C == 64 && NW == 12, "score block table");
+        constexpr signed char t[12] = {0x30, 0x31, 0x32, 0x33, 0x20, 0x21, 0x22, 0x10, 0x11, 0x00, -1, -1};
+        return k == 0 ? t[w] : -1;
+    }
+}
+
+template <int C, int NW>
+constexpr int score_lead() {
+    return C == 128 ? (NW == 12 ? 2 : 3) : 1;
+}
+
+// Element offset of row `row`, 16-byte unit `u` (0 or 1) of a 16x16 bf16 score
+// block: the unit index is flipped on rows 8..15 so the 16 rows read by one
+// lane group spread over all banks.
+__device__ __forceinline__ int as_off(int row, int u) { return row * 16 + 8 * (u ^ ((row >> 3) & 1)); }
+
+// Output of query strips 2K and 2K+1 for this wave's 16 NCB columns:
+//   O^T = b (.) S^T Q^T  +  V^T A^T, scaled and stored as bf16.
+//
+// The S^T operand of k-step p (features 32p .. 32p+31) pairs this wave's state
+// block (16 rows) with the partner's, published as bf16 in `xs_other`:
+// rows 32p + 4g + r from the HH = 0 wave, rows 32p + 16 + 4g + r from HH = 1.
+// `pws[x + 1]` = scale * lam^x and the score blocks already carry `scale`.
+template <int C, int LDK, int NCB, int K, int HH>
+__device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, const f32x4 (&Sacc)[3][NCB],
+                                         const bf16x4* xs_other, const bf16x8 (&vf)[NCB][C / 32],
+                                         const float* pws, bf16* ob, size_t tokV, int t0, int ceff, int colbase,
+                                         int n, int g) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f32x4 OT[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) OT[cb] = zero4();
+#pragma unroll
+        for (int p = 0; p < kDK / 32; ++p) {
+            const bf16x8 q0 = op_row_pair(Qs, LDK, 32 * K + 16 * u + n, 32 * p + 4 * g);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const bf16x4 own = bf16x4{to_bf16(Sacc[p][cb][0]), to_bf16(Sacc[p][cb][1]), to_bf16(Sacc[p][cb][2]),
+                                          to_bf16(Sacc[p][cb][3])};
+                const bf16x4 oth = xs_other[(p * NCB + cb) * 64];
+                bf16x8 sop;
+                if constexpr (HH == 0) sop = __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7);
+                else sop = __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
+                OT[cb] = mfma(sop, q0, OT[cb]);
+            }
+        }
+        const float bi = pws[32 * K + 16 * u + n + 2];  // scale * lam^(i+1), i = 16 (2K + u) + n
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) OT[cb][r] *= bi;
+        const int ib = 2 * K + u;
+#pragma unroll
+        for (int p = 0; p <= K; ++p) {
+            const int jb = 2 * p + (g >> 1);
+            bf16x8 aop = bf16x8{};
+            if (p < K || u == 1 || jb <= ib)
+                aop = *reinterpret_cast<const bf16x8*>(As + (ib * (ib + 1) / 2 + jb) * 256 + as_off(n, g & 1));
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf[cb][p], aop, OT[cb]);
+        }
+        const int irow = 32 * K + 16 * u + n;
+        if (irow < ceff) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                store4<bf16>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT[cb]);
+            }
+        }
+    }
+}
+
+template <int C, int LDK, int NCB, bool SO>
+__global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdArgs a) {
+    using L = F8<C, LDK, NCB>;
+    constexpr int NT = L::NT, NP = L::NP, NIB = L::NIB, LDV = L::LDV, NCG = L::NCG;
+
+    __shared__ __align__(16) bf16 Qs[SO ? 8 : C * LDK];
+    __shared__ __align__(16) bf16 Ks[C * LDK];
+    __shared__ __align__(16) bf16 Vs[C * LDV];
+    __shared__ __align__(16) unsigned char XA[SO ? 16 : L::XA_BYTES];
+    __shared__ __align__(16) float cj[2][C];  // c_j = lam^(C-1-j); for the partial last chunk lam^(ceff-1-j) or 0
+    __shared__ float pws[C + 2];              // pws[0] = 0, pws[x + 1] = scale * lam^x (x = 0..C)
+
+    const int tid = threadIdx.x;
+    // The wave index is wave-uniform: kept in scalar registers, so everything
+    // derived from it (column base, score-block slots) is scalar too.
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int h = wave / NCG, colbase = 16 * NCB * (wave % NCG);
+    const int partner = h == 0 ? wave + NCG : wave - NCG;
+    const int seg = blockIdx.x, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int hd = bh % H, b = bh / H;
+    const int c_begin = seg * a.seg_chunks;
+    const int c_end = min(a.nc, c_begin + a.seg_chunks);
+    const float lam = a.lambda[hd];
+
+    if (tid < C + 2) pws[tid] = tid == 0 ? 0.f : a.scale * pow_int(lam, tid - 1);
+    const int ctail = T % C;  // length of a partial last chunk (0: none)
+    if (tid < C) {
+        cj[0][tid] = pow_int(lam, C - 1 - tid);
+        cj[1][tid] = tid < ctail ? pow_int(lam, ctail - 1 - tid) : 0.f;
+    }
+    const float lamC = pow_int(lam, C), lamTail = pow_int(lam, ctail);
+
+    const int tokK = H * kDK, tokV = H * kDV;
+    const size_t tok0 = (size_t)b * T * H + hd;
+    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + tok0 * kDV;
+
+    // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n]
+    f32x4 Sacc[3][NCB];
+    auto sidx = [&](int i, int cb, int r) -> int {
+        return (16 * (2 * i + h) + 4 * g + r) * kDV + colbase + cb * 16 + n;
+    };
+    const float* Sin = nullptr;
+    if constexpr (!SO) {
+        if (seg == 0) Sin = a.S0 ? a.S0 + (size_t)bh * kDK * kDV : nullptr;
+        else Sin = a.U + ((size_t)bh * (a.nseg - 1) + (seg - 1)) * kDK * kDV;
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[i][cb][r] = Sin ? Sin[sidx(i, cb, r)] : 0.f;
+
+    using StageK = std::conditional_t<NT % (kDK / 8) == 0, RowStage<C, kDK, NT>, BufStage<C, kDK, NT>>;
+    using StageV = std::conditional_t<NT % (kDV / 8) == 0, RowStage<C, kDV, NT>, BufStage<C, kDV, NT>>;
+    StageK tq, tk;
+    StageV tv;
+    auto load_chunk = [&](int t, int tid) {
+        if constexpr (!SO) tq.load(qb + (size_t)t * tokK, tokK, T - t, tid);
+        tk.load(kb + (size_t)t * tokK, tokK, T - t, tid);
+        tv.load(vb + (size_t)t * tokV, tokV, T - t, tid);
+    };
+    if (c_begin < c_end) load_chunk(c_begin * C, tid);
+
+    bf16x4* XS = reinterpret_cast<bf16x4*>(XA);
+    bf16* As = reinterpret_cast<bf16*>(XA + L::AS_OFF);
+
+    // This wave's score blocks (scalar): query strips sa (slot 0) and sb (last slot).
+    constexpr int NS = L::NSLOT;
+    int blk[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) blk[k] = __builtin_amdgcn_readfirstlane(score_block<C, L::NW>(wave, k));
+    const int sa = blk[0] >= 0 ? blk[0] >> 4 : 0;
+    int sb = sa;
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        if (blk[k] >= 0) sb = blk[k] >> 4;
+    constexpr int NA = score_lead<C, L::NW>();
+    bool use_b[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) use_b[k] = k >= NA && blk[k] >= 0 && (blk[k] >> 4) != sa;
+
+    for (int c = c_begin; c < c_end; ++c) {
+        // Lane-derived addresses are recomputed every chunk from an opaque copy
+        // of the thread index instead of being kept live across the loop.
+        int tid_v = threadIdx.x;
+        asm volatile("" : "+v"(tid_v));
+        const int tid = tid_v, lane = tid % 64, n = lane % 16, g = lane / 16;
+        auto xs_at = [&](int w, int i, int cb) { return XS + ((w * 3 + i) * NCB + cb) * 64 + lane; };
+        const int t0 = c * C;
+        const int ceff = min(C, T - t0);
+        __syncthreads();  // the previous chunk's LDS reads are done
+        if constexpr (!SO) tq.template store<LDK>(Qs, tid);
+        tk.template store<LDK>(Ks, tid);
+        tv.template store<LDV>(Vs, tid);
+        if constexpr (!SO) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    *xs_at(wave, i, cb) = bf16x4{to_bf16(Sacc[i][cb][0]), to_bf16(Sacc[i][cb][1]),
+                                                 to_bf16(Sacc[i][cb][2]), to_bf16(Sacc[i][cb][3])};
+        }
+        __syncthreads();
+        if (c + 1 < c_end) load_chunk(t0 + C, tid);
+
+        // This wave's value fragments: vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
+        // (loaded after the score blocks, which do not need them).
+        bf16x8 vf[NCB][NP];
+        auto load_vf = [&]() {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int p = 0; p < NP; ++p) vf[cb][p] = op_col8(Vs, LDV, 32 * p, colbase + 16 * cb, n, g);
+        };
+        if constexpr (SO) load_vf();
+
+        if constexpr (!SO) {
+            // Score blocks: AT[k][4g + r][n] = q_(16 ib + n) . k_(16 jb + 4g + r).
+            f32x4 AT[NS];
+#pragma unroll
+            for (int k = 0; k < NS; ++k) AT[k] = zero4();
+#pragma unroll
+            for (int p = 0; p < kDK / 32; ++p) {
+                const bf16x8 qa = op_row8(Qs, LDK, 16 * sa + n, 32 * p + 8 * g);
+                const bf16x8 qc = op_row8(Qs, LDK, 16 * sb + n, 32 * p + 8 * g);
+#pragma unroll
+                for (int k = 0; k < NS; ++k) {
+                    const int jb = blk[k] >= 0 ? blk[k] & 15 : 0;
+                    const bf16x8 q = (k < NA || !use_b[k]) ? qa : qc;
+                    AT[k] = mfma(op_row8(Ks, LDK, 16 * jb + n, 32 * p + 8 * g), q, AT[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                if (blk[k] < 0) continue;
+                const int ib = blk[k] >> 4, jb = blk[k] & 15;
+                // scale * D_ij = scale * lam^(i-j) for i >= j, else 0, with
+                // i - j = 16 (ib - jb) + n - 4g - r: one table read per element.
+                const int d1 = 16 * (ib - jb) + n - 4 * g + 1;
+                f32x4 x = AT[k];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] *= pws[max(d1 - r, 0)];
+                *reinterpret_cast<bf16x4*>(As + (ib * (ib + 1) / 2 + jb) * 256 + as_off(n, g >> 1) + 4 * (g & 1)) =
+                    bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
+            }
+            load_vf();
+            __syncthreads();  // score blocks complete
+
+            const bf16x4* xo = xs_at(partner, 0, 0);
+            if constexpr (C == 128) {
+                if (h == 0) {
+                    out_pair<C, LDK, NCB, 0, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 3, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                } else {
+                    out_pair<C, LDK, NCB, 1, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 2, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                }
+            } else {
+                if (h == 0) out_pair<C, LDK, NCB, 0, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                else out_pair<C, LDK, NCB, 1, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            }
+        }
+
+        // State advance: S <- lam^ceff S + K^T diag(c) V, with c_j folded into
+        // this wave's value fragments.
+        const float Lam = ceff == C ? lamC : lamTail;
+        const float* cjc = cj[ceff == C ? 0 : 1];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(cjc + 32 * p + 8 * g);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(cjc + 32 * p + 8 * g + 4);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[cb][p][e] = to_bf16(to_f32(vf[cb][p][e]) * (e < 4 ? c0[e] : c1[e - 4]));
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[i][cb][r] *= Lam;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const bf16x8 kop = op_col8(Ks, LDK, 32 * p, 16 * (2 * i + h), n, g);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) Sacc[i][cb] = mfma(kop, vf[cb][p], Sacc[i][cb]);
+            }
+    }
+
+    float* dst = nullptr;
+    if (SO) dst = a.U + ((size_t)bh * (a.nseg - 1) + seg) * kDK * kDV;
+    else if (seg == a.nseg - 1 && a.S_final) dst = a.S_final + (size_t)bh * kDK * kDV;
+    if (dst) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[sidx(i, cb, r)] = Sacc[i][cb][r];
+    }
+}
+
+template <int C, int LDK, int NCB>
+hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k, const void* v,
+                    const float* lambda, const float* S0, float scale, void* o, float* S_final, void* ws,
+                    hipStream_t stream) {
+    FwdArgs a{};
+    a.T = T;
+    a.H = H;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lambda = lambda;
+    a.S0 = S0;
+    a.scale = scale;
+    a.o = o;
+    a.S_final = S_final;
+    a.U = static_cast<float*>(ws);
+    a.nseg = plan.nseg;
+    a.seg_chunks = plan.seg_chunks;
+    a.nc = plan.nc;
+    const unsigned units = (unsigned)B * H;
+    if (plan.nseg > 1) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, true>), dim3(plan.nseg - 1, units), dim3(F8<C, LDK, NCB>::NT),
+                           0, stream, a);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        err = launch_seg_scan(S0, a.U, lambda, H, plan.nseg, plan.seg_chunks * C, kDK * kDV, units, stream);
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, false>), dim3(plan.nseg, units), dim3(F8<C, LDK, NCB>::NT), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
+                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                           void* ws, hipStream_t stream) {
+    // Waves per workgroup: 12 (two 16-column blocks each) or 8 (three each).
+    int ncb = 2;
+    if (const char* e = getenv("GLA_FWD_NCB")) ncb = atoi(e) == 3 ? 3 : 2;  // tuning override (sweeps)
+#define GLA_CASE(C_, NCB_)                                                                                          \
+    if (chunk == C_ && ncb == NCB_)                                                                                  \
+        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, stream);
+    GLA_CASE(128, 2)
+    GLA_CASE(128, 3)
+    GLA_CASE(64, 2)
+    GLA_CASE(64, 3)
+#undef GLA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -6,6 +6,20 @@
 
 namespace gla {
 
+struct FwdArgs {
+    int T, H;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* lambda;
+    const float* S0;
+    float scale;
+    void* o;
+    float* S_final;
+    float* U;          // [B*H][nseg-1][DK][DV]: segment-local end states, then segment start states
+    int nseg, seg_chunks, nc;
+};
+
 struct FwdPlan {
     int nc;          // chunks in the sequence
     int nseg;        // sequence segments run in parallel
@@ -19,6 +33,11 @@ hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, in
                       int chunk, const void* q, const void* k, const void* v, const float* lambda,
                       const float* S0, float scale, void* o, float* S_final, void* ws,
                       hipStream_t stream);
+
+// bf16 forward (dk = 96, dv = 192, chunk 64 or 128): prologue, scan and main launches.
+hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
+                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                           void* ws, hipStream_t stream);
 
 // Sequence segments run in parallel (at most this many per sequence).
 constexpr int kMaxSegments = 16;

@@ -99,13 +99,15 @@ struct TileStage {
     static_assert(D % VEC == 0, "rows are whole 16-byte pieces");
     uint4 r[PER];
 
-    __device__ __forceinline__ void load(const E* base, size_t tok_stride, int valid, int tid) {
+    // Offsets inside one tile stay in 32 bits (rows * tok_stride < 2^31 for every
+    // supported shape), so no 64-bit address per piece stays live.
+    __device__ __forceinline__ void load(const E* base, int tok_stride, int valid, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int p = tid + NT * i;
             const int row = p / KC, kc = p % KC;
             if ((NP % NT == 0 || p < NP) && row < valid)
-                r[i] = *reinterpret_cast<const uint4*>(base + (size_t)row * tok_stride + kc * VEC);
+                r[i] = *reinterpret_cast<const uint4*>(base + (row * tok_stride + kc * VEC));
             else
                 r[i] = make_uint4(0u, 0u, 0u, 0u);
         }
@@ -141,6 +143,85 @@ struct TileStage {
             }
             *reinterpret_cast<uint4*>(dst + row * LD + (p % KC) * VEC) = w;
         }
+    }
+};
+
+// Buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9-family parts.
+constexpr int kBufWord3 = 0x00020000;
+
+// Stages a ROWS x D bf16 tile like TileStage, with buffer loads: the tile base
+// and its byte range live in one scalar resource and each piece needs only a
+// 32-bit offset.  Rows at or past `valid` lie outside the range and read as
+// zeros (the hardware returns 0 for out-of-range buffer loads).
+template <int ROWS, int D, int NT>
+struct BufStage {
+    static constexpr int KC = D / 8;
+    static constexpr int NP = ROWS * KC;
+    static constexpr int PER = (NP + NT - 1) / NT;
+    static_assert(D % 8 == 0, "rows are whole 16-byte pieces");
+    uint4 r[PER];
+
+    __device__ __forceinline__ void load(const bf16* base, int tok_stride, int valid, int tid) {
+        const unsigned rows = (unsigned)(valid < ROWS ? valid : ROWS);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)(rows * (unsigned)tok_stride * 2u), kBufWord3);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = tid + NT * i;
+            if (NP % NT == 0 || p < NP) {
+                const int row = p / KC, kc = p % KC;
+                r[i] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((unsigned)(row * tok_stride + kc * 8) * 2u), 0, 0));
+            } else {
+                r[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    template <int LD>
+    __device__ __forceinline__ void store(bf16* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = tid + NT * i;
+            if (NP % NT != 0 && p >= NP) continue;
+            *reinterpret_cast<uint4*>(dst + (p / KC) * LD + (p % KC) * 8) = r[i];
+        }
+    }
+};
+
+// BufStage for thread counts that are a multiple of the 16-byte pieces per row:
+// thread t always stages column piece t % KC of rows t / KC + i * (NT / KC), so
+// one 32-bit offset per thread serves every load (the row step rides in the
+// scalar offset) and the LDS stores differ by compile-time constants.
+template <int ROWS, int D, int NT>
+struct RowStage {
+    static constexpr int KC = D / 8;
+    static constexpr int RSTEP = NT / KC;
+    static constexpr int PER = (ROWS + RSTEP - 1) / RSTEP;
+    static_assert(D % 8 == 0 && NT % KC == 0, "whole rows per round");
+    uint4 r[PER];
+
+    __device__ __forceinline__ void load(const bf16* base, int tok_stride, int valid, int tid) {
+        const unsigned rows = (unsigned)(valid < ROWS ? valid : ROWS);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)(rows * (unsigned)tok_stride * 2u), kBufWord3);
+        const int row0 = tid / KC;
+        const int vo = (int)((unsigned)(row0 * tok_stride + (tid % KC) * 8) * 2u);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (ROWS % RSTEP == 0 || row0 + i * RSTEP < ROWS)
+                r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rs, vo, (int)((unsigned)(i * RSTEP * tok_stride) * 2u), 0));
+            else
+                r[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    template <int LD>
+    __device__ __forceinline__ void store(bf16* dst, int tid) const {
+        const int row0 = tid / KC;
+        bf16* d = dst + row0 * LD + (tid % KC) * 8;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (ROWS % RSTEP == 0 || row0 + i * RSTEP < ROWS) *reinterpret_cast<uint4*>(d + i * RSTEP * LD) = r[i];
     }
 };
 

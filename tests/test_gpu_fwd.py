@@ -74,6 +74,18 @@ def test_segment_split_equivalence(nseg, monkeypatch):
     _run_and_check(gi.workloads()[1], seed=200 + nseg, B=1, T=2000, chunk=64, s0_var=0.01)
 
 
+@pytest.mark.parametrize("ncb", ["2", "3"])
+@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("nseg", [1, 3])
+def test_bf16_wave_layouts(ncb, chunk, nseg, monkeypatch):
+    """Both bf16 workgroup layouts (12 waves with 32-column pairs, 8 waves with
+    48-column pairs), with and without sequence segments, ragged tail, S0."""
+    monkeypatch.setenv("GLA_FWD_NCB", ncb)
+    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(nseg))
+    _run_and_check(gi.workloads()[1], seed=300 + 7 * int(ncb) + chunk + nseg, B=2, T=1000, chunk=chunk,
+                   s0_var=0.01)
+
+
 def test_train_batch_forward_chunk64_and_128():
     w = gi.workloads()[2]
     for chunk in (128, 64):
