@@ -40,6 +40,12 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// A wave-uniform fp32 value moved to a scalar register (bit pattern preserved;
+// the readfirstlane builtin itself operates on 32-bit integers).
+__device__ __forceinline__ float uniform_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // lambda^n for integer n >= 0 with lambda^0 = 1 (also for lambda = 0): binary
 // powering in double (at most ~17 squarings for the sizes used here, relative
 // error ~1e-15), rounded once to fp32.  No ratio of powers is ever formed and

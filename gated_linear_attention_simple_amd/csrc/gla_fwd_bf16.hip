@@ -190,7 +190,10 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         cj[0][tid] = pow_int(lam, C - 1 - tid);
         cj[1][tid] = tid < ctail ? pow_int(lam, ctail - 1 - tid) : 0.f;
     }
-    const float lamC = pow_int(lam, C), lamTail = pow_int(lam, ctail);
+    // uniform: kept in scalar registers (a spilled copy would be reloaded behind
+    // the in-flight tile loads)
+    const float lamC = uniform_f32(pow_int(lam, C));
+    const float lamTail = uniform_f32(pow_int(lam, ctail));
 
     const int tokK = H * kDK, tokV = H * kDV;
     const size_t tok0 = (size_t)b * T * H + hd;
@@ -254,9 +257,15 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         auto xs_at = [&](int w, int i, int cb) { return XS + ((w * 3 + i) * NCB + cb) * 64 + lane; };
         const int t0 = c * C;
         const int ceff = min(C, T - t0);
+        const float* cjc = cj[ceff == C ? 0 : 1];
         __syncthreads();  // the previous chunk's LDS reads are done
-        if constexpr (!SO) tq.template store<LDK>(Qs, tid);
-        tk.template store<LDK>(Ks, tid);
+        if constexpr (!SO) {
+            tq.template store<LDK>(Qs, tid);
+            tk.template store<LDK>(Ks, tid);
+        } else {
+            // state only: keys are needed only scaled, K^T diag(c)
+            tk.template store_scaled<LDK>(Ks, tid, [&](int row) { return cjc[row]; });
+        }
         tv.template store<LDV>(Vs, tid);
         if constexpr (!SO) {
 #pragma unroll
@@ -267,7 +276,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                                                  to_bf16(Sacc[i][cb][2]), to_bf16(Sacc[i][cb][3])};
         }
         __syncthreads();
-        if (c + 1 < c_end) load_chunk(t0 + C, tid);
+        if (c + 1 < c_end) load_chunk(t0 + C, tid);  // next chunk's tiles, consumed at its start
 
         // This wave's value fragments: vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
         // (loaded after the score blocks, which do not need them).
@@ -310,7 +319,16 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                     bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
             }
             load_vf();
-            __syncthreads();  // score blocks complete
+            __syncthreads();  // score blocks complete; every wave holds its value fragments
+
+            // The value tile is dead now: reuse it for the c_j-scaled keys of the
+            // state update, K^T diag(c) (complete at the barrier before the update).
+            bf16* Kc = Vs;
+            for (int pc = tid; pc < C * (kDK / 8); pc += NT) {
+                const int row = pc / (kDK / 8), col = (pc % (kDK / 8)) * 8;
+                *reinterpret_cast<uint4*>(Kc + row * LDK + col) =
+                    scale_bf16x8(*reinterpret_cast<const uint4*>(Ks + row * LDK + col), cjc[row]);
+            }
 
             const bf16x4* xo = xs_at(partner, 0, 0);
             if constexpr (C == 128) {
@@ -327,19 +345,14 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
             }
         }
 
-        // State advance: S <- lam^ceff S + K^T diag(c) V, with c_j folded into
-        // this wave's value fragments.
-        const float Lam = ceff == C ? lamC : lamTail;
-        const float* cjc = cj[ceff == C ? 0 : 1];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const f32x4 c0 = *reinterpret_cast<const f32x4*>(cjc + 32 * p + 8 * g);
-            const f32x4 c1 = *reinterpret_cast<const f32x4*>(cjc + 32 * p + 8 * g + 4);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vf[cb][p][e] = to_bf16(to_f32(vf[cb][p][e]) * (e < 4 ? c0[e] : c1[e - 4]));
+        // State advance: S <- lam^ceff S + (diag(c) K)^T V, the scaled keys in
+        // the old value tile (main) or the key tile (state only).
+        const bf16* Ksc = Ks;
+        if constexpr (!SO) {
+            __syncthreads();  // scaled keys complete
+            Ksc = Vs;
         }
+        const float Lam = ceff == C ? lamC : lamTail;
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
@@ -350,7 +363,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         for (int p = 0; p < NP; ++p)
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
-                const bf16x8 kop = op_col8(Ks, LDK, 32 * p, 16 * (2 * i + h), n, g);
+                const bf16x8 kop = op_col8(Ksc, LDK, 32 * p, 16 * (2 * i + h), n, g);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) Sacc[i][cb] = mfma(kop, vf[cb][p], Sacc[i][cb]);
             }

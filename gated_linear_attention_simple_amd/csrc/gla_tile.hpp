@@ -146,6 +146,14 @@ struct TileStage {
     }
 };
 
+// bf16x8 scaled by one fp32 factor, rounded back to bf16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 raw, float c) {
+    bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = to_bf16(to_f32(x[e]) * c);
+    return __builtin_bit_cast(uint4, x);
+}
+
 // Buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9-family parts.
 constexpr int kBufWord3 = 0x00020000;
 
@@ -186,6 +194,16 @@ struct BufStage {
             *reinterpret_cast<uint4*>(dst + (p / KC) * LD + (p % KC) * 8) = r[i];
         }
     }
+    // Row-scaled copy: dst[row] = coef(row) * tile[row], rounded to bf16.
+    template <int LD, typename F>
+    __device__ __forceinline__ void store_scaled(bf16* dst, int tid, F coef) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int p = tid + NT * i;
+            if (NP % NT != 0 && p >= NP) continue;
+            *reinterpret_cast<uint4*>(dst + (p / KC) * LD + (p % KC) * 8) = scale_bf16x8(r[i], coef(p / KC));
+        }
+    }
 };
 
 // BufStage for thread counts that are a multiple of the 16-byte pieces per row:
@@ -222,6 +240,15 @@ struct RowStage {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
             if (ROWS % RSTEP == 0 || row0 + i * RSTEP < ROWS) *reinterpret_cast<uint4*>(d + i * RSTEP * LD) = r[i];
+    }
+    template <int LD, typename F>
+    __device__ __forceinline__ void store_scaled(bf16* dst, int tid, F coef) const {
+        const int row0 = tid / KC;
+        bf16* d = dst + row0 * LD + (tid % KC) * 8;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (ROWS % RSTEP == 0 || row0 + i * RSTEP < ROWS)
+                *reinterpret_cast<uint4*>(d + i * RSTEP * LD) = scale_bf16x8(r[i], coef(row0 + i * RSTEP));
     }
 };
 
