@@ -35,24 +35,8 @@
 
 namespace gla {
 
-constexpr int kNPart = 8;  // dlam partial slots per (batch*head, chunk)
-
 // ---------------------------------------------------------------- state passes
 
-struct StateArgs {
-    int T, H;
-    const void* x;        // [B][T][H][DK]: keys (forward pass) or queries (reverse pass)
-    const void* y;        // [B][T][H][DV]: values (forward pass) or output gradients (reverse pass)
-    const float* lambda;
-    float xscale;         // extra row factor on x: 1 (forward) or the readout scale (reverse)
-    const float* S_edge;  // state entering the pass: S0 (forward) or dS_T (reverse); nullable
-    float* U;             // [BH][nseg-1][DK][DV]: segment-local states, then segment start states
-    void* snap;           // [BH][NC][DK][DV] (E): per-chunk snapshots written by the emit pass
-    float* S_out;         // reverse emit pass: dS0 (nullable)
-    const void* sbar;     // reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
-    float* part;          // reverse emit pass: dlam partials, slot 0
-    int nseg, seg_chunks, nc;
-};
 
 // One workgroup runs one (batch*head, segment) of the chain
 //   forward:  S <- lam^ceff S + (diag(lam^(ceff-1-j)) K)^T V    over chunks upward
@@ -231,22 +215,6 @@ __global__ __launch_bounds__(256) void rev_scan_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------- gradient kernels
 
-struct GradArgs {
-    int T, H;
-    const void* q;
-    const void* k;
-    const void* v;
-    const void* d_o;
-    const float* lambda;
-    float scale;
-    const void* sbar;  // [BH][NC][DK][DV] (E): chunk start states
-    const void* gbar;  // [BH][NC][DK][DV] (E): chunk end state gradients
-    void* dq;
-    void* dk;
-    void* dv;
-    float* part;       // [BH][NC][kNPart]
-    int nc;
-};
 
 template <typename E, int DK, int DV, int C>
 struct GradShape {
@@ -259,7 +227,7 @@ struct GradShape {
     static constexpr int LDK = DK + PAD, LDV = DV + PAD;
     static constexpr int NDB = DK / 16, NVB = DV / 16;
     static constexpr int NPAIR = BF ? ST / 32 : ST / 16;  // k-steps of the tile (pairs of blocks for bf16)
-    static_assert(1 + 2 * NSUB <= kNPart, "partial slots");
+    static_assert(kChainSlots + 2 * NSUB <= kNPart, "partial slots");
 };
 
 // Decay factor and its lam-derivative for a non-negative distance d:
@@ -304,7 +272,7 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dkdv_kerne
     const int t0 = cid * C;
     const int ceff = min(C, T - t0);
     const int kt0 = jt * ST;  // chunk-local first key of the tile
-    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + 1 + jt;
+    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + kChainSlots + jt;
     if (kt0 >= ceff) {
         if (tid == 0) *part = 0.f;
         return;
@@ -486,7 +454,7 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(
     const int t0 = cid * C;
     const int ceff = min(C, T - t0);
     const int qt0 = it * ST;
-    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + 1 + NSUB + it;
+    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + kChainSlots + NSUB + it;
     if (qt0 >= ceff) {
         if (tid == 0) *part = 0.f;
         return;
@@ -605,17 +573,20 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(
     block_partial(a.scale * t3, red, NW, part);
 }
 
-// dlam[h] = sum over batch, chunks and partial slots, in a fixed order (double).
+// dlam[h] = sum over batch, chunks and partial slots (chain slots [0, nchain),
+// gradient slots [kChainSlots, kChainSlots + ngrad)), in a fixed order (double).
 __global__ __launch_bounds__(256) void dlambda_reduce_kernel(const float* __restrict__ part, int B, int H, int nc,
-                                                             int nslots, float* __restrict__ dlambda) {
+                                                             int nchain, int ngrad, float* __restrict__ dlambda) {
     __shared__ double red[256];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
+    const int nslots = nchain + ngrad;
     const long per_b = (long)nc * nslots;
     double s = 0.0;
     for (long e = tid; e < (long)B * per_b; e += 256) {
         const long bb = e / per_b, rest = e % per_b;
-        const long c = rest / nslots, slot = rest % nslots;
+        const long c = rest / nslots, k = rest % nslots;
+        const long slot = k < nchain ? k : kChainSlots + (k - nchain);
         s += (double)part[(((size_t)bb * H + h) * nc + c) * kNPart + slot];
     }
     red[tid] = s;
@@ -690,15 +661,32 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     s.xscale = 1.f;
     s.S_edge = S0;
     s.snap = sbar;
+    constexpr bool BF = sizeof(E) == 2;
+    auto chain = [&](bool rev, bool emit, unsigned gx) -> hipError_t {
+        if constexpr (BF) {
+            return launch_chain_bf16(C, rev, emit, s, gx, units, stream);
+        } else {
+            if (!rev && !emit)
+                hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, false>), dim3(gx, units), dim3(NW * 64), 0,
+                                   stream, s);
+            else if (!rev && emit)
+                hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, true>), dim3(gx, units), dim3(NW * 64), 0,
+                                   stream, s);
+            else if (rev && !emit)
+                hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, false>), dim3(gx, units), dim3(NW * 64), 0,
+                                   stream, s);
+            else
+                hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, true>), dim3(gx, units), dim3(NW * 64), 0,
+                                   stream, s);
+            return hipGetLastError();
+        }
+    };
     if (nseg > 1) {
-        hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, false>), dim3(nseg - 1, units), dim3(NW * 64), 0,
-                           stream, s);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = chain(false, false, nseg - 1)) != hipSuccess) return err;
         if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) != hipSuccess)
             return err;
     }
-    hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, false, true>), dim3(nseg, units), dim3(NW * 64), 0, stream, s);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = chain(false, true, nseg)) != hipSuccess) return err;
     // reverse chain: snapshots Gbar, dS0, <Gbar, Sbar> partials
     s.x = q;
     s.y = d_o;
@@ -709,15 +697,12 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     s.sbar = sbar;
     s.part = part;
     if (nseg > 1) {
-        hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, false>), dim3(nseg - 1, units), dim3(NW * 64), 0,
-                           stream, s);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = chain(true, false, nseg - 1)) != hipSuccess) return err;
         hipLaunchKernelGGL(rev_scan_kernel, dim3((dkdv / 4 + 255) / 256, units), dim3(256), 0, stream, dST, U, lambda,
                            H, nseg, plan.seg_chunks * C, T, dkdv);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((state_kernel<E, DK, DV, C, NW, true, true>), dim3(nseg, units), dim3(NW * 64), 0, stream, s);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = chain(true, true, nseg)) != hipSuccess) return err;
 
     GradArgs ga{};
     ga.T = T;
@@ -736,14 +721,18 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     ga.part = part;
     ga.nc = plan.nc;
     using GS = GradShape<E, DK, DV, C>;
-    const dim3 ggrid(plan.nc * GS::NSUB, units);
-    hipLaunchKernelGGL((grad_dkdv_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((grad_dq_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if constexpr (BF) {
+        if ((err = launch_grad_bf16(C, ga, units, stream)) != hipSuccess) return err;
+    } else {
+        const dim3 ggrid(plan.nc * GS::NSUB, units);
+        hipLaunchKernelGGL((grad_dkdv_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((grad_dq_kernel<E, DK, DV, C>), ggrid, dim3(GS::NT), 0, stream, ga);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if (dlambda) {
         hipLaunchKernelGGL(dlambda_reduce_kernel, dim3(H), dim3(256), 0, stream, part, B, H, plan.nc,
-                           1 + 2 * GS::NSUB, dlambda);
+                           BF ? kChainSlots : 1, 2 * GS::NSUB, dlambda);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;

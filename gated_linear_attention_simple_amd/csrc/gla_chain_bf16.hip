@@ -1,0 +1,226 @@
+// gla_chain_bf16.hip -- the backward's chunk-state chains for bf16 q/k/v/do
+// (dk = 96, dv = 192, chunks of 64 or 128 tokens) on gfx950.
+//
+// Laplace 3B post, sections "Challenge 1" and "Challenge 3": the chunked
+// backward needs, for every chunk c, the state entering it (Sbar_c) and the
+// gradient of the loss with respect to the state leaving it (Gbar_c):
+//   forward:  S <- lam^ceff S + K^T diag(c) V,                   c_j = lam^(ceff-1-j)
+//   reverse:  G <- lam^ceff G + Q^T diag(scale b) dO,            b_i = lam^(i+1)
+// plus, on the reverse emit pass, the chunk's term of dlam through lam^ceff:
+//   ceff lam^(ceff-1) <Gbar_c, Sbar_c>.
+// LOCAL passes start from zero and write each segment's local result; EMIT
+// passes start from the scanned segment state and write, before each chunk's
+// update, the state as that chunk's bf16 snapshot.
+//
+// Work decomposition: one workgroup of 12 waves per (batch*head, segment), as
+// in the bf16 forward -- wave w keeps the state rows 16 (2i + h) .. +16
+// (h = w / 6, i = 0..2) of the 32 columns [32 (w % 6), +32) in fp32 accumulator
+// registers; x (k or q, pre-scaled per row) and y (v or do) tiles are staged
+// row-major in LDS with buffer loads prefetched one chunk ahead; both MFMA
+// operands are token-contracted and come from the LDS transpose read.  A
+// snapshot goes through an LDS staging tile so it leaves as coalesced 16-byte
+// row pieces; the reverse pass stages fp32 and takes the <Gbar, Sbar> product
+// from the fp32 values during that copy (one partial per wave and chunk).
+#include "gla_common.hpp"
+#include "gla_internal.hpp"
+#include "gla_tile.hpp"
+
+namespace gla {
+namespace {
+
+constexpr int kDK = 96, kDV = 192;
+constexpr int kNCB = 2, kNCG = 6, kNW = 12, kNT = 768;
+
+template <int C, bool REV, bool EMIT>
+__global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
+    constexpr int NP = C / 32;
+    constexpr int LDK = kDK + 8, LDV = kDV + 8;
+    constexpr bool STAGE32 = EMIT && REV;     // fp32 staging (the <Gbar, Sbar> term)
+    constexpr int LDS32 = kDV + 4;
+    __shared__ __align__(16) bf16 Xs[C * LDK];
+    __shared__ __align__(16) bf16 Ys[C * LDV];
+    __shared__ __align__(16) bf16 Sb[EMIT && !STAGE32 ? kDK * LDV : 8];
+    __shared__ __align__(16) float Sf[STAGE32 ? kDK * LDS32 : 4];
+    __shared__ __align__(16) float xc[2][C];  // row factors of x: full chunk, partial last chunk
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int h = wave / kNCG, colbase = 32 * (wave % kNCG);
+    const int seg = blockIdx.x + ((!EMIT && REV) ? 1 : 0);
+    const int bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int hd = bh % H, b = bh / H;
+    const int c_begin = seg * a.seg_chunks;
+    const int c_end = min(a.nc, c_begin + a.seg_chunks);
+    const float lam = a.lambda[hd];
+
+    const int ctail = T % C;  // length of a partial last chunk (0: none)
+    if (tid < C) {
+        if constexpr (REV) {
+            const float bi = a.xscale * pow_int(lam, tid + 1);
+            xc[0][tid] = bi;
+            xc[1][tid] = tid < ctail ? bi : 0.f;
+        } else {
+            xc[0][tid] = pow_int(lam, C - 1 - tid);
+            xc[1][tid] = tid < ctail ? pow_int(lam, ctail - 1 - tid) : 0.f;
+        }
+    }
+    const float lamC = uniform_f32(pow_int(lam, C));
+    const float lamTail = uniform_f32(pow_int(lam, ctail));
+    // d(lam^ceff)/dlam for the <Gbar, Sbar> term
+    const float dlamC = uniform_f32((float)C * pow_int(lam, C - 1));
+    const float dlamTail = uniform_f32(ctail > 0 ? (float)ctail * pow_int(lam, ctail - 1) : 0.f);
+
+    const int tokX = H * kDK, tokY = H * kDV;
+    const size_t tok0 = (size_t)b * T * H + hd;
+    const bf16* xb = static_cast<const bf16*>(a.x) + tok0 * kDK;
+    const bf16* yb = static_cast<const bf16*>(a.y) + tok0 * kDV;
+
+    // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n]
+    f32x4 Sacc[3][kNCB];
+    auto sidx = [&](int i, int cb, int r) -> int {
+        return (16 * (2 * i + h) + 4 * g + r) * kDV + colbase + cb * 16 + n;
+    };
+    const float* Sin = nullptr;
+    if constexpr (EMIT) {
+        if (!REV) Sin = seg == 0 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg - 1) * kDK * kDV;
+        else Sin = seg == a.nseg - 1 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg) * kDK * kDV;
+        if (Sin && Sin == a.S_edge) Sin += (size_t)bh * kDK * kDV;
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[i][cb][r] = Sin ? Sin[sidx(i, cb, r)] : 0.f;
+
+    RowStage<C, kDK, kNT> tx;
+    RowStage<C, kDV, kNT> ty;
+    const int nchunks = c_end - c_begin;
+    auto chunk_of = [&](int ci) { return REV ? c_end - 1 - ci : c_begin + ci; };
+    auto load_chunk = [&](int c, int tid) {
+        const int t = c * C;
+        tx.load(xb + (size_t)t * tokX, tokX, T - t, tid);
+        ty.load(yb + (size_t)t * tokY, tokY, T - t, tid);
+    };
+    if (nchunks > 0) load_chunk(chunk_of(0), tid);
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+        // lane-derived addresses are recomputed per chunk, not held across the loop
+        int tid_v = threadIdx.x;
+        asm volatile("" : "+v"(tid_v));
+        const int tid = tid_v, lane = tid % 64, n = lane % 16, g = lane / 16;
+        const int c = chunk_of(ci);
+        const int t0 = c * C;
+        const int ceff = min(C, T - t0);
+        const float* xcc = xc[ceff == C ? 0 : 1];
+        __syncthreads();  // the previous chunk's LDS reads are done
+        tx.template store_scaled<LDK>(Xs, tid, [&](int row) { return xcc[row]; });
+        ty.template store<LDV>(Ys, tid);
+        if constexpr (EMIT) {
+            // this chunk's snapshot: the state before its update
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * (2 * i + h) + 4 * g + r, col = colbase + 16 * cb + n;
+                        if constexpr (STAGE32) Sf[row * LDS32 + col] = Sacc[i][cb][r];
+                        else Sb[row * LDV + col] = to_bf16(Sacc[i][cb][r]);
+                    }
+        }
+        __syncthreads();
+        if (ci + 1 < nchunks) load_chunk(chunk_of(ci + 1), tid);
+
+        if constexpr (EMIT) {
+            // Copy the snapshot out as 16-byte row pieces (96 rows x 24 pieces).
+            bf16* snap = static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV;
+            float dot = 0.f;
+            for (int pc = tid; pc < kDK * (kDV / 8); pc += kNT) {
+                const int row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
+                bf16x8 x;
+                if constexpr (STAGE32) {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col);
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col + 4);
+                    const bf16x8 sb = *reinterpret_cast<const bf16x8*>(
+                        static_cast<const bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV + row * kDV + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = to_bf16(lo[e]);
+                        x[e + 4] = to_bf16(hi[e]);
+                        dot = fmaf(lo[e], to_f32(sb[e]), dot);
+                        dot = fmaf(hi[e], to_f32(sb[e + 4]), dot);
+                    }
+                } else {
+                    x = *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col);
+                }
+                *reinterpret_cast<bf16x8*>(snap + row * kDV + col) = x;
+            }
+            if constexpr (STAGE32) {
+                dot = wave_sum(dot);
+                if (lane == 0) a.part[((size_t)bh * a.nc + c) * kNPart + wave] = (ceff == C ? dlamC : dlamTail) * dot;
+            }
+        }
+
+        // S <- lam^ceff S + X^T Y over the chunk's tokens (X rows pre-scaled)
+        const float Lam = ceff == C ? lamC : lamTail;
+        bf16x8 yf[kNCB][NP];
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) yf[cb][p] = op_col8(Ys, LDV, 32 * p, colbase + 16 * cb, n, g);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[i][cb][r] *= Lam;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const bf16x8 xop = op_col8(Xs, LDK, 32 * p, 16 * (2 * i + h), n, g);
+#pragma unroll
+                for (int cb = 0; cb < kNCB; ++cb) Sacc[i][cb] = mfma(xop, yf[cb][p], Sacc[i][cb]);
+            }
+    }
+
+    float* dst = nullptr;
+    if (!EMIT) dst = a.U + ((size_t)bh * (a.nseg - 1) + (REV ? seg - 1 : seg)) * kDK * kDV;
+    else if (REV && seg == 0 && a.S_out) dst = a.S_out + (size_t)bh * kDK * kDV;
+    if (dst) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[sidx(i, cb, r)] = Sacc[i][cb][r];
+    }
+}
+
+template <int C, bool REV, bool EMIT>
+hipError_t launch_chain_c(const StateArgs& s, unsigned grid_x, unsigned units, hipStream_t stream) {
+    hipLaunchKernelGGL((chain_bf16_kernel<C, REV, EMIT>), dim3(grid_x, units), dim3(kNT), 0, stream, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chain_bf16(int chunk, bool rev, bool emit, const StateArgs& s, unsigned grid_x, unsigned units,
+                             hipStream_t stream) {
+#define GLA_CHAIN(C_)                                                                    \
+    if (chunk == C_) {                                                                   \
+        if (!rev && !emit) return launch_chain_c<C_, false, false>(s, grid_x, units, stream); \
+        if (!rev && emit) return launch_chain_c<C_, false, true>(s, grid_x, units, stream);   \
+        if (rev && !emit) return launch_chain_c<C_, true, false>(s, grid_x, units, stream);   \
+        return launch_chain_c<C_, true, true>(s, grid_x, units, stream);                      \
+    }
+    GLA_CHAIN(128)
+    GLA_CHAIN(64)
+#undef GLA_CHAIN
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -47,6 +47,52 @@ constexpr int kMaxSegments = 16;
 hipError_t launch_seg_scan(const float* S0, float* U, const float* lambda, int H, int nseg, int seg_tokens,
                            int dkdv, unsigned units, hipStream_t stream);
 
+// dlam partials: [B*H][chunks][kNPart] fp32.  Slots [0, kChainSlots) hold the
+// chain term ceff lam^(ceff-1) <Gbar, Sbar> (one per chain wave; the fp32 chain
+// uses slot 0 only), slots [kChainSlots, kChainSlots + 2 * tiles) the gradient
+// kernels' terms.  All are summed per head in a fixed order.
+constexpr int kChainSlots = 12;
+constexpr int kNPart = 16;
+
+struct StateArgs {
+    int T, H;
+    const void* x;        // [B][T][H][DK]: keys (forward pass) or queries (reverse pass)
+    const void* y;        // [B][T][H][DV]: values (forward pass) or output gradients (reverse pass)
+    const float* lambda;
+    float xscale;         // extra row factor on x: 1 (forward) or the readout scale (reverse)
+    const float* S_edge;  // state entering the pass: S0 (forward) or dS_T (reverse); nullable
+    float* U;             // [BH][nseg-1][DK][DV]: segment-local states, then segment start states
+    void* snap;           // [BH][NC][DK][DV] (E): per-chunk snapshots written by the emit pass
+    float* S_out;         // reverse emit pass: dS0 (nullable)
+    const void* sbar;     // reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
+    float* part;          // reverse emit pass: dlam partials
+    int nseg, seg_chunks, nc;
+};
+
+// bf16 chains (dk = 96, dv = 192, chunk 64 or 128); grid (grid_x, units).
+hipError_t launch_chain_bf16(int chunk, bool rev, bool emit, const StateArgs& s, unsigned grid_x, unsigned units,
+                             hipStream_t stream);
+
+struct GradArgs {
+    int T, H;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* d_o;
+    const float* lambda;
+    float scale;
+    const void* sbar;  // [BH][NC][DK][DV] (E): chunk start states
+    const void* gbar;  // [BH][NC][DK][DV] (E): chunk end state gradients
+    void* dq;
+    void* dk;
+    void* dv;
+    float* part;       // [BH][NC][kNPart]
+    int nc;
+};
+
+// bf16 gradient kernels (dk = 96, dv = 192, chunk 64 or 128): dK/dV then dQ.
+hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipStream_t stream);
+
 struct BwdPlan {
     int nc, nseg, seg_chunks;
     size_t snap_bytes;  // per-chunk snapshots (one array for states, one for state gradients)
