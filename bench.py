@@ -122,13 +122,14 @@ class FwdLeg:
         self.stream = torch.cuda.current_stream()
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         self.fn = gla.load().gla_fwd_chunked
-        self.args = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]),
+        self.head = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]),
                      p(x["S0"]), ctypes.c_float(x["scale"]), p(self.o), p(self.S), p(self.ws),
-                     ctypes.c_size_t(need), ctypes.c_void_p(self.stream.cuda_stream))
+                     ctypes.c_size_t(need))
         self.gla = gla
 
-    def __call__(self):
-        st = self.fn(*self.args)
+    def __call__(self, stream=None):
+        s = self.stream if stream is None else stream
+        st = self.fn(*self.head, ctypes.c_void_p(s.cuda_stream))
         if st != 0:
             raise RuntimeError(f"gla_fwd_chunked: {self.gla.status_str(st)}")
 
@@ -204,40 +205,33 @@ class DecodeLeg:
             raise RuntimeError(f"gla_decode_step: {self.gla.status_str(st)}")
 
 
-def time_fwd(torch, leg, K, W):
+def time_region(torch, stream, fn, K, W):
+    """W untimed calls, then K calls bracketed by synchronisation and by HIP events
+    recorded on the stream the library launches on.  Returns (wall seconds, GPU
+    seconds of the region); no per-call host work is added inside the region."""
     for _ in range(W):
-        leg()
+        fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(leg.stream)
-        leg()
-        b.record(leg.stream)
+    a.record(stream)
+    for _ in range(K):
+        fn()
+    b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) * 1e-3 for a, b in evs]
-    return wall, per
+    return time.perf_counter() - t0, a.elapsed_time(b) * 1e-3
 
 
 def time_decode(torch, leg, K, W):
-    for s in range(W):
+    """K decode steps (each: one launch per layer) -> (wall, GPU region seconds)."""
+    step = [0]
+
+    def one_step():
         for layer in range(leg.layers):
-            leg.launch(layer, s)
-    torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(leg.layers)] for _ in range(K)]
-    t0 = time.perf_counter()
-    for s in range(K):
-        for layer in range(leg.layers):
-            a, b = evs[s][layer]
-            a.record(leg.stream)
-            leg.launch(layer, W + s)
-            b.record(leg.stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) * 1e-3 for row in evs for a, b in row]
-    return wall, per
+            leg.launch(layer, step[0])
+        step[0] += 1
+
+    return time_region(torch, leg.stream, one_step, K, W)
 
 
 def cpu_baseline_fwd(gi, w, seed, budget_s=12.0):
@@ -334,7 +328,7 @@ def ingest_counters(fetch_csv, write_csv):
         copies = [v for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
         ref = max(copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
         fac[counter] = (1 << 30) / (ref * 1024.0)
-        groups = {"fwd": ["fwd_kernel", "seg_scan"], "decode": ["decode_kernel"]}
+        groups = {"fwd": ["fwd_bf16_kernel", "seg_scan"], "decode": ["decode_kernel"]}
         for key, pats in groups.items():
             # per call: sum over the kernels one call launches, averaged over the 3 calls
             tot = sum(v for (d, name), v in by.items() if any(pt in name for pt in pats))
@@ -373,9 +367,9 @@ def main():
     # ---- forward leg (Laplace layer)
     w1 = ws[1]
     fleg = FwdLeg(gla, gi, torch, w1, 1, args.chunk)
-    f_wall, f_per = time_fwd(torch, fleg, K, W)
+    f_wall, f_gpu = time_region(torch, fleg.stream, fleg, K, W)
+    f_avg = f_gpu / K
     f_ms = f_wall / K * 1e3
-    f_avg = sum(f_per) / len(f_per)
     f_bytes = FWD_BYTES_PER_TOKEN_HEAD[w1.dtype] * fleg.token_heads
     f_flops = fwd_flops_per_token_head(args.chunk) * fleg.token_heads
     f_ach = f_bytes / f_avg / 1e9
@@ -394,7 +388,8 @@ def main():
                      "alg_bytes_per_launch": f_bytes, "avg_launch_us": f_avg * 1e6,
                      "mfma_tflops": f_flops / f_avg / 1e12,
                      "mfma_frac": f_flops / f_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS},
-        "fwd": {"ms_per_call_wall": f_ms, "avg_launch_us": f_avg * 1e6, "min_launch_us": min(f_per) * 1e6},
+        "fwd": {"ms_per_call_wall": f_ms, "avg_call_us_events": f_avg * 1e6,
+                "timing": "K back-to-back gla_fwd_chunked calls; HIP events on the launch stream around the region"},
     }
 
     # ---- training-step legs (mixer-train workload, chunk 128 and 64)
@@ -403,8 +398,8 @@ def main():
     result["train"] = {}
     for C in (() if args.no_train else (128, 64)):
         tleg = TrainLeg(gla, gi, torch, w2, 2, C)
-        t_wall, t_per = time_fwd(torch, tleg, K, W)
-        t_avg = sum(t_per) / len(t_per)
+        t_wall, t_gpu = time_region(torch, tleg.stream, tleg, K, W)
+        t_avg = t_gpu / K
         tb = train_bytes_per_token_head(C) * tleg.token_heads
         tf = train_flops_per_token_head(C) * tleg.token_heads
         leg = {"value": K * tleg.tokens / t_wall, "unit": "tokens/s", "ms_per_step": t_wall / K * 1e3,
@@ -423,10 +418,10 @@ def main():
     if not args.no_decode:
         w4 = ws[4]
         dleg = DecodeLeg(gla, gi, torch, w4, 4)
-        d_wall, d_per = time_decode(torch, dleg, K, W)
+        d_wall, d_gpu = time_decode(torch, dleg, K, W)
         d_ms = d_wall / K * 1e3
         per_launch_bytes = DEC_BYTES_PER_SEQ_HEAD * w4.B * w4.H
-        d_avg = sum(d_per) / len(d_per)
+        d_avg = d_gpu / (K * w4.decode_layers)
         d_ach = per_launch_bytes / d_avg / 1e9
         result["decode"] = {
             "value": per_launch_bytes * w4.decode_layers * K / d_wall / 1e9, "unit": "GB/s",
