@@ -54,7 +54,7 @@ struct F8 {
     static constexpr int Q_BYTES = C * LDK * 2, V_BYTES = C * LDV * 2;
     static constexpr int XS_BYTES = NW * NDW * NCB * 64 * 8;   // bf16 state halves
     static constexpr int AS_BYTES = NTRI * 16 * 16 * 2;        // score blocks, unpadded (swizzled)
-    static constexpr int TAIL_BYTES = (C + 2) * 4 + 2 * C * 4;
+    static constexpr int TAIL_BYTES = (C + 2) * 4 + 2 * C * 4 + 8;
     static constexpr int XA_BYTES = XS_BYTES + AS_BYTES;   // exchange area, then score blocks
     static constexpr int AS_OFF = XS_BYTES;
     static_assert(2 * Q_BYTES + V_BYTES + XA_BYTES + TAIL_BYTES <= 160 * 1024, "LDS budget");
@@ -169,6 +169,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
     __shared__ __align__(16) unsigned char XA[SO ? 16 : L::XA_BYTES];
     __shared__ __align__(16) float cj[2][C];  // c_j = lam^(C-1-j); for the partial last chunk lam^(ceff-1-j) or 0
     __shared__ float pws[C + 2];              // pws[0] = 0, pws[x + 1] = scale * lam^x (x = 0..C)
+    __shared__ float lamv[2];                 // lam^C, lam^(length of a partial last chunk)
 
     const int tid = threadIdx.x;
     // The wave index is wave-uniform: kept in scalar registers, so everything
@@ -190,10 +191,9 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         cj[0][tid] = pow_int(lam, C - 1 - tid);
         cj[1][tid] = tid < ctail ? pow_int(lam, ctail - 1 - tid) : 0.f;
     }
-    // uniform: kept in scalar registers (a spilled copy would be reloaded behind
-    // the in-flight tile loads)
-    const float lamC = uniform_f32(pow_int(lam, C));
-    const float lamTail = uniform_f32(pow_int(lam, ctail));
+    // Chunk decay read from LDS at its use (a register copy held across the loop
+    // gets spilled, and its reload would wait behind the in-flight tile loads).
+    if (tid < 2) lamv[tid] = pow_int(lam, tid == 0 ? C : ctail);
 
     const int tokK = H * kDK, tokV = H * kDV;
     const size_t tok0 = (size_t)b * T * H + hd;
@@ -258,6 +258,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         const int t0 = c * C;
         const int ceff = min(C, T - t0);
         const float* cjc = cj[ceff == C ? 0 : 1];
+        const bool need_state = SO || c + 1 < c_end || (seg == a.nseg - 1 && a.S_final != nullptr);
         __syncthreads();  // the previous chunk's LDS reads are done
         if constexpr (!SO) {
             tq.template store<LDK>(Qs, tid);
@@ -324,7 +325,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
             // The value tile is dead now: reuse it for the c_j-scaled keys of the
             // state update, K^T diag(c) (complete at the barrier before the update).
             bf16* Kc = Vs;
-            for (int pc = tid; pc < C * (kDK / 8); pc += NT) {
+            for (int pc = tid; need_state && pc < C * (kDK / 8); pc += NT) {
                 const int row = pc / (kDK / 8), col = (pc % (kDK / 8)) * 8;
                 *reinterpret_cast<uint4*>(Kc + row * LDK + col) =
                     scale_bf16x8(*reinterpret_cast<const uint4*>(Ks + row * LDK + col), cjc[row]);
@@ -347,12 +348,15 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
 
         // State advance: S <- lam^ceff S + (diag(c) K)^T V, the scaled keys in
         // the old value tile (main) or the key tile (state only).
+        // The state after a segment's last chunk is needed only by the sequence's
+        // last segment (S_final); other segments hand over through the scan.
+        if (!need_state) continue;
         const bf16* Ksc = Ks;
         if constexpr (!SO) {
             __syncthreads();  // scaled keys complete
             Ksc = Vs;
         }
-        const float Lam = ceff == C ? lamC : lamTail;
+        const float Lam = lamv[ceff == C ? 0 : 1];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
