@@ -60,7 +60,7 @@ const char* gla_status_str(int status) {
 
 size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
-    return gla::fwd_plan(B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
+    return gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
 }
 
 int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
@@ -71,7 +71,7 @@ int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, c
     if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda)))
         return GLA_ERR_INVALID_ARG;
     if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
-    const gla::FwdPlan plan = gla::fwd_plan(B, T, H, dk, dv, chunk, kPlanCUs);
+    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
     if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
     const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
                                            scale, o, S_final, ws, static_cast<hipStream_t>(stream));

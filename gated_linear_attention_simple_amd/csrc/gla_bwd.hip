@@ -618,7 +618,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
     BwdPlan p{};
-    const FwdPlan f = fwd_plan(B, T, H, dk, dv, chunk, num_cu);
+    const FwdPlan f = fwd_plan(bf16_io, B, T, H, dk, dv, chunk, num_cu);
     p.nc = f.nc;
     p.nseg = f.nseg;
     p.seg_chunks = f.seg_chunks;

@@ -297,7 +297,7 @@ bool fwd_supported(bool bf16_io, int dk, int dv, int chunk) {
            (dk == 16 && dv == 32 && chunk == 32 && !bf16_io);
 }
 
-FwdPlan fwd_plan(int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
+FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
     FwdPlan p{};
     p.nc = T > 0 ? (T + chunk - 1) / chunk : 0;
     const long units = (long)B * H;
@@ -313,7 +313,8 @@ FwdPlan fwd_plan(int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
     nseg = nseg > p.nc && p.nc > 0 ? p.nc : nseg;
     p.seg_chunks = p.nc > 0 ? (p.nc + nseg - 1) / nseg : 0;
     p.nseg = p.nc > 0 ? (p.nc + p.seg_chunks - 1) / p.seg_chunks : 1;
-    p.ws_bytes = (size_t)units * (p.nseg - 1) * dk * dv * sizeof(float);
+    // fp32 segment states; the bf16 path adds a bf16 copy of each start state
+    p.ws_bytes = (size_t)units * (p.nseg - 1) * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
     return p;
 }
 

@@ -17,26 +17,31 @@
 // the whole chunk loop.  Per chunk:
 //  * q, k, v tiles (prefetched into registers during the previous chunk) go to
 //    LDS row-major, as they sit in HBM;
-//  * each wave publishes a bf16 copy of its state half and reads its partner's,
-//    so both hold S^T for their 48 columns as MFMA operands (the accumulator's
-//    row index is the contraction index) for the inter-chunk term b (.) S^T Q^T;
 //  * the decay-masked score blocks A = (Q K^T) (.) D (16x16, lower triangle)
 //    are dealt to the waves in sets that share query fragments, masked in fp32
 //    and shared through LDS in bf16;
+//  * each wave publishes a bf16 copy of its state half and reads its partner's,
+//    so both hold S^T for their 16 NCB columns as MFMA operands (the
+//    accumulator's row index is the contraction index) for the inter-chunk term
+//    b (.) S^T Q^T;
 //  * the pair splits the query strips for the output (h = 0 takes strip pairs
 //    whose intra-chunk work sums to the same as h = 1's) and writes O^T blocks,
 //    one strip at a time, as 4 consecutive columns per lane;
-//  * the value fragments each wave loaded for O^T += V^T A^T are reused, scaled
-//    by c_j in registers, for the state update S += K^T diag(c) V (K^T read with
-//    the gfx950 LDS transpose read).
-// Long sequences with few (batch, head) units are cut into segments exactly as
-// in the fp32 kernel: a state-only prologue, a segment scan, then this kernel.
+//  * the value fragments each wave loaded for O^T += V^T A^T are reused for the
+//    state update S += (diag(c) K)^T V, with the keys scaled by c_j in place
+//    once the score blocks are done.
+// Long sequences with few (batch, head) units are cut into segments as in the
+// fp32 kernel: a state-only prologue, a segment scan, then this kernel.  Here
+// the segment states sit in the workspace in register order (16-byte pieces),
+// and a one-chunk segment reads its start state as the bf16 copy the scan
+// leaves (the only form it uses, so the result is unchanged).
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
 
 #include <stdlib.h>
 #include <type_traits>
+#include <utility>
 
 namespace gla {
 namespace {
@@ -68,7 +73,7 @@ struct F8 {
 // (C = 64) blocks of the lower triangle over the NW waves.  The first
 // score_lead<C, NW>() slots of every wave lie in its first strip.
 template <int C, int NW>
-__device__ __forceinline__ int score_block(int w, int k) {
+__host__ __device__ constexpr int score_block(int w, int k) {
     if constexpr (C == 128 && NW == 8) {
         constexpr signed char t[8][5] = {{0x70, 0x71, 0x72, 0x73, -1}, {0x74, 0x75, 0x76, 0x77, -1},
                                          {0x60, 0x61, 0x62, 0x63, -1}, {0x64, 0x65, 0x66, 0x00, -1},
@@ -90,6 +95,33 @@ __device__ __forceinline__ int score_block(int w, int k) {
         constexpr signed char t[12] = {0x30, 0x31, 0x32, 0x33, 0x20, 0x21, 0x22, 0x10, 0x11, 0x00, -1, -1};
         return k == 0 ? t[w] : -1;
     }
+}
+
+// The same table for a wave-uniform w without a memory load: each slot's entries
+// packed as bytes into two 64-bit constants (waves 0..7, 8..15), so the lookup
+// is a scalar select and shift.  (A table read would be a vector load, and its
+// wait would also wait for every tile load issued before it.)
+template <int C, int NW>
+__host__ __device__ constexpr unsigned long long score_word(int k, int half) {
+    unsigned long long r = 0;
+    for (int j = 0; j < 8; ++j) {
+        const int w = 8 * half + j;
+        const int v = w < NW ? score_block<C, NW>(w, k) : -1;
+        r |= (unsigned long long)(unsigned char)(signed char)v << (8 * j);
+    }
+    return r;
+}
+
+template <int C, int NW, int K>
+struct ScoreWords {
+    static constexpr unsigned long long lo = score_word<C, NW>(K, 0), hi = score_word<C, NW>(K, 1);
+};
+
+template <int C, int NW, int... K>
+__device__ __forceinline__ void score_blocks_uniform(int w, int* blk, std::integer_sequence<int, K...>) {
+    ((blk[K] = (int)(signed char)(unsigned char)((w < 8 ? ScoreWords<C, NW, K>::lo : ScoreWords<C, NW, K>::hi) >>
+                                                 (8 * (w & 7)))),
+     ...);
 }
 
 template <int C, int NW>
@@ -183,8 +215,101 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
     const int hd = bh % H, b = bh / H;
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nc, c_begin + a.seg_chunks);
-    const float lam = a.lambda[hd];
 
+    const int tokK = H * kDK, tokV = H * kDV;
+    const size_t tok0 = (size_t)b * T * H + hd;
+    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + tok0 * kDV;
+
+    // This wave's score blocks (scalar): query strips sa (slot 0) and sb (last slot).
+    constexpr int NS = L::NSLOT;
+    int blk[NS];
+    score_blocks_uniform<C, L::NW>(wave, blk, std::make_integer_sequence<int, NS>{});
+    const int sa = blk[0] >= 0 ? blk[0] >> 4 : 0;
+    int sb = sa;
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        if (blk[k] >= 0) sb = blk[k] >> 4;
+    constexpr int NA = score_lead<C, L::NW>();
+    bool use_b[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) use_b[k] = k >= NA && blk[k] >= 0 && (blk[k] >> 4) != sa;
+
+    // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n].  Segment
+    // states in the workspace are kept in this register order ("fragment
+    // order": float4 ((wave * 3 + i) * NCB + cb) * 64 + lane holds Sacc[i][cb]),
+    // so they move as 16-byte (fp32) or 8-byte (bf16) pieces.
+    f32x4 Sacc[3][NCB];
+    auto sidx = [&](int i, int cb, int r) -> int {
+        return (16 * (2 * i + h) + 4 * g + r) * kDV + colbase + cb * 16 + n;
+    };
+    auto fidx = [&](int i, int cb) -> int { return ((wave * 3 + i) * NCB + cb) * 64 + lane; };
+    // The start state is consumed only in the chunk loop (its bf16 copy for the
+    // partner wave): its loads stay in flight until then (no conversion here, no
+    // select on the loaded values; it is requested before the tiles, so a wait
+    // for it never waits for a tile).  Packed bf16 start states are unpacked there.
+    bool sin_packed = false;
+    if constexpr (!SO) {
+        if (seg == 0) {
+            // S0 through a buffer descriptor whose range is empty without S0:
+            // the loads then return zeros.
+            const float* s0 = a.S0 ? a.S0 + (size_t)bh * kDK * kDV : a.lambda;
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s0), 0,
+                                                              a.S0 ? kDK * kDV * 4 : 0, kBufWord3);
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Sacc[i][cb][r] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * sidx(i, cb, r), 0, 0));
+        } else {
+            const size_t st = ((size_t)bh * (a.nseg - 1) + (seg - 1)) * kDK * kDV;
+            // A one-chunk segment only reads its start state as a bf16 MFMA
+            // operand, unless it must also produce the final state.  The four
+            // bf16 values stay packed in the first two registers for now.
+            if (a.seg_chunks == 1 && !(seg == a.nseg - 1 && a.S_final)) {
+                const uint2* ub = reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.Ub) + st);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const uint2 x = ub[fidx(i, cb)];
+                        Sacc[i][cb] = f32x4{__builtin_bit_cast(float, x.x), __builtin_bit_cast(float, x.y), 0.f, 0.f};
+                    }
+                sin_packed = true;
+            } else {
+                const f32x4* u = reinterpret_cast<const f32x4*>(a.U + st);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) Sacc[i][cb] = u[fidx(i, cb)];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) Sacc[i][cb] = zero4();
+    }
+
+    // The first chunk's tiles, right after the start state.
+    using StageK = std::conditional_t<NT % (kDK / 8) == 0, RowStage<C, kDK, NT>, BufStage<C, kDK, NT>>;
+    using StageV = std::conditional_t<NT % (kDV / 8) == 0, RowStage<C, kDV, NT>, BufStage<C, kDV, NT>>;
+    StageK tq, tk;
+    StageV tv;
+    // Tiles of the chunk at token t, rows [0, valid) read.
+    auto load_chunk = [&](int t, int valid, int tid) {
+        if constexpr (!SO) tq.load(qb + (size_t)t * tokK, tokK, valid, tid);
+        tk.load(kb + (size_t)t * tokK, tokK, valid, tid);
+        tv.load(vb + (size_t)t * tokV, tokV, valid, tid);
+    };
+    if (c_begin < c_end) load_chunk(c_begin * C, T - c_begin * C, tid);
+
+    const float lam = a.lambda[hd];
     if (tid < C + 2) pws[tid] = tid == 0 ? 0.f : a.scale * pow_int(lam, tid - 1);
     const int ctail = T % C;  // length of a partial last chunk (0: none)
     if (tid < C) {
@@ -195,58 +320,8 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
     // gets spilled, and its reload would wait behind the in-flight tile loads).
     if (tid < 2) lamv[tid] = pow_int(lam, tid == 0 ? C : ctail);
 
-    const int tokK = H * kDK, tokV = H * kDV;
-    const size_t tok0 = (size_t)b * T * H + hd;
-    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
-    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
-    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
-    bf16* ob = static_cast<bf16*>(a.o) + tok0 * kDV;
-
-    // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n]
-    f32x4 Sacc[3][NCB];
-    auto sidx = [&](int i, int cb, int r) -> int {
-        return (16 * (2 * i + h) + 4 * g + r) * kDV + colbase + cb * 16 + n;
-    };
-    const float* Sin = nullptr;
-    if constexpr (!SO) {
-        if (seg == 0) Sin = a.S0 ? a.S0 + (size_t)bh * kDK * kDV : nullptr;
-        else Sin = a.U + ((size_t)bh * (a.nseg - 1) + (seg - 1)) * kDK * kDV;
-    }
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[i][cb][r] = Sin ? Sin[sidx(i, cb, r)] : 0.f;
-
-    using StageK = std::conditional_t<NT % (kDK / 8) == 0, RowStage<C, kDK, NT>, BufStage<C, kDK, NT>>;
-    using StageV = std::conditional_t<NT % (kDV / 8) == 0, RowStage<C, kDV, NT>, BufStage<C, kDV, NT>>;
-    StageK tq, tk;
-    StageV tv;
-    auto load_chunk = [&](int t, int tid) {
-        if constexpr (!SO) tq.load(qb + (size_t)t * tokK, tokK, T - t, tid);
-        tk.load(kb + (size_t)t * tokK, tokK, T - t, tid);
-        tv.load(vb + (size_t)t * tokV, tokV, T - t, tid);
-    };
-    if (c_begin < c_end) load_chunk(c_begin * C, tid);
-
     bf16x4* XS = reinterpret_cast<bf16x4*>(XA);
     bf16* As = reinterpret_cast<bf16*>(XA + L::AS_OFF);
-
-    // This wave's score blocks (scalar): query strips sa (slot 0) and sb (last slot).
-    constexpr int NS = L::NSLOT;
-    int blk[NS];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) blk[k] = __builtin_amdgcn_readfirstlane(score_block<C, L::NW>(wave, k));
-    const int sa = blk[0] >= 0 ? blk[0] >> 4 : 0;
-    int sb = sa;
-#pragma unroll
-    for (int k = 0; k < NS; ++k)
-        if (blk[k] >= 0) sb = blk[k] >> 4;
-    constexpr int NA = score_lead<C, L::NW>();
-    bool use_b[NS];
-#pragma unroll
-    for (int k = 0; k < NS; ++k) use_b[k] = k >= NA && blk[k] >= 0 && (blk[k] >> 4) != sa;
 
     for (int c = c_begin; c < c_end; ++c) {
         // Lane-derived addresses are recomputed every chunk from an opaque copy
@@ -263,21 +338,35 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         if constexpr (!SO) {
             tq.template store<LDK>(Qs, tid);
             tk.template store<LDK>(Ks, tid);
-        } else {
-            // state only: keys are needed only scaled, K^T diag(c)
-            tk.template store_scaled<LDK>(Ks, tid, [&](int row) { return cjc[row]; });
-        }
-        tv.template store<LDV>(Vs, tid);
-        if constexpr (!SO) {
+            tv.template store<LDV>(Vs, tid);
+            if (sin_packed) {  // first chunk only: bf16 start state -> fp32 (exact)
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        // (element values taken first: a bit cast applied to a vector
+                        // element itself reads element 0 with this compiler)
+                        const float fx = Sacc[i][cb][0], fy = Sacc[i][cb][1];
+                        const unsigned x = __builtin_bit_cast(unsigned, fx);
+                        const unsigned y = __builtin_bit_cast(unsigned, fy);
+                        Sacc[i][cb] = f32x4{__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xffff0000u),
+                                            __builtin_bit_cast(float, y << 16), __builtin_bit_cast(float, y & 0xffff0000u)};
+                    }
+                sin_packed = false;
+            }
 #pragma unroll
             for (int i = 0; i < 3; ++i)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
                     *xs_at(wave, i, cb) = bf16x4{to_bf16(Sacc[i][cb][0]), to_bf16(Sacc[i][cb][1]),
                                                  to_bf16(Sacc[i][cb][2]), to_bf16(Sacc[i][cb][3])};
+        } else {
+            // state only: keys are needed only scaled, K^T diag(c)
+            tk.template store_scaled<LDK>(Ks, tid, [&](int row) { return cjc[row]; });
+            tv.template store<LDV>(Vs, tid);
         }
         __syncthreads();
-        if (c + 1 < c_end) load_chunk(t0 + C, tid);  // next chunk's tiles, consumed at its start
+        if (c + 1 < c_end) load_chunk(t0 + C, T - (t0 + C), tid);  // next chunk's tiles, consumed at its start
 
         // This wave's value fragments: vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
         // (loaded after the score blocks, which do not need them).
@@ -320,15 +409,14 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                     bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
             }
             load_vf();
-            __syncthreads();  // score blocks complete; every wave holds its value fragments
+            __syncthreads();  // score blocks complete
 
-            // The value tile is dead now: reuse it for the c_j-scaled keys of the
-            // state update, K^T diag(c) (complete at the barrier before the update).
-            bf16* Kc = Vs;
+            // The keys are only needed scaled now, K^T diag(c) for the state
+            // update: scaled in place (complete at the barrier before the update).
             for (int pc = tid; need_state && pc < C * (kDK / 8); pc += NT) {
                 const int row = pc / (kDK / 8), col = (pc % (kDK / 8)) * 8;
-                *reinterpret_cast<uint4*>(Kc + row * LDK + col) =
-                    scale_bf16x8(*reinterpret_cast<const uint4*>(Ks + row * LDK + col), cjc[row]);
+                uint4* kp = reinterpret_cast<uint4*>(Ks + row * LDK + col);
+                *kp = scale_bf16x8(*kp, cjc[row]);
             }
 
             const bf16x4* xo = xs_at(partner, 0, 0);
@@ -346,16 +434,13 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
             }
         }
 
-        // State advance: S <- lam^ceff S + (diag(c) K)^T V, the scaled keys in
-        // the old value tile (main) or the key tile (state only).
+        // State advance: S <- lam^ceff S + (diag(c) K)^T V, with the scaled keys
+        // in the key tile.
         // The state after a segment's last chunk is needed only by the sequence's
         // last segment (S_final); other segments hand over through the scan.
         if (!need_state) continue;
+        if constexpr (!SO) __syncthreads();  // scaled keys complete
         const bf16* Ksc = Ks;
-        if constexpr (!SO) {
-            __syncthreads();  // scaled keys complete
-            Ksc = Vs;
-        }
         const float Lam = lamv[ceff == C ? 0 : 1];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
@@ -373,16 +458,62 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
             }
     }
 
-    float* dst = nullptr;
-    if (SO) dst = a.U + ((size_t)bh * (a.nseg - 1) + seg) * kDK * kDV;
-    else if (seg == a.nseg - 1 && a.S_final) dst = a.S_final + (size_t)bh * kDK * kDV;
-    if (dst) {
+    if (SO) {
+        // segment-local end state, fragment order
+        f32x4* u = reinterpret_cast<f32x4*>(a.U + ((size_t)bh * (a.nseg - 1) + seg) * kDK * kDV);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) u[fidx(i, cb)] = Sacc[i][cb];
+    } else if (seg == a.nseg - 1 && a.S_final) {
+        float* dst = a.S_final + (size_t)bh * kDK * kDV;
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[sidx(i, cb, r)] = Sacc[i][cb][r];
+    }
+}
+
+// Segment scan over fragment-ordered states:  U[s] <- lam^L U[s-1] + U[s]
+// (U[-1] = S0), i.e. the start state of segment s + 1, as in the fp32 path's
+// scan.  One thread per float4 of the state.  One-chunk segments need their
+// start state only as bf16 (written to Ub); fp32 is kept where a segment runs
+// a state chain (several chunks) or produces the final state (the last one).
+template <int NCB>
+__global__ __launch_bounds__(256) void seg_scan_frag_kernel(const float* __restrict__ S0, float* __restrict__ U,
+                                                            bf16* __restrict__ Ub, const float* __restrict__ lambda,
+                                                            int H, int nseg, int seg_chunks, int seg_tokens,
+                                                            int last_f32) {
+    constexpr int NCG = kDV / (16 * NCB), NF = kDK * kDV / 4;
+    const int bh = blockIdx.y;
+    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= NF) return;
+    const float lamL = pow_int(lambda[bh % H], seg_tokens);
+    f32x4 run = zero4();
+    if (S0) {
+        const int lane = f % 64, rest = f / 64;
+        const int cb = rest % NCB, i = (rest / NCB) % 3, wave = rest / (3 * NCB);
+        const int h = wave / NCG, col = 16 * NCB * (wave % NCG) + 16 * cb + lane % 16;
+        const float* s0 = S0 + (size_t)bh * kDK * kDV + (16 * (2 * i + h) + 4 * (lane / 16)) * kDV + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) run[r] = s0[r * kDV];
+    }
+    f32x4* u = reinterpret_cast<f32x4*>(U + (size_t)bh * (nseg - 1) * kDK * kDV) + f;
+    bf16x4* ub = reinterpret_cast<bf16x4*>(Ub + (size_t)bh * (nseg - 1) * kDK * kDV) + f;
+    f32x4 x[kMaxSegments - 1];
+#pragma unroll
+    for (int s = 0; s < kMaxSegments - 1; ++s)
+        if (s < nseg - 1) x[s] = u[s * NF];
+#pragma unroll
+    for (int s = 0; s < kMaxSegments - 1; ++s) {
+        if (s < nseg - 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) run[e] = fmaf(lamL, run[e], x[s][e]);
+            if (seg_chunks > 1 || (last_f32 && s == nseg - 2)) u[s * NF] = run;
+            if (seg_chunks == 1) ub[s * NF] = bf16x4{to_bf16(run[0]), to_bf16(run[1]), to_bf16(run[2]), to_bf16(run[3])};
+        }
     }
 }
 
@@ -402,6 +533,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     a.o = o;
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
+    a.Ub = static_cast<char*>(ws) + (size_t)B * H * (plan.nseg > 1 ? plan.nseg - 1 : 0) * kDK * kDV * sizeof(float);
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
     a.nc = plan.nc;
@@ -411,7 +543,10 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
                            0, stream, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        err = launch_seg_scan(S0, a.U, lambda, H, plan.nseg, plan.seg_chunks * C, kDK * kDV, units, stream);
+        hipLaunchKernelGGL(seg_scan_frag_kernel<NCB>, dim3((kDK * kDV / 4 + 255) / 256, units), dim3(256), 0, stream,
+                           S0, a.U, static_cast<bf16*>(a.Ub), lambda, H, plan.nseg, plan.seg_chunks,
+                           plan.seg_chunks * C, S_final != nullptr ? 1 : 0);
+        err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, false>), dim3(plan.nseg, units), dim3(F8<C, LDK, NCB>::NT), 0,

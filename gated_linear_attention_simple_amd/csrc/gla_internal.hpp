@@ -16,7 +16,8 @@ struct FwdArgs {
     float scale;
     void* o;
     float* S_final;
-    float* U;          // [B*H][nseg-1][DK][DV]: segment-local end states, then segment start states
+    float* U;          // [B*H][nseg-1][DK*DV]: segment-local end states, then segment start states
+    void* Ub;          // bf16 copies of the start states (bf16 path, one-chunk segments), or null
     int nseg, seg_chunks, nc;
 };
 
@@ -24,11 +25,11 @@ struct FwdPlan {
     int nc;          // chunks in the sequence
     int nseg;        // sequence segments run in parallel
     int seg_chunks;  // chunks per segment (the last segment may hold fewer)
-    size_t ws_bytes; // segment-local states: B*H*(nseg-1)*dk*dv fp32
+    size_t ws_bytes; // segment states: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path)
 };
 
 bool fwd_supported(bool bf16_io, int dk, int dv, int chunk);
-FwdPlan fwd_plan(int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
 hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv,
                       int chunk, const void* q, const void* k, const void* v, const float* lambda,
                       const float* S0, float scale, void* o, float* S_final, void* ws,

@@ -160,7 +160,8 @@ constexpr int kBufWord3 = 0x00020000;
 // Stages a ROWS x D bf16 tile like TileStage, with buffer loads: the tile base
 // and its byte range live in one scalar resource and each piece needs only a
 // 32-bit offset.  Rows at or past `valid` lie outside the range and read as
-// zeros (the hardware returns 0 for out-of-range buffer loads).
+// zeros (the hardware returns 0 for out-of-range buffer loads); with valid <= 0
+// the range is empty and nothing is read at all.
 template <int ROWS, int D, int NT>
 struct BufStage {
     static constexpr int KC = D / 8;
@@ -170,9 +171,10 @@ struct BufStage {
     uint4 r[PER];
 
     __device__ __forceinline__ void load(const bf16* base, int tok_stride, int valid, int tid) {
-        const unsigned rows = (unsigned)(valid < ROWS ? valid : ROWS);
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)(rows * (unsigned)tok_stride * 2u), kBufWord3);
+        const unsigned rows = (unsigned)(valid <= 0 ? 0 : valid < ROWS ? valid : ROWS);
+        // (the range is wave-uniform; readfirstlane keeps it in a scalar register)
+        const int range = __builtin_amdgcn_readfirstlane((int)(rows * (unsigned)tok_stride * 2u));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, range, kBufWord3);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int p = tid + NT * i;
@@ -219,9 +221,10 @@ struct RowStage {
     uint4 r[PER];
 
     __device__ __forceinline__ void load(const bf16* base, int tok_stride, int valid, int tid) {
-        const unsigned rows = (unsigned)(valid < ROWS ? valid : ROWS);
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)(rows * (unsigned)tok_stride * 2u), kBufWord3);
+        const unsigned rows = (unsigned)(valid <= 0 ? 0 : valid < ROWS ? valid : ROWS);
+        // (the range is wave-uniform; readfirstlane keeps it in a scalar register)
+        const int range = __builtin_amdgcn_readfirstlane((int)(rows * (unsigned)tok_stride * 2u));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, range, kBufWord3);
         const int row0 = tid / KC;
         const int vo = (int)((unsigned)(row0 * tok_stride + (tid % KC) * 8) * 2u);
 #pragma unroll
