@@ -315,6 +315,18 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     p.nseg = p.nc > 0 ? (p.nc + p.seg_chunks - 1) / p.seg_chunks : 1;
     // fp32 segment states; the bf16 path adds a bf16 copy of each start state
     p.ws_bytes = (size_t)units * (p.nseg - 1) * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
+    // bf16, short sequence: a tiled state chain can emit every chunk's start
+    // state for one output workgroup per chunk.  Measured on gfx950 it beats the
+    // segment split only for 128-token chunks and at most 16 (batch, head)
+    // units (by ~4% at 16 units x 2,048 tokens; its passes are bound by LDS
+    // transposed reads, ~0.7 us each).
+    p.chain = bf16_io && chunk == 128 && units <= 16 && p.nseg > 1 && p.nc <= kChainMaxChunks;
+    if (const char* e = getenv("GLA_FWD_CHAIN")) {  // tuning override (sweeps, tests)
+        const int forced = atoi(e);
+        if (forced == 0) p.chain = 0;
+        if (forced == 1 && bf16_io && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
+    }
+    if (p.chain) p.ws_bytes = (size_t)units * (p.nc - 1) * dk * dv * 2;
     return p;
 }
 

@@ -517,6 +517,265 @@ __global__ __launch_bounds__(256) void seg_scan_frag_kernel(const float* __restr
     }
 }
 
+
+// ---------------------------------------------------------------- tiled chain
+//
+// Chunk start states for the per-chunk output kernel, by running the state
+// recurrence of the chunked form (same section: S <- lam^C S + K^T diag(c) V
+// per chunk) over tiles of the state.  The recurrence is independent per state
+// element, so a workgroup owns a 32-row x 16 NVB-column tile of one (batch,
+// head) unit and walks all its chunks; each wave keeps NJ 16x16 blocks of it
+// in fp32 registers.
+// Each chunk's contribution L = K^T diag(c) V is formed on its own (MFMA from
+// zero, c_j-scaled bf16 keys) and folded in as S <- fma(lam^C, S, L): exactly
+// the local states and the fma scan of the segment split with one chunk per
+// segment, so the start states, and the outputs, equal that path's bit for
+// bit (the final state rounds like the scan too).  Chunk tiles come through a
+// ring of D register sets (loads issued D chunks ahead) and three LDS buffers.
+//
+// Start state of chunk c >= 1 goes to snap[(bh * (nc - 1) + c - 1)] as bf16 in
+// the output kernel's register order for NCBO columns blocks per wave; the
+// state after the last chunk to S_final (fp32, [dk][dv]) when requested.
+struct ChainArgs {
+    int T, H, nc, units, ncbo;
+    const bf16* k;
+    const bf16* v;
+    const float* lambda;
+    const float* S0;
+    bf16* snap;
+    float* S_final;
+};
+
+template <int C, int NVB, int NJ>
+struct ChainShape {
+    static constexpr int NW = NVB * (2 / NJ), NT = 64 * NW;  // waves: NJ 16-row blocks x one 16-column block each
+    static constexpr int TK = 32, TV = 16 * NVB;
+    static constexpr int NTK = kDK / TK, NTV = kDV / TV, NTILE = NTK * NTV;
+    static constexpr int LKT = TK + 16, LVT = TV + 16;      // LDS row strides (elements)
+    static constexpr int NPK = C * (TK / 8), NPV = C * (TV / 8);   // 16-byte pieces per chunk tile
+    static constexpr int PK = (NPK + NT - 1) / NT, PV = (NPV + NT - 1) / NT;
+    static_assert(kDV % TV == 0 && (NJ == 1 || NJ == 2), "tile shape");
+};
+
+template <int C, int NVB, int NJ, int D>
+__global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel(ChainArgs a) {
+    static_assert(D % 2 == 0, "pass parity");
+    using L = ChainShape<C, NVB, NJ>;
+    constexpr int NT = L::NT, TK = L::TK, TV = L::TV, LKT = L::LKT, LVT = L::LVT, PK = L::PK, PV = L::PV;
+    constexpr int NPK = L::NPK, NPV = L::NPV;
+    __shared__ __align__(16) bf16 Kt[3][C * LKT];   // chunk tiles, three buffers
+    __shared__ __align__(16) bf16 Vt[3][C * LVT];
+
+    // Workgroups of one unit share an XCD (dispatch goes round-robin over 8):
+    // linear id = 8 * NTILE * (unit / 8) + 8 * tile + unit % 8.
+    const int lin = blockIdx.x;
+    const int grp = lin / (8 * L::NTILE), rem = lin % (8 * L::NTILE);
+    const int tile = rem / 8, bh = 8 * grp + rem % 8;
+    if (bh >= a.units) return;
+    const int tk = tile / L::NTV, tv = tile % L::NTV;
+    const int dk0 = TK * tk, dv0 = TV * tv;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int vb = wave % NVB, jlo = NJ == 2 ? 0 : wave / NVB;  // this wave's blocks: rows 16 (jlo + j), columns 16 vb
+    const int H = a.H, T = a.T, nc = a.nc;
+    const int hd = bh % H, b = bh / H;
+    const int tokK = H * kDK, tokV = H * kDV;
+    const size_t tok0 = (size_t)b * T * H + hd;
+    const bf16* kb = a.k + tok0 * kDK + dk0;
+    const bf16* vb_ = a.v + tok0 * kDV + dv0;
+
+    // Start state of the tile (fp32 [dk][dv] -> this wave's blocks), requested
+    // before the tiles so that waiting for it waits for no tile.
+    f32x4 S[NJ];
+    const float* s0 = a.S0 ? a.S0 + (size_t)bh * kDK * kDV : nullptr;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[j][r] = s0 ? s0[(dk0 + 16 * (jlo + j) + 4 * g + r) * kDV + dv0 + 16 * vb + n] : 0.f;
+
+    // Ring of register tiles: piece p = tid + NT i is row p / (W / 8), 16-byte
+    // column group p % (W / 8) of the chunk's W-wide tile.  Every pass issues
+    // the same loads (chunks past the end with an empty range: nothing is
+    // read), so each wait for a tile is exact and never waits for the tiles
+    // requested after it.
+    uint4 rk[D][PK], rv[D][PV];
+    auto load = [&](uint4 (&xk)[PK], uint4 (&xv)[PV], int t) {
+        const int valid = t < T ? min(C, T - t) : 0;
+        const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kb + (size_t)t * tokK), 0,
+                                                           __builtin_amdgcn_readfirstlane(valid * tokK * 2), kBufWord3);
+        const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(vb_ + (size_t)t * tokV), 0,
+                                                           __builtin_amdgcn_readfirstlane(valid * tokV * 2), kBufWord3);
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int p = tid + NT * i, row = p / (TK / 8), kc = p % (TK / 8);
+            if (NPK % NT == 0 || p < NPK)
+                xk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsk, (row * tokK + 8 * kc) * 2, 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int p = tid + NT * i, row = p / (TV / 8), kc = p % (TV / 8);
+            if (NPV % NT == 0 || p < NPV)
+                xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, (row * tokV + 8 * kc) * 2, 0, 0));
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(rk[d], rv[d], d * C);
+
+    // Decay factors: c_j of the key rows this thread stages (a full chunk, a
+    // partial last chunk) and the chunk decays lam^C, lam^(partial length).
+    const float lam = a.lambda[hd];
+    const int ctail = T % C;
+    float ck[PK][2];
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+        const int row = (tid + NT * i) / (TK / 8);
+        ck[i][0] = pow_int(lam, C - 1 - row);
+        ck[i][1] = row < ctail ? pow_int(lam, ctail - 1 - row) : 0.f;
+    }
+    const float lamC = uniform_f32(pow_int(lam, C)), lamT = uniform_f32(pow_int(lam, ctail));
+
+    // Snapshot positions (bf16x4 units) of this wave's blocks in the output
+    // kernel's register order.
+    int spos[NJ];
+    {
+        const int ncgo = kDV / (16 * a.ncbo), vblk = dv0 / 16 + vb;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int db = dk0 / 16 + jlo + j, h = db & 1, i = db >> 1;
+            const int wo = h * ncgo + vblk / a.ncbo, cb = vblk % a.ncbo;
+            spos[j] = ((wo * 3 + i) * a.ncbo + cb) * 64 + lane;
+        }
+    }
+    bf16x4* snap = reinterpret_cast<bf16x4*>(a.snap + (size_t)bh * (nc - 1) * kDK * kDV);
+
+    // Chunk x sits in ring slot x % D; staging writes it to LDS buffer x % 3
+    // (keys scaled by c_j), then the slot is refilled with chunk x + D.
+    auto stage = [&](uint4 (&xk)[PK], uint4 (&xv)[PV], int x) {
+        const bool full = T - x * C >= C;
+        bf16* kt = Kt[x % 3];
+        bf16* vt = Vt[x % 3];
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int p = tid + NT * i, row = p / (TK / 8), kc = p % (TK / 8);
+            if (NPK % NT == 0 || p < NPK)
+                *reinterpret_cast<uint4*>(kt + row * LKT + 8 * kc) = scale_bf16x8(xk[i], full ? ck[i][0] : ck[i][1]);
+        }
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            const int p = tid + NT * i, row = p / (TV / 8), kc = p % (TV / 8);
+            if (NPV % NT == 0 || p < NPV) *reinterpret_cast<uint4*>(vt + row * LVT + 8 * kc) = xv[i];
+        }
+    };
+    // Operands of chunk x (LDS buffer x % 3): this wave's value and key columns.
+    bf16x8 vop[2][C / 32], kop[2][C / 32][NJ];  // [chunk parity]
+    auto operands = [&](int par, int x) {
+        const bf16* kt = Kt[x % 3];
+        const bf16* vt = Vt[x % 3];
+#pragma unroll
+        for (int p = 0; p < C / 32; ++p) {
+            vop[par][p] = op_col8(vt, LVT, 32 * p, 16 * vb, n, g);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) kop[par][p][j] = op_col8(kt, LKT, 32 * p, 16 * (jlo + j), n, g);
+        }
+    };
+    stage(rk[0], rv[0], 0);
+    load(rk[0], rv[0], D * C);
+    stage(rk[1], rv[1], 1);
+    load(rk[1], rv[1], (D + 1) * C);
+    __syncthreads();
+    operands(0, 0);
+
+    // Pass c: chunk c's operands are in registers (read a pass earlier), chunk
+    // c + 1 is complete in LDS, chunk c + 2 is staged into the third buffer
+    // (last read two passes ago).  Chunk c's own contribution
+    // Lc = (diag(c) K)^T V is multiplied in pass c; the chain itself,
+    // S <- lam^C S + L(c-1), one fma per element, runs a pass later, so the
+    // chunk's MFMAs never wait for the chain, and LDS reads, LDS writes and
+    // MFMAs of neighbouring chunks overlap.  One barrier per pass.
+    f32x4 Lc[2][NJ];  // [pass parity][block]
+    for (int c0 = 0; c0 < nc; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int c = c0 + d;
+            if (c >= nc) break;
+            const int cur = d & 1, prv = cur ^ 1;  // D is even: parity of c
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) Lc[cur][j] = zero4();
+#pragma unroll
+            for (int p = 0; p < C / 32; ++p)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Lc[cur][j] = mfma(kop[cur][p][j], vop[cur][p], Lc[cur][j]);
+            // chain step of the previous chunk: S = start state of chunk c
+            if (c >= 1) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[j][r] = fmaf(lamC, S[j][r], Lc[prv][j][r]);  // a full chunk
+                    snap[(size_t)(c - 1) * (kDK * kDV / 4) + spos[j]] =
+                        bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
+                }
+            }
+            operands(prv, c + 1);
+            // chunk c + 2 staged, its slot refilled; issued on every pass (past
+            // the end: zeros, no reads), so the waits for the ring stay exact
+            const int d2 = (d + 2) % D;  // compile-time once unrolled
+            stage(rk[d2], rv[d2], c + 2);
+            load(rk[d2], rv[d2], (c + 2 + D) * C);
+            __syncthreads();  // chunk c + 2 staged; chunk c + 1's operands read
+        }
+    }
+    {
+        // the last chunk (possibly partial): S_final = lam^ceff S + L(nc-1)
+        const float Lam = T - (nc - 1) * C >= C ? lamC : lamT;
+        const int last = (nc - 1) & 1;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[j][r] = fmaf(Lam, S[j][r], last ? Lc[1][j][r] : Lc[0][j][r]);
+    }
+    if (a.S_final) {
+        float* dst = a.S_final + (size_t)bh * kDK * kDV;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(dk0 + 16 * (jlo + j) + 4 * g + r) * kDV + dv0 + 16 * vb + n] = S[j][r];
+    }
+}
+
+template <int C>
+hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, const void* k, const void* v,
+                        const float* lambda, const float* S0, float* S_final, void* ws, hipStream_t stream) {
+    // 4 waves, two 16x16 blocks each, over a 32 x 64 tile (the fastest of the
+    // shapes tried; a pass costs ~0.7 us, about half of it LDS time for the
+    // transposed operand reads).  Chunks in flight: as deep as the wave's
+    // memory counter can follow exactly (at most 63 outstanding operations; a
+    // chunk costs PK + PV loads and NJ snapshot stores); even, so the pass
+    // parity is known at compile time in the unrolled loop.
+    constexpr int NVB = 4, NJ = 2;
+    using L = ChainShape<C, NVB, NJ>;
+    constexpr int D = C == 128 ? 6 : 12;
+    static_assert(D * (L::PK + L::PV + NJ) <= 63, "memory counter");
+    ChainArgs c{};
+    c.T = T;
+    c.H = H;
+    c.nc = plan.nc;
+    c.units = B * H;
+    c.ncbo = ncbo;
+    c.k = static_cast<const bf16*>(k);
+    c.v = static_cast<const bf16*>(v);
+    c.lambda = lambda;
+    c.S0 = S0;
+    c.snap = static_cast<bf16*>(ws);
+    c.S_final = S_final;
+    const unsigned groups = (unsigned)((c.units + 7) / 8);
+    hipLaunchKernelGGL((fwd_chain_kernel<C, NVB, NJ, D>), dim3(groups * 8 * L::NTILE), dim3(L::NT), 0, stream, c);
+    return hipGetLastError();
+}
+
 template <int C, int LDK, int NCB>
 hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k, const void* v,
                     const float* lambda, const float* S0, float scale, void* o, float* S_final, void* ws,
@@ -538,6 +797,20 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     a.seg_chunks = plan.seg_chunks;
     a.nc = plan.nc;
     const unsigned units = (unsigned)B * H;
+    if (plan.chain) {
+        // every chunk's start state from the tiled chain, then one output
+        // workgroup per chunk (one-chunk segments reading bf16 start states)
+        hipError_t err = launch_chain<C>(plan, B, T, H, NCB, k, v, lambda, S0, S_final, ws, stream);
+        if (err != hipSuccess) return err;
+        a.nseg = plan.nc;
+        a.seg_chunks = 1;
+        a.U = nullptr;
+        a.Ub = ws;
+        a.S_final = nullptr;
+        hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, false>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
     if (plan.nseg > 1) {
         hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, true>), dim3(plan.nseg - 1, units), dim3(F8<C, LDK, NCB>::NT),
                            0, stream, a);

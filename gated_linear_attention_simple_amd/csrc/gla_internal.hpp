@@ -25,8 +25,14 @@ struct FwdPlan {
     int nc;          // chunks in the sequence
     int nseg;        // sequence segments run in parallel
     int seg_chunks;  // chunks per segment (the last segment may hold fewer)
-    size_t ws_bytes; // segment states: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path)
+    int chain;       // bf16 path: tiled state chain + per-chunk output instead of segments
+    size_t ws_bytes; // segments: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path);
+                     // chain: B*H*(nc-1)*dk*dv bf16 chunk start states
 };
+
+// The tiled chain runs the chunk recurrence itself (sequential over chunks);
+// it replaces the segment split only up to this many chunks.
+constexpr int kChainMaxChunks = 64;
 
 bool fwd_supported(bool bf16_io, int dk, int dv, int chunk);
 FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);

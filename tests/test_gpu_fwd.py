@@ -71,19 +71,54 @@ def test_fp32_laplace_shape_chunk64():
 def test_segment_split_equivalence(nseg, monkeypatch):
     """Forcing different sequence-segment counts gives the oracle's result."""
     monkeypatch.setenv("GLA_FWD_SEGMENTS", str(nseg))
+    monkeypatch.setenv("GLA_FWD_CHAIN", "0")
     _run_and_check(gi.workloads()[1], seed=200 + nseg, B=1, T=2000, chunk=64, s0_var=0.01)
 
 
 @pytest.mark.parametrize("ncb", ["2", "3"])
 @pytest.mark.parametrize("chunk", [128, 64])
-@pytest.mark.parametrize("nseg", [1, 3])
-def test_bf16_wave_layouts(ncb, chunk, nseg, monkeypatch):
+@pytest.mark.parametrize("mode", ["seg1", "seg3", "chain"])
+def test_bf16_wave_layouts(ncb, chunk, mode, monkeypatch):
     """Both bf16 workgroup layouts (12 waves with 32-column pairs, 8 waves with
-    48-column pairs), with and without sequence segments, ragged tail, S0."""
+    48-column pairs): unsplit, with sequence segments, and with the tiled state
+    chain feeding one output workgroup per chunk; ragged tail, S0."""
     monkeypatch.setenv("GLA_FWD_NCB", ncb)
-    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(nseg))
-    _run_and_check(gi.workloads()[1], seed=300 + 7 * int(ncb) + chunk + nseg, B=2, T=1000, chunk=chunk,
+    monkeypatch.setenv("GLA_FWD_SEGMENTS", "3" if mode == "seg3" else "1")
+    monkeypatch.setenv("GLA_FWD_CHAIN", "1" if mode == "chain" else "0")
+    _run_and_check(gi.workloads()[1], seed=300 + 7 * int(ncb) + chunk + len(mode), B=2, T=1000, chunk=chunk,
                    s0_var=0.01)
+
+
+@pytest.mark.parametrize("ncb", ["2", "3"])
+@pytest.mark.parametrize("chunk,T,s0", [(128, 2048, None), (64, 1000, None), (128, 700, 0.01), (64, 700, 0.01)])
+@pytest.mark.parametrize("want_final", [True, False])
+def test_chain_matches_one_chunk_segments_bitwise(ncb, chunk, T, s0, want_final, monkeypatch):
+    """The tiled state chain forms each chunk's contribution on its own and folds
+    it in with the segment scan's fma, i.e. the arithmetic of the segment split
+    with one chunk per segment: the outputs agree bit for bit, the final states
+    (rounded in a different order by the segment path's last workgroup) to fp32
+    accuracy.  Both also meet the oracle."""
+    w = gi.workloads()[1]
+    monkeypatch.setenv("GLA_FWD_NCB", ncb)
+    x = gi.fwd_inputs(w, DEV, 900 + chunk + T, B=1, T=T, s0_var=s0)
+    nc = (T + chunk - 1) // chunk
+    _say(f"chain vs {nc} one-chunk segments ncb={ncb} C={chunk} T={T} S0={s0 is not None} S_final={want_final}")
+    outs = []
+    for segs, chain in ((str(nc), "0"), ("1", "1")):
+        monkeypatch.setenv("GLA_FWD_SEGMENTS", segs)
+        monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+        o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk,
+                               S_final=want_final)
+        outs.append((o, S))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]), "o differs between the segment and chain paths"
+    if want_final:
+        a, b = f64(outs[0][1]), f64(outs[1][1])
+        assert np.linalg.norm(a - b) <= 1e-6 * np.linalg.norm(a), "S_final: segment and chain paths disagree"
+        ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]),
+                            S0=None if x["S0"] is None else f64(x["S0"]), scale=x["scale"])
+        assert_close(f64(outs[1][0]), ro, w.dtype, "o")
+        assert_close(b, rS, w.dtype, "S_final")
 
 
 def test_train_batch_forward_chunk64_and_128():

@@ -22,12 +22,15 @@ def _say(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
-def test_graph_replays_match_eager(chunk):
+@pytest.mark.parametrize("chunk,chain", [(128, "0"), (64, "0"), (128, "1")])
+def test_graph_replays_match_eager(chunk, chain, monkeypatch):
+    """Also with the forward's tiled state chain (two launches, a chunk start
+    state workspace) in the captured sequence."""
+    monkeypatch.setenv("GLA_FWD_CHAIN", chain)
     w = gi.workloads()[1]
     x = gi.fwd_inputs(w, DEV, 41 + chunk, B=2, T=700, with_do=True, s0_var=0.01)
     y = gi.fwd_inputs(w, DEV, 43 + chunk, B=2, T=700, with_do=True, s0_var=0.01)
-    _say(f"graph capture fwd+bwd B=2 T=700 C={chunk}")
+    _say(f"graph capture fwd+bwd B=2 T=700 C={chunk} chain={chain}")
     args = (x["q"], x["k"], x["v"], x["lam"])
     o_ref, S_ref = gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk)
     g_ref = gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk)
