@@ -326,7 +326,7 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
         if (forced == 0) p.chain = 0;
         if (forced == 1 && bf16_io && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
     }
-    if (p.chain) p.ws_bytes = (size_t)units * (p.nc - 1) * dk * dv * 2;
+    if (p.chain) p.ws_bytes = (size_t)units * p.nc * dk * dv * 2;  // every chunk's start state, bf16
     return p;
 }
 

@@ -134,16 +134,53 @@ constexpr int score_lead() {
 // lane group spread over all banks.
 __device__ __forceinline__ int as_off(int row, int u) { return row * 16 + 8 * (u ^ ((row >> 3) & 1)); }
 
+// This wave's decay-masked score blocks (slot k: block 16 ib + jb of the
+// lower triangle, or -1), A = scale * (Q K^T) (.) D, written to As as bf16.
+// AT[k][4g + r][n] = q_(16 ib + n) . k_(16 jb + 4g + r); query fragments of
+// strips sa (the first NA slots) and sb are read once per k-step.
+template <int C, int LDK, int NW, int NS>
+__device__ __forceinline__ void score_blocks_to_lds(const bf16* Qs, const bf16* Ks, bf16* As, const float* pws,
+                                                    const int (&blk)[NS], int sa, int sb, const bool (&use_b)[NS],
+                                                    int n, int g) {
+    constexpr int NA = score_lead<C, NW>();
+    f32x4 AT[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) AT[k] = zero4();
+#pragma unroll
+    for (int p = 0; p < kDK / 32; ++p) {
+        const bf16x8 qa = op_row8(Qs, LDK, 16 * sa + n, 32 * p + 8 * g);
+        const bf16x8 qc = op_row8(Qs, LDK, 16 * sb + n, 32 * p + 8 * g);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const int jb = blk[k] >= 0 ? blk[k] & 15 : 0;
+            const bf16x8 q = (k < NA || !use_b[k]) ? qa : qc;
+            AT[k] = mfma(op_row8(Ks, LDK, 16 * jb + n, 32 * p + 8 * g), q, AT[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        if (blk[k] < 0) continue;
+        const int ib = blk[k] >> 4, jb = blk[k] & 15;
+        // scale * D_ij = scale * lam^(i-j) for i >= j, else 0, with
+        // i - j = 16 (ib - jb) + n - 4g - r: one table read per element.
+        const int d1 = 16 * (ib - jb) + n - 4 * g + 1;
+        f32x4 x = AT[k];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] *= pws[max(d1 - r, 0)];
+        *reinterpret_cast<bf16x4*>(As + (ib * (ib + 1) / 2 + jb) * 256 + as_off(n, g >> 1) + 4 * (g & 1)) =
+            bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
+    }
+}
+
 // Output of query strips 2K and 2K+1 for this wave's 16 NCB columns:
 //   O^T = b (.) S^T Q^T  +  V^T A^T, scaled and stored as bf16.
 //
-// The S^T operand of k-step p (features 32p .. 32p+31) pairs this wave's state
-// block (16 rows) with the partner's, published as bf16 in `xs_other`:
-// rows 32p + 4g + r from the HH = 0 wave, rows 32p + 16 + 4g + r from HH = 1.
+// sop(p, cb) is the S^T operand of k-step p (features 32p .. 32p+31) for
+// column block cb: this wave's state block (16 rows) paired with the partner's,
+// rows 32p + 4g + r from the h = 0 wave, rows 32p + 16 + 4g + r from h = 1.
 // `pws[x + 1]` = scale * lam^x and the score blocks already carry `scale`.
-template <int C, int LDK, int NCB, int K, int HH>
-__device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, const f32x4 (&Sacc)[3][NCB],
-                                         const bf16x4* xs_other, const bf16x8 (&vf)[NCB][C / 32],
+template <int C, int LDK, int NCB, int K, typename SopF>
+__device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, SopF sop, const bf16x8 (&vf)[NCB][C / 32],
                                          const float* pws, bf16* ob, size_t tokV, int t0, int ceff, int colbase,
                                          int n, int g) {
 #pragma unroll
@@ -155,15 +192,7 @@ __device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, const f
         for (int p = 0; p < kDK / 32; ++p) {
             const bf16x8 q0 = op_row_pair(Qs, LDK, 32 * K + 16 * u + n, 32 * p + 4 * g);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const bf16x4 own = bf16x4{to_bf16(Sacc[p][cb][0]), to_bf16(Sacc[p][cb][1]), to_bf16(Sacc[p][cb][2]),
-                                          to_bf16(Sacc[p][cb][3])};
-                const bf16x4 oth = xs_other[(p * NCB + cb) * 64];
-                bf16x8 sop;
-                if constexpr (HH == 0) sop = __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7);
-                else sop = __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
-                OT[cb] = mfma(sop, q0, OT[cb]);
-            }
+            for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(sop(p, cb), q0, OT[cb]);
         }
         const float bi = pws[32 * K + 16 * u + n + 2];  // scale * lam^(i+1), i = 16 (2K + u) + n
 #pragma unroll
@@ -380,34 +409,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
         if constexpr (SO) load_vf();
 
         if constexpr (!SO) {
-            // Score blocks: AT[k][4g + r][n] = q_(16 ib + n) . k_(16 jb + 4g + r).
-            f32x4 AT[NS];
-#pragma unroll
-            for (int k = 0; k < NS; ++k) AT[k] = zero4();
-#pragma unroll
-            for (int p = 0; p < kDK / 32; ++p) {
-                const bf16x8 qa = op_row8(Qs, LDK, 16 * sa + n, 32 * p + 8 * g);
-                const bf16x8 qc = op_row8(Qs, LDK, 16 * sb + n, 32 * p + 8 * g);
-#pragma unroll
-                for (int k = 0; k < NS; ++k) {
-                    const int jb = blk[k] >= 0 ? blk[k] & 15 : 0;
-                    const bf16x8 q = (k < NA || !use_b[k]) ? qa : qc;
-                    AT[k] = mfma(op_row8(Ks, LDK, 16 * jb + n, 32 * p + 8 * g), q, AT[k]);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < NS; ++k) {
-                if (blk[k] < 0) continue;
-                const int ib = blk[k] >> 4, jb = blk[k] & 15;
-                // scale * D_ij = scale * lam^(i-j) for i >= j, else 0, with
-                // i - j = 16 (ib - jb) + n - 4g - r: one table read per element.
-                const int d1 = 16 * (ib - jb) + n - 4 * g + 1;
-                f32x4 x = AT[k];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) x[r] *= pws[max(d1 - r, 0)];
-                *reinterpret_cast<bf16x4*>(As + (ib * (ib + 1) / 2 + jb) * 256 + as_off(n, g >> 1) + 4 * (g & 1)) =
-                    bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
-            }
+            score_blocks_to_lds<C, LDK, L::NW, NS>(Qs, Ks, As, pws, blk, sa, sb, use_b, n, g);
             load_vf();
             __syncthreads();  // score blocks complete
 
@@ -419,18 +421,27 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                 *kp = scale_bf16x8(*kp, cjc[row]);
             }
 
+            // S^T operands: own half from the accumulators, the partner's from its
+            // published copy
             const bf16x4* xo = xs_at(partner, 0, 0);
+            auto sop = [&](int p, int cb) -> bf16x8 {
+                const bf16x4 own = bf16x4{to_bf16(Sacc[p][cb][0]), to_bf16(Sacc[p][cb][1]), to_bf16(Sacc[p][cb][2]),
+                                          to_bf16(Sacc[p][cb][3])};
+                const bf16x4 oth = xo[(p * NCB + cb) * 64];
+                return h == 0 ? __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7)
+                              : __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
             if constexpr (C == 128) {
                 if (h == 0) {
-                    out_pair<C, LDK, NCB, 0, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                    out_pair<C, LDK, NCB, 3, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
                 } else {
-                    out_pair<C, LDK, NCB, 1, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                    out_pair<C, LDK, NCB, 2, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
                 }
             } else {
-                if (h == 0) out_pair<C, LDK, NCB, 0, 0>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                else out_pair<C, LDK, NCB, 1, 1>(Qs, As, Sacc, xo, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
             }
         }
 
@@ -518,6 +529,105 @@ __global__ __launch_bounds__(256) void seg_scan_frag_kernel(const float* __restr
 }
 
 
+// Output of one chunk from its start state, a bf16 snapshot in register order
+// written by the tiled chain (snapshot bh * nc + c of a.Ub):
+//     O_c = scale * ( (Q K^T (.) D) V  +  diag(b) Q S ).
+// One workgroup per (chunk, unit), laid out like the main kernel, without the
+// state update and without the pair exchange: both halves of a wave pair's
+// S^T operand come straight from the snapshot.  q and k are staged first, so
+// the score blocks overlap the arrival of the values and the start state.
+template <int C, int LDK, int NCB>
+__global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdArgs a) {
+    using L = F8<C, LDK, NCB>;
+    constexpr int NT = L::NT, NP = L::NP, LDV = L::LDV, NCG = L::NCG;
+    __shared__ __align__(16) bf16 Qs[C * LDK];
+    __shared__ __align__(16) bf16 Ks[C * LDK];
+    __shared__ __align__(16) bf16 Vs[C * LDV];
+    __shared__ __align__(16) bf16 As[L::AS_BYTES / 2];
+    __shared__ float pws[C + 2];  // pws[0] = 0, pws[x + 1] = scale * lam^x (x = 0..C)
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int h = wave / NCG, colbase = 16 * NCB * (wave % NCG);
+    const int partner = h == 0 ? wave + NCG : wave - NCG;
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int hd = bh % H, b = bh / H;
+    const int t0 = c * C, ceff = min(C, T - t0);
+    const int tokK = H * kDK, tokV = H * kDV;
+    const size_t tok0 = ((size_t)b * T + t0) * H + hd;
+    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + ((size_t)b * T * H + hd) * kDV;
+
+    constexpr int NS = L::NSLOT;
+    int blk[NS];
+    score_blocks_uniform<C, L::NW>(wave, blk, std::make_integer_sequence<int, NS>{});
+    const int sa = blk[0] >= 0 ? blk[0] >> 4 : 0;
+    int sb = sa;
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        if (blk[k] >= 0) sb = blk[k] >> 4;
+    constexpr int NA = score_lead<C, L::NW>();
+    bool use_b[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) use_b[k] = k >= NA && blk[k] >= 0 && (blk[k] >> 4) != sa;
+
+    using StageK = std::conditional_t<NT % (kDK / 8) == 0, RowStage<C, kDK, NT>, BufStage<C, kDK, NT>>;
+    using StageV = std::conditional_t<NT % (kDV / 8) == 0, RowStage<C, kDV, NT>, BufStage<C, kDV, NT>>;
+    StageK tq, tk;
+    StageV tv;
+    tq.load(qb, tokK, ceff, tid);
+    tk.load(kb, tokK, ceff, tid);
+    tv.load(vb, tokV, ceff, tid);
+    // start state: this wave's half and the partner's, 4 bf16 per block and lane
+    const uint2* sn = reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.Ub) + ((size_t)bh * a.nc + c) * kDK * kDV);
+    uint2 so[3][NCB], sp[3][NCB];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            so[i][cb] = sn[((wave * 3 + i) * NCB + cb) * 64 + lane];
+            sp[i][cb] = sn[((partner * 3 + i) * NCB + cb) * 64 + lane];
+        }
+
+    const float lam = a.lambda[hd];
+    if (tid < C + 2) pws[tid] = tid == 0 ? 0.f : a.scale * pow_int(lam, tid - 1);
+
+    tq.template store<LDK>(Qs, tid);
+    tk.template store<LDK>(Ks, tid);
+    __syncthreads();  // q, k, decay table
+    score_blocks_to_lds<C, LDK, L::NW, NS>(Qs, Ks, As, pws, blk, sa, sb, use_b, n, g);
+    tv.template store<LDV>(Vs, tid);
+    __syncthreads();  // score blocks, values
+
+    bf16x8 vf[NCB][NP];  // vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) vf[cb][p] = op_col8(Vs, LDV, 32 * p, colbase + 16 * cb, n, g);
+    auto sop = [&](int p, int cb) -> bf16x8 {
+        const bf16x4 own = __builtin_bit_cast(bf16x4, so[p][cb]);
+        const bf16x4 oth = __builtin_bit_cast(bf16x4, sp[p][cb]);
+        return h == 0 ? __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7)
+                      : __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    if constexpr (C == 128) {
+        if (h == 0) {
+            out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+        } else {
+            out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+        }
+    } else {
+        if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+        else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+    }
+}
+
 // ---------------------------------------------------------------- tiled chain
 //
 // Chunk start states for the per-chunk output kernel, by running the state
@@ -533,9 +643,9 @@ __global__ __launch_bounds__(256) void seg_scan_frag_kernel(const float* __restr
 // bit (the final state rounds like the scan too).  Chunk tiles come through a
 // ring of D register sets (loads issued D chunks ahead) and three LDS buffers.
 //
-// Start state of chunk c >= 1 goes to snap[(bh * (nc - 1) + c - 1)] as bf16 in
-// the output kernel's register order for NCBO columns blocks per wave; the
-// state after the last chunk to S_final (fp32, [dk][dv]) when requested.
+// Start state of chunk c goes to snap[bh * nc + c] as bf16 in the output
+// kernel's register order for NCBO column blocks per wave; the state after the
+// last chunk to S_final (fp32, [dk][dv]) when requested.
 struct ChainArgs {
     int T, H, nc, units, ncbo;
     const bf16* k;
@@ -649,7 +759,7 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
             spos[j] = ((wo * 3 + i) * a.ncbo + cb) * 64 + lane;
         }
     }
-    bf16x4* snap = reinterpret_cast<bf16x4*>(a.snap + (size_t)bh * (nc - 1) * kDK * kDV);
+    bf16x4* snap = reinterpret_cast<bf16x4*>(a.snap + (size_t)bh * nc * kDK * kDV);
 
     // Chunk x sits in ring slot x % D; staging writes it to LDS buffer x % 3
     // (keys scaled by c_j), then the slot is refilled with chunk x + D.
@@ -709,14 +819,14 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) Lc[cur][j] = mfma(kop[cur][p][j], vop[cur][p], Lc[cur][j]);
             // chain step of the previous chunk: S = start state of chunk c
-            if (c >= 1) {
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
+            for (int j = 0; j < NJ; ++j) {
+                if (c >= 1) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) S[j][r] = fmaf(lamC, S[j][r], Lc[prv][j][r]);  // a full chunk
-                    snap[(size_t)(c - 1) * (kDK * kDV / 4) + spos[j]] =
-                        bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
                 }
+                snap[(size_t)c * (kDK * kDV / 4) + spos[j]] =
+                    bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
             }
             operands(prv, c + 1);
             // chunk c + 2 staged, its slot refilled; issued on every pass (past
@@ -799,16 +909,14 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     const unsigned units = (unsigned)B * H;
     if (plan.chain) {
         // every chunk's start state from the tiled chain, then one output
-        // workgroup per chunk (one-chunk segments reading bf16 start states)
+        // workgroup per chunk
         hipError_t err = launch_chain<C>(plan, B, T, H, NCB, k, v, lambda, S0, S_final, ws, stream);
         if (err != hipSuccess) return err;
-        a.nseg = plan.nc;
-        a.seg_chunks = 1;
         a.U = nullptr;
         a.Ub = ws;
         a.S_final = nullptr;
-        hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, false>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT), 0,
-                           stream, a);
+        hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT), 0, stream,
+                           a);
         return hipGetLastError();
     }
     if (plan.nseg > 1) {

@@ -27,7 +27,7 @@ struct FwdPlan {
     int seg_chunks;  // chunks per segment (the last segment may hold fewer)
     int chain;       // bf16 path: tiled state chain + per-chunk output instead of segments
     size_t ws_bytes; // segments: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path);
-                     // chain: B*H*(nc-1)*dk*dv bf16 chunk start states
+                     // chain: B*H*nc*dk*dv bf16 chunk start states
 };
 
 // The tiled chain runs the chunk recurrence itself (sequential over chunks);
