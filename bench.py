@@ -328,7 +328,8 @@ def ingest_counters(fetch_csv, write_csv):
         copies = [v for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
         ref = max(copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
         fac[counter] = (1 << 30) / (ref * 1024.0)
-        groups = {"fwd": ["fwd_bf16_kernel", "seg_scan"], "decode": ["decode_kernel"]}
+        groups = {"fwd": ["fwd_bf16_kernel", "seg_scan", "fwd_chain_kernel", "fwd_out_kernel"],
+                  "decode": ["decode_kernel"]}
         for key, pats in groups.items():
             # per call: sum over the kernels one call launches, averaged over the 3 calls
             tot = sum(v for (d, name), v in by.items() if any(pt in name for pt in pats))
@@ -384,7 +385,7 @@ def main():
                    "global_batch": 1, "seq_len": 2048, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": f_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": f_ach / HBM_PEAK_GBS, "traffic": stored_traffic("fwd", f_bytes),
-                     "kernel": "gla_fwd_chunked (segment prologue + main)",
+                     "kernel": "gla_fwd_chunked (tiled state chain + per-chunk output kernel)",
                      "alg_bytes_per_launch": f_bytes, "avg_launch_us": f_avg * 1e6,
                      "mfma_tflops": f_flops / f_avg / 1e12,
                      "mfma_frac": f_flops / f_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS},
