@@ -198,9 +198,21 @@ class DecodeLeg:
                      for layer in range(L)]
         self.layers = L
         self.n_inputs = n_inputs
+        # page-pool form: the same pages addressed through a fixed shuffle of slots
+        perm = torch.randperm(w.B, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+        self.slots = perm.to(dev)
+        self.fn_pool = gla.load().gla_decode_step_pool
+        self.args_pool = [[(gla.GLA_BF16, w.B, w.H, w.dk, w.dv, p(d["q"]), p(d["k"]), p(d["v"]), p(self.lam),
+                            p(self.pool[layer]), w.B, p(self.slots), ctypes.c_float(w.scale), p(self.o),
+                            ctypes.c_void_p(self.stream.cuda_stream)) for d in self.inputs[layer]]
+                          for layer in range(L)]
+        self.use_pool = False
 
     def launch(self, layer, step):
-        st = self.fn(*self.args[layer][step % self.n_inputs])
+        if self.use_pool:
+            st = self.fn_pool(*self.args_pool[layer][step % self.n_inputs])
+        else:
+            st = self.fn(*self.args[layer][step % self.n_inputs])
         if st != 0:
             raise RuntimeError(f"gla_decode_step: {self.gla.status_str(st)}")
 
@@ -434,6 +446,15 @@ def main():
                          "kernel": "gla_decode_step", "alg_bytes_per_launch": per_launch_bytes,
                          "avg_launch_us": d_avg * 1e6},
         }
+        # the same steps through gla_decode_step_pool, pages addressed by shuffled slots
+        dleg.use_pool = True
+        p_wall, p_gpu = time_decode(torch, dleg, K, W)
+        p_avg = p_gpu / (K * w4.decode_layers)
+        result["decode"]["pool"] = {
+            "kernel": "gla_decode_step_pool (1,280 rows, pages at a shuffled slot permutation)",
+            "ms_per_step": p_wall / K * 1e3, "avg_launch_us": p_avg * 1e6,
+            "achieved": per_launch_bytes / p_avg / 1e9, "unit": "GB/s",
+            "frac": per_launch_bytes / p_avg / 1e9 / HBM_PEAK_GBS}
         del dleg
         torch.cuda.empty_cache()
     result["ms_per_step"] = f_ms + t_ms + d_ms

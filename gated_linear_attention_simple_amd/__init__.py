@@ -26,6 +26,7 @@ SYMBOLS = (
     "gla_bwd_workspace_bytes",
     "gla_bwd_chunked",
     "gla_decode_step",
+    "gla_decode_step_pool",
 )
 
 _lib = None
@@ -58,6 +59,8 @@ def load():
         lib.gla_bwd_chunked.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.gla_decode_step.restype = i
         lib.gla_decode_step.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, f, vp, vp]
+        lib.gla_decode_step_pool.restype = i
+        lib.gla_decode_step_pool.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, i, vp, f, vp, vp]
         _lib = lib
     return _lib
 
@@ -184,4 +187,28 @@ def decode_step(q, k, v, lam, S, scale=1.0, o=None, stream=None):
                              float(scale), _ptr(o), _stream(stream))
     if st != GLA_OK:
         raise GlaError(st, "gla_decode_step")
+    return o
+
+
+def decode_step_pool(q, k, v, lam, pool, slots, scale=1.0, o=None, stream=None):
+    """Decode on a page pool: row n uses page slots[n] of pool [P, H, dk, dv] (in place);
+    a slot outside [0, P) (-1: padding row) gives a zero output row.  Returns o."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    P = pool.shape[0]
+    dev = q.device
+    _check(q, "q", (N, H, dk), q.dtype, dev)
+    _check(k, "k", (N, H, dk), q.dtype, dev)
+    _check(v, "v", (N, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    _check(pool, "pool", (P, H, dk, dv), torch.float32, dev)
+    _check(slots, "slots", (N,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(o, "o", (N, H, dv), q.dtype, dev)
+    st = lib.gla_decode_step_pool(_dt(q), N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(pool), P,
+                                  _ptr(slots), float(scale), _ptr(o), _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_decode_step_pool")
     return o

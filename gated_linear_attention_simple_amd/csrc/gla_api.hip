@@ -45,7 +45,7 @@ int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
 
 extern "C" {
 
-int gla_abi_version(void) { return 1; }
+int gla_abi_version(void) { return 2; }
 
 const char* gla_status_str(int status) {
     switch (status) {
@@ -110,8 +110,24 @@ int gla_decode_step(int dtype, int N, int H, int dk, int dv, const void* q, cons
     if (N == 0) return GLA_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(S) || !ok_ptr(o))
         return GLA_ERR_INVALID_ARG;
-    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, scale, o,
-                                              static_cast<hipStream_t>(stream));
+    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, nullptr, 0,
+                                              scale, o, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                         const float* lambda, float* pool, int P, const int* slots, float scale, void* o,
+                         void* stream) {
+    if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1 || P < 0) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(N, H, dk, dv) || !sane_count(P, H, dk, dv)) return GLA_ERR_INVALID_ARG;
+    if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
+    if ((long)N * H > 2147483647L) return GLA_ERR_UNSUPPORTED;
+    if (N == 0) return GLA_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(o) || !ok_ptr(slots))
+        return GLA_ERR_INVALID_ARG;
+    if (P > 0 && !ok_ptr(pool)) return GLA_ERR_INVALID_ARG;
+    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, pool, slots, P,
+                                              scale, o, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 

@@ -12,15 +12,22 @@
 // One workgroup per (sequence, head).  Thread t owns float4 column group
 // cg = t % (DV/4) and rows r = rg, rg + RG, ... with rg = t / (DV/4); its
 // loads of one row sweep are contiguous across the workgroup.
+//
+// Pool form (same section: one fixed page per sequence, serving batches padded
+// to fixed widths): row n of the batch uses page slots[n] of a pool of P pages
+// [P][H][dk][dv]; a slot outside [0, P) (-1 marks a padding row) touches no
+// page and yields a zero output.  Every (row, head) is computed alone, so a
+// sequence's results do not depend on the batch it is in.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 
 namespace gla {
 
-template <typename E, int DK, int DV, int RG>
+template <typename E, int DK, int DV, int RG, bool POOL>
 __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
     int H, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ lambda, float* __restrict__ S, float scale, E* __restrict__ o) {
+    const float* __restrict__ lambda, float* __restrict__ S, const int* __restrict__ slots, int P, float scale,
+    E* __restrict__ o) {
     constexpr int NCG = DV / 4;          // float4 column groups per row
     constexpr int NT = NCG * RG;         // threads
     constexpr int RPT = DK / RG;         // rows per thread
@@ -35,6 +42,15 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
     const int t = threadIdx.x;
     const int cg = t % NCG;
     const int rg = t / NCG;
+    size_t page = unit;                  // state page of this (row, head)
+    if constexpr (POOL) {
+        const int slot = slots[unit / H];
+        if (slot < 0 || slot >= P) {     // padding row: no state access, zero output
+            for (int c = t; c < DV; c += NT) o[(size_t)unit * DV + c] = from_f32<E>(0.f);
+            return;
+        }
+        page = (size_t)slot * H + h;
+    }
 
     for (int i = t; i < DK; i += NT) {
         qs[i] = to_f32(q[(size_t)unit * DK + i]);
@@ -45,7 +61,7 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[(size_t)unit * DV + cg * 4 + e]);
 
-    f32x4* Sp = reinterpret_cast<f32x4*>(S + (size_t)unit * DK * DV);
+    f32x4* Sp = reinterpret_cast<f32x4*>(S + page * DK * DV);
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + i * RG) * NCG + cg);
@@ -76,12 +92,17 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
 
 template <typename E, int DK, int DV, int RG>
 static hipError_t launch_decode_t(int N, int H, const void* q, const void* k, const void* v,
-                                  const float* lambda, float* S, float scale, void* o,
+                                  const float* lambda, float* S, const int* slots, int P, float scale, void* o,
                                   hipStream_t stream) {
     const int units = N * H;
-    hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG>), dim3(units), dim3((DV / 4) * RG), 0, stream,
-                       H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
-                       lambda, S, scale, static_cast<E*>(o));
+    if (slots)
+        hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG, true>), dim3(units), dim3((DV / 4) * RG), 0, stream,
+                           H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+                           lambda, S, slots, P, scale, static_cast<E*>(o));
+    else
+        hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG, false>), dim3(units), dim3((DV / 4) * RG), 0, stream,
+                           H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+                           lambda, S, nullptr, 0, scale, static_cast<E*>(o));
     return hipGetLastError();
 }
 
@@ -90,14 +111,14 @@ bool decode_supported(int dk, int dv) {
 }
 
 hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* lambda, float* S, float scale, void* o,
-                         hipStream_t stream) {
+                         const void* v, const float* lambda, float* S, const int* slots, int P, float scale,
+                         void* o, hipStream_t stream) {
     if (dk == 96 && dv == 192) {
-        return bf16_io ? launch_decode_t<bf16, 96, 192, 4>(N, H, q, k, v, lambda, S, scale, o, stream)
-                       : launch_decode_t<float, 96, 192, 4>(N, H, q, k, v, lambda, S, scale, o, stream);
+        return bf16_io ? launch_decode_t<bf16, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream)
+                       : launch_decode_t<float, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream);
     }
-    return bf16_io ? launch_decode_t<bf16, 16, 32, 16>(N, H, q, k, v, lambda, S, scale, o, stream)
-                   : launch_decode_t<float, 16, 32, 16>(N, H, q, k, v, lambda, S, scale, o, stream);
+    return bf16_io ? launch_decode_t<bf16, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream)
+                   : launch_decode_t<float, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream);
 }
 
 }  // namespace gla

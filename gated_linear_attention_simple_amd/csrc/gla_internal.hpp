@@ -115,8 +115,9 @@ hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, in
                       float* dS0, void* ws, hipStream_t stream);
 
 bool decode_supported(int dk, int dv);
+// slots == nullptr: row n uses page n of S; else page slots[n] of a P-page pool.
 hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* lambda, float* S, float scale, void* o,
-                         hipStream_t stream);
+                         const void* v, const float* lambda, float* S, const int* slots, int P, float scale,
+                         void* o, hipStream_t stream);
 
 }  // namespace gla

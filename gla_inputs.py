@@ -27,6 +27,16 @@ def laplace_lambdas(H: int = 16):
     return [1.0 - 10.0 ** (-1.0 - 2.0 * h / (H - 1)) for h in range(H)]
 
 
+def page_lambdas(H: int = 16, t_min: float = 1.0, t_max: float = 2048.0):
+    """The Laplace 3B post's geometric decay schedule (section "i14 and the Laplace 3B
+    architecture", paragraph *Decay schedule*) read as half-lives spaced geometrically
+    from t_min to t_max tokens: lambda_h = 2^(-1 / half-life_h).  Head 0 is 0.5, so
+    lambda^C underflows fp32's normal range at C = 128 (a stress input)."""
+    if H == 1:
+        return [2.0 ** (-1.0 / t_min)]
+    return [2.0 ** (-1.0 / (t_min * (t_max / t_min) ** (h / (H - 1)))) for h in range(H)]
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

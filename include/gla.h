@@ -141,6 +141,28 @@ int gla_decode_step(int dtype, int N, int H, int dk, int dv,
                     const float* lambda, float* S, float scale, void* o,
                     void* stream);
 
+/*
+ * The same decode step on a pool of state pages (Laplace 3B post, section
+ * "Optimizing inference on Trainium2": the serving stack gives every sequence
+ * one fixed state page, and decode batches are padded to fixed widths).
+ *   pool   [P][H][dk][dv] fp32, one page per sequence slot, updated in place
+ *   slots  [N] int32 (device): row n of q, k, v, o uses page slots[n].  A slot
+ *          outside [0, P) -- use -1 for a padding row -- touches no page and
+ *          gives a zero output row.  Two rows of one call must not share a
+ *          page (they would race).
+ *   q, k, v, o, lambda, scale   as in gla_decode_step
+ * Each (row, head) is computed on its own: a sequence's outputs and page are
+ * bit-identical whatever batch, position or padding it is decoded in.  A
+ * prefill hands over by passing a page range of the pool as gla_fwd_chunked's
+ * S_final (batch element b -> page first + b).
+ * Errors: as gla_decode_step; P < 0 or a NULL slots pointer -> GLA_ERR_INVALID_ARG.
+ * No workspace.  One kernel launch per call.
+ */
+int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv,
+                         const void* q, const void* k, const void* v,
+                         const float* lambda, float* pool, int P, const int* slots,
+                         float scale, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     for name in decl:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert set(gla.SYMBOLS) <= set(decl)
-    assert lib.gla_abi_version() == 1
+    assert lib.gla_abi_version() == 2
 
 
 def test_status_strings():
@@ -85,6 +85,20 @@ def test_decode_rejects_bad_arguments():
     assert d(q=None) == gla.GLA_ERR_INVALID_ARG
     assert d(S=MIS) == gla.GLA_ERR_INVALID_ARG
     assert d(N=0, q=None) == gla.GLA_OK        # nothing to do, nothing enqueued
+
+
+def test_decode_pool_rejects_bad_arguments():
+    lib = gla.load()
+    d = lambda dtype=1, N=4, H=16, dk=96, dv=192, pool=P, Pn=8, slots=P: lib.gla_decode_step_pool(
+        dtype, N, H, dk, dv, P, P, P, P, pool, Pn, slots, 1.0, P, None)
+    assert d(dtype=5) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(Pn=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(dk=80) == gla.GLA_ERR_UNSUPPORTED
+    assert d(slots=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(slots=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert d(pool=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=0, slots=None) == gla.GLA_OK
 
 
 def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,

@@ -85,3 +85,14 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("chunk", [128, 64])
+def test_page_decay_schedule(chunk):
+    """The pages' geometric half-life schedule (head 0: lambda = 0.5, whose
+    powers leave fp32's normal range inside a 128-token chunk) as a stress set
+    for the backward, dlambda included."""
+    w = gi.workloads()[1]
+    w = gi.Workload(w.name + "-page-decay", w.B, w.T, w.H, w.dk, w.dv, w.chunk, w.dtype,
+                    tuple(gi.page_lambdas(w.H)), w.scale)
+    _run(w, seed=90 + chunk, B=2, T=600, chunk=chunk, s0_var=0.01)

@@ -225,3 +225,15 @@ def test_causality():
     o2, _ = _fwd(y)
     torch.cuda.synchronize()
     assert torch.equal(o[:, :cut], o2[:, :cut])
+
+
+@pytest.mark.parametrize("chunk,chain", [(128, "0"), (128, "1"), (64, "0")])
+def test_page_decay_schedule(chunk, chain, monkeypatch):
+    """The pages' geometric half-life schedule (head 0: lambda = 0.5, so lambda^C
+    underflows fp32's normal range at C = 128) on the Laplace-layer shape, through
+    the segment split and the tiled chain."""
+    monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+    w = gi.workloads()[1]
+    w = gi.Workload(w.name + "-page-decay", w.B, w.T, w.H, w.dk, w.dv, chunk, w.dtype,
+                    tuple(gi.page_lambdas(w.H)), w.scale)
+    _run_and_check(w, seed=95 + chunk, chunk=chunk, s0_var=0.01)
