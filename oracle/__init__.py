@@ -17,6 +17,10 @@ Parity status of each function (what pins it is in tests/test_oracle.py):
           form, and the (t+1)(q.dq - k.dk) identity for dlambda.
   decode  pinned: k decode steps == forward over the same k tokens, and the
           lambda=0 / lambda=1 closed forms.
+  epilogue  pinned: closed forms -- a constant head vector normalises to
+          sign * w of its tier, a one-hot value with a gate of sigmoid(ln 3)
+          = 3/4 gives the 7/4 channel ratio, a = 0 gives the half skip,
+          silu(ln 3) = (3/4) ln 3, a zero vector stays zero (eps > 0).
 """
 from __future__ import annotations
 
@@ -58,7 +62,10 @@ def _bind(lib):
                                    _D, _D, i]
     lib.gla_oracle_decode.argtypes = [i, i, i, i, _D, _D, _D, _D, _D,
                                       ctypes.c_double, _D, i]
-    for f in (lib.gla_oracle_fwd, lib.gla_oracle_bwd, lib.gla_oracle_decode):
+    lib.gla_oracle_epilogue.argtypes = [i, i, i, i, _D, _D, _D, _D, _D, _D, _D,
+                                        ctypes.POINTER(ctypes.c_int), i, ctypes.c_double, _D, i]
+    for f in (lib.gla_oracle_fwd, lib.gla_oracle_bwd, lib.gla_oracle_decode,
+              lib.gla_oracle_epilogue):
         f.restype = ctypes.c_int
     lib.gla_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -158,6 +165,24 @@ def decode(q, k, v, lam, S, scale=1.0, nthreads=0, _lib_=None):
     return o, S
 
 
+def epilogue(q, k, v, o, g, a, w, tier, eps=1e-6, nthreads=0, _lib_=None):
+    """Mixer epilogue: q,k [..., H, dk]; v, o, g [..., H, dv]; a [H, dk] or None (a = 0);
+    w [n_tiers, dv]; tier [H] ints -> y [..., H, dv]."""
+    q, k, v, o, g, w = map(_f64, (q, k, v, o, g, w))
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    M = int(np.prod(q.shape[:-2]))
+    ap = None if a is None else _f64(a)
+    t = np.ascontiguousarray(np.asarray(tier, dtype=np.int32))
+    y = np.zeros(v.shape)
+    rc = (_lib_ or _load()).gla_oracle_epilogue(
+        M, H, dk, dv, _p(q), _p(k), _p(v), _p(o), _p(g), _p(ap) if ap is not None else None, _p(w),
+        t.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), int(w.shape[0]), float(eps), _p(y), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_epilogue failed")
+    return y
+
+
 class _Variant:
     def __init__(self, lib):
         self.lib = lib
@@ -170,3 +195,6 @@ class _Variant:
 
     def decode(self, *a, **kw):
         return decode(*a, _lib_=self.lib, **kw)
+
+    def epilogue(self, *a, **kw):
+        return epilogue(*a, _lib_=self.lib, **kw)

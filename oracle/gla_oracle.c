@@ -21,6 +21,13 @@
  *     head, shared by every sequence of a batch.
  *   - Section "Optimizing inference" (decode): one fixed state page per
  *     sequence, read and written by one decode step per token.
+ *   - Section "i14 and the Laplace 3B architecture", paragraph "GLA mixer",
+ *     the sentences after the readout (gla_oracle_epilogue): a self-augmentation
+ *     adds a copy of the value gated by the sigmoid of the query dotted with a
+ *     learned per-channel rescaling a of the key (a = 0 gives a half-strength
+ *     skip); each head's output then goes through the RMSNorm of its decay
+ *     tier, the heads are concatenated and gated by SiLU(g).  The equation
+ *     image is missing; the readings are written at the function.
  *
  * Everything is the plain per-token recurrence: no chunking, no blocking, no
  * reassociation.  The reverse-mode routine is the textbook adjoint of that
@@ -32,7 +39,10 @@
  *   q, k, dq, dk : [B][T][H][dk]      v, o, do, dv : [B][T][H][dv]
  *   S0, S_final, dS_T, dS0 : [B][H][dk][dv]      lambda, dlambda : [H]
  *   decode: q, k [N][H][dk], v, o [N][H][dv], S [N][H][dk][dv]
+ *   epilogue: q, k [M][H][dk], v, o, g, y [M][H][dv] (M = rows, e.g. B*T),
+ *             a [H][dk], w [n_tiers][dv], tier [H]
  */
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -239,6 +249,49 @@ int gla_oracle_decode(int N, int H, int dk, int dv,
                      v + IDX_TOK(n, 0, h, 0, 1, H, dv));
         readout(Sp, dk, dv, scale, q + IDX_TOK(n, 0, h, 0, 1, H, dk),
                 o + IDX_TOK(n, 0, h, 0, 1, H, dv));
+    }
+    return 0;
+}
+
+/*
+ * Mixer epilogue, for every row m and head h (readings of the missing image):
+ *   gate   s  = sigmoid( sum_i q_i a_{h,i} k_i )        raw q and k, no `scale`
+ *   x_c       = o_c + s v_c                              o: the mixer readout
+ *   x_hat_c   = x_c / sqrt( mean_c' x_c'^2 + eps ) * w_{tier(h), c}
+ *   y_c       = silu(g_c) x_hat_c,   silu(z) = z sigmoid(z),   sigmoid(z) = 1 / (1 + e^-z)
+ * a == NULL means a = 0 (s = 1/2).  Concatenating the heads is the layout itself.
+ */
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+int gla_oracle_epilogue(int M, int H, int dk, int dv, const double* q, const double* k,
+                        const double* v, const double* o, const double* g, const double* a,
+                        const double* w, const int* tier, int n_tiers, double eps, double* y,
+                        int nthreads) {
+    if (M < 0 || H < 1 || dk < 1 || dv < 1 || n_tiers < 1 || eps < 0) return -1;
+    for (int h = 0; h < H; ++h)
+        if (tier[h] < 0 || tier[h] >= n_tiers) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < (long)M * H; ++u) {
+        const int h = (int)(u % H);
+        const double* qu = q + (size_t)u * dk;
+        const double* ku = k + (size_t)u * dk;
+        double z = 0.0;
+        for (int i = 0; i < dk; ++i) z += qu[i] * (a ? a[(size_t)h * dk + i] : 0.0) * ku[i];
+        const double s = sigmoid(z);
+        double* x = (double*)malloc(sizeof(double) * (size_t)dv);
+        double ss = 0.0;
+        for (int c = 0; c < dv; ++c) {
+            x[c] = o[(size_t)u * dv + c] + s * v[(size_t)u * dv + c];
+            ss += x[c] * x[c];
+        }
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        const double* wt = w + (size_t)tier[h] * dv;
+        for (int c = 0; c < dv; ++c) {
+            const double gc = g[(size_t)u * dv + c];
+            y[(size_t)u * dv + c] = gc * sigmoid(gc) * x[c] * inv * wt[c];
+        }
+        free(x);
     }
     return 0;
 }

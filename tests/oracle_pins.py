@@ -13,7 +13,12 @@ recurrence, written from what the Laplace 3B post states:
 * the state is a fixed dk x dv matrix per head whatever the sequence length
   (section "GLA mixer" and the closing remark of the architecture section);
 * the gradient checks use central finite differences, fp64 autograd of the
-  quadratic (all-pairs) form, and a scaling identity for dlambda.
+  quadratic (all-pairs) form, and a scaling identity for dlambda;
+* the mixer epilogue (section "GLA mixer", after the readout: a value copy
+  gated by sigmoid(q . (a (.) k)), half strength at a = 0; per-tier head
+  RMSNorm; SiLU(g) gate) is checked on closed forms: sigmoid(ln 3) = 3/4,
+  a constant vector normalises to its sign times the tier's weight, a
+  one-hot value shows the gate as a channel ratio.
 
 Each pin takes an oracle-like object (the ``oracle`` package or a variant with
 a planted mistake) and returns True when it holds.
@@ -301,3 +306,73 @@ ALL_PINS = {
     "autograd_quadratic": pin_autograd_quadratic,
     "dlambda_identity": pin_dlambda_identity,
 }
+
+
+# ---------------------------------------------------------------- epilogue
+
+
+def _epi_case(H=3, dk=5, dv=7):
+    rng = np.random.default_rng(RNG_SEED + 7)
+    w = rng.uniform(0.5, 2.0, size=(2, dv))
+    tier = [h % 2 for h in range(H)]
+    return rng, w, tier
+
+
+def pin_epilogue_constant_vector(orc, tol=1e-12):
+    """o + s v constant over the channels (v = 0, o = c): RMSNorm gives sign(c) w,
+    and silu(ln 3) = (3/4) ln 3, so y = sign(c) (3/4) ln 3 w[tier(h)], eps = 0."""
+    rng, w, tier = _epi_case()
+    M, H, dk, dv = 4, 3, 5, 7
+    c = np.array([-2.5, 0.3, 7.0, -0.01])
+    o = np.broadcast_to(c[:, None, None], (M, H, dv)).copy()
+    v = np.zeros((M, H, dv))
+    q, k = rng.normal(size=(M, H, dk)), rng.normal(size=(M, H, dk))
+    g = np.full((M, H, dv), np.log(3.0))
+    y = orc.epilogue(q, k, v, o, g, rng.normal(size=(H, dk)), w, tier, eps=0.0)
+    want = np.sign(c)[:, None, None] * 0.75 * np.log(3.0) * w[np.array(tier)][None]
+    return bool(rel(y, want) < tol)
+
+
+def pin_epilogue_gate_ratio(orc, tol=1e-12):
+    """o = 1, v = e_0 and q . (a (.) k) = ln 3 give the gate 3/4, so channel 0 of x
+    is 7/4 and the others 1: y_0 / y_c = 7/4 (w = 1, g constant); with a = 0 the
+    gate is 1/2 and the ratio 3/2."""
+    M, H, dk, dv = 2, 2, 4, 6
+    o = np.ones((M, H, dv))
+    v = np.zeros((M, H, dv))
+    v[..., 0] = 1.0
+    q = np.zeros((M, H, dk))
+    k = np.zeros((M, H, dk))
+    q[..., 2] = 2.0
+    k[..., 2] = 0.5
+    a = np.zeros((H, dk))
+    a[:, 2] = np.log(3.0)               # q . (a (.) k) = 2 * ln 3 * 0.5
+    g = np.full((M, H, dv), 1.3)
+    w = np.ones((1, dv))
+    y = orc.epilogue(q, k, v, o, g, a, w, [0] * H, eps=0.0)
+    y0 = orc.epilogue(q, k, v, o, g, None, w, [0] * H, eps=0.0)
+    r = y[..., 0][..., None] / y[..., 1:]
+    r0 = y0[..., 0][..., None] / y0[..., 1:]
+    return bool(np.abs(r - 1.75).max() < tol and np.abs(r0 - 1.5).max() < tol)
+
+
+def pin_epilogue_zero_and_scale(orc, tol=1e-12):
+    """A zero head vector stays zero (eps > 0, no division by zero), and with
+    eps = 0 scaling o and v by any positive factor leaves y unchanged."""
+    rng, w, tier = _epi_case()
+    M, H, dk, dv = 3, 3, 5, 7
+    q, k = rng.normal(size=(M, H, dk)), rng.normal(size=(M, H, dk))
+    g = rng.normal(size=(M, H, dv))
+    a = rng.normal(size=(H, dk))
+    z = orc.epilogue(q, k, np.zeros((M, H, dv)), np.zeros((M, H, dv)), g, a, w, tier, eps=1e-6)
+    o, v = rng.normal(size=(M, H, dv)), rng.normal(size=(M, H, dv))
+    y1 = orc.epilogue(q, k, v, o, g, a, w, tier, eps=0.0)
+    y2 = orc.epilogue(q, k, 37.0 * v, 37.0 * o, g, a, w, tier, eps=0.0)
+    return bool(np.all(z == 0.0) and rel(y1, y2) < tol)
+
+
+ALL_PINS.update({
+    "epilogue_constant_vector": pin_epilogue_constant_vector,
+    "epilogue_gate_ratio": pin_epilogue_gate_ratio,
+    "epilogue_zero_and_scale": pin_epilogue_zero_and_scale,
+})

@@ -134,6 +134,13 @@ MUTANTS = [
                      v + IDX_TOK(n, 0, h, 0, 1, H, dv));"""),
     ("batch_index_slip", "#define IDX_ST(b, h, H, DK, DV) (((size_t)(b) * (H) + (h)) * (size_t)(DK) * (DV))",
      "#define IDX_ST(b, h, H, DK, DV) (((size_t)(0) * (H) + (h)) * (size_t)(DK) * (DV))"),
+    ("epi_gate_ignores_a", "z += qu[i] * (a ? a[(size_t)h * dk + i] : 0.0) * ku[i];", "z += qu[i] * ku[i];"),
+    ("epi_norm_sum_not_mean", "const double inv = 1.0 / sqrt(ss / dv + eps);", "const double inv = 1.0 / sqrt(ss + eps);"),
+    ("epi_ungated_value", "x[c] = o[(size_t)u * dv + c] + s * v[(size_t)u * dv + c];",
+     "x[c] = o[(size_t)u * dv + c] + v[(size_t)u * dv + c];"),
+    ("epi_silu_is_identity", "y[(size_t)u * dv + c] = gc * sigmoid(gc) * x[c] * inv * wt[c];",
+     "y[(size_t)u * dv + c] = gc * x[c] * inv * wt[c];"),
+    ("epi_wrong_tier", "const double* wt = w + (size_t)tier[h] * dv;", "const double* wt = w;"),
 ]
 
 CHEAP_PINS = [n for n in P.ALL_PINS if n != "autograd_quadratic"]
