@@ -27,9 +27,18 @@ SYMBOLS = (
     "gla_bwd_chunked",
     "gla_decode_step",
     "gla_decode_step_pool",
+    "gla_mixer_epilogue",
+    "gla_decode_step_epilogue",
 )
 
 _lib = None
+
+
+class EpilogueParams(ctypes.Structure):
+    """gla_epilogue_params: device aug_a / norm_w, host head_tier."""
+    _fields_ = [("aug_a", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("head_tier", ctypes.POINTER(ctypes.c_int)), ("n_tiers", ctypes.c_int),
+                ("eps", ctypes.c_float)]
 
 
 class GlaError(RuntimeError):
@@ -61,6 +70,11 @@ def load():
         lib.gla_decode_step.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, f, vp, vp]
         lib.gla_decode_step_pool.restype = i
         lib.gla_decode_step_pool.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, i, vp, f, vp, vp]
+        ep = ctypes.POINTER(EpilogueParams)
+        lib.gla_mixer_epilogue.restype = i
+        lib.gla_mixer_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, ep, vp, vp]
+        lib.gla_decode_step_epilogue.restype = i
+        lib.gla_decode_step_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, vp, i, vp, f, ep, vp, vp]
         _lib = lib
     return _lib
 
@@ -212,3 +226,75 @@ def decode_step_pool(q, k, v, lam, pool, slots, scale=1.0, o=None, stream=None):
     if st != GLA_OK:
         raise GlaError(st, "gla_decode_step_pool")
     return o
+
+
+def _epi_params(H, dk, dv, aug_a, norm_w, head_tier, eps, dev):
+    if aug_a is not None:
+        _check(aug_a, "aug_a", (H, dk), torch.float32, dev)
+    n_tiers = norm_w.shape[0]
+    _check(norm_w, "norm_w", (n_tiers, dv), torch.float32, dev)
+    tiers = [int(t) for t in head_tier]
+    if len(tiers) != H:
+        raise ValueError(f"head_tier: expected {H} entries, got {len(tiers)}")
+    tier_arr = (ctypes.c_int * H)(*tiers)
+    p = EpilogueParams(None if aug_a is None else aug_a.data_ptr(), norm_w.data_ptr(),
+                       ctypes.cast(tier_arr, ctypes.POINTER(ctypes.c_int)), n_tiers, float(eps))
+    return p, tier_arr
+
+
+def mixer_epilogue(q, k, v, o, g, norm_w, head_tier, aug_a=None, eps=1e-6, y=None, stream=None):
+    """y = silu(g) * RMSNorm_tier(o + sigmoid(q.(a*k)) v) per (row, head).
+    q, k [..., H, dk]; v, o, g [..., H, dv]; norm_w [n_tiers, dv] fp32; head_tier: H ints;
+    aug_a [H, dk] fp32 or None.  `y` may be `o` (in place).  Returns y."""
+    lib = load()
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    lead = tuple(q.shape[:-2])
+    M = 1
+    for d in lead:
+        M *= int(d)
+    dev = q.device
+    _check(q, "q", lead + (H, dk), q.dtype, dev)
+    _check(k, "k", lead + (H, dk), q.dtype, dev)
+    for t, name in ((v, "v"), (o, "o"), (g, "g")):
+        _check(t, name, lead + (H, dv), q.dtype, dev)
+    if y is None:
+        y = torch.empty(lead + (H, dv), dtype=q.dtype, device=dev)
+    _check(y, "y", lead + (H, dv), q.dtype, dev)
+    p, _keep = _epi_params(H, dk, dv, aug_a, norm_w, head_tier, eps, dev)
+    st = lib.gla_mixer_epilogue(_dt(q), M, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(g),
+                                ctypes.byref(p), _ptr(y), _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_mixer_epilogue")
+    return y
+
+
+def decode_step_epilogue(q, k, v, g, lam, S, norm_w, head_tier, aug_a=None, eps=1e-6, scale=1.0,
+                         slots=None, y=None, stream=None):
+    """Decode step with the epilogue fused: S (pages [N, H, dk, dv], or a pool [P, H, dk, dv]
+    indexed by int32 `slots`) is updated in place; returns y [N, H, dv]."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    _check(q, "q", (N, H, dk), q.dtype, dev)
+    _check(k, "k", (N, H, dk), q.dtype, dev)
+    _check(v, "v", (N, H, dv), q.dtype, dev)
+    _check(g, "g", (N, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    P = S.shape[0]
+    if slots is None:
+        _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+    else:
+        _check(S, "pool", (P, H, dk, dv), torch.float32, dev)
+        _check(slots, "slots", (N,), torch.int32, dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(y, "y", (N, H, dv), q.dtype, dev)
+    p, _keep = _epi_params(H, dk, dv, aug_a, norm_w, head_tier, eps, dev)
+    st = lib.gla_decode_step_epilogue(_dt(q), N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(lam),
+                                      _ptr(S), P, _ptr(slots), float(scale), ctypes.byref(p), _ptr(y),
+                                      _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_decode_step_epilogue")
+    return y

@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 namespace {
 
 // gfx950 parts (MI350X / MI355X) have 256 compute units; the launch plan is
@@ -41,11 +43,33 @@ int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     return GLA_OK;
 }
 
+// Checks the epilogue parameters and fills the device-side argument block
+// (tier map by value).  Tensor pointers are checked by the callers.
+int epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::EpilogueArgs* a) {
+    if (ep == nullptr || !ok_ptr(ep->norm_w) || !ok_opt(ep->aug_a) || ep->head_tier == nullptr ||
+        ep->n_tiers < 1 || !(ep->eps >= 0.f) || !std::isfinite(ep->eps))
+        return GLA_ERR_INVALID_ARG;
+    if (H > GLA_EPI_MAX_HEADS || !gla::epilogue_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
+    *a = gla::EpilogueArgs{};
+    for (int h = 0; h < H; ++h) {
+        const int t = ep->head_tier[h];
+        if (t < 0 || t >= ep->n_tiers) return GLA_ERR_INVALID_ARG;
+        a->tier[h] = t;
+    }
+    a->H = H;
+    a->aug_a = ep->aug_a;
+    a->norm_w = ep->norm_w;
+    a->eps = ep->eps;
+    return GLA_OK;
+}
+
+static_assert(GLA_EPI_MAX_HEADS == gla::kEpiMaxHeads, "tier map capacity");
+
 }  // namespace
 
 extern "C" {
 
-int gla_abi_version(void) { return 2; }
+int gla_abi_version(void) { return 3; }
 
 const char* gla_status_str(int status) {
     switch (status) {
@@ -111,7 +135,7 @@ int gla_decode_step(int dtype, int N, int H, int dk, int dv, const void* q, cons
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(S) || !ok_ptr(o))
         return GLA_ERR_INVALID_ARG;
     const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, nullptr, 0,
-                                              scale, o, static_cast<hipStream_t>(stream));
+                                              scale, o, nullptr, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 
@@ -127,7 +151,50 @@ int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv, const void* q,
         return GLA_ERR_INVALID_ARG;
     if (P > 0 && !ok_ptr(pool)) return GLA_ERR_INVALID_ARG;
     const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, pool, slots, P,
-                                              scale, o, static_cast<hipStream_t>(stream));
+                                              scale, o, nullptr, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                       const void* o, const void* g, const gla_epilogue_params* ep, void* y, void* stream) {
+    if (!ok_dtype(dtype) || M < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(M, H, dk, dv)) return GLA_ERR_INVALID_ARG;
+    gla::EpilogueArgs a;
+    const int st = epi_fill(ep, H, dk, dv, &a);
+    if (st != GLA_OK) return st;
+    if (M == 0) return GLA_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(g) || !ok_ptr(y))
+        return GLA_ERR_INVALID_ARG;
+    a.units = (long)M * H;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.g = g;
+    a.y = y;
+    const hipError_t err = gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                             const void* g, const float* lambda, float* S, int P, const int* slots, float scale,
+                             const gla_epilogue_params* ep, void* y, void* stream) {
+    if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
+    if (slots != nullptr && P < 0) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(N, H, dk, dv) || (slots != nullptr && !sane_count(P, H, dk, dv))) return GLA_ERR_INVALID_ARG;
+    if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
+    if ((long)N * H > 2147483647L) return GLA_ERR_UNSUPPORTED;
+    gla::EpilogueArgs a;
+    const int st = epi_fill(ep, H, dk, dv, &a);
+    if (st != GLA_OK) return st;
+    if (N == 0) return GLA_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(lambda) || !ok_ptr(y) || !ok_opt(slots))
+        return GLA_ERR_INVALID_ARG;
+    if ((slots == nullptr || P > 0) && !ok_ptr(S)) return GLA_ERR_INVALID_ARG;
+    a.units = (long)N * H;
+    a.g = g;
+    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, slots,
+                                              slots ? P : 0, scale, y, &a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 

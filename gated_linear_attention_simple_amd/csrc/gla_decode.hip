@@ -18,16 +18,22 @@
 // [P][H][dk][dv]; a slot outside [0, P) (-1 marks a padding row) touches no
 // page and yields a zero output.  Every (row, head) is computed alone, so a
 // sequence's results do not depend on the batch it is in.
+//
+// Epilogue form (section "GLA mixer", the sentences after the readout): the
+// workgroup holds a head's whole output row, so the value copy gated by
+// sigmoid(q . (a (.) k)), the head RMSNorm of the head's tier and the SiLU(g)
+// gate are applied before the store (as in gla_epilogue.hip).
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
+#include "gla_tile.hpp"
 
 namespace gla {
 
-template <typename E, int DK, int DV, int RG, bool POOL>
+template <typename E, int DK, int DV, int RG, bool POOL, bool EPI>
 __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
     int H, const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ lambda, float* __restrict__ S, const int* __restrict__ slots, int P, float scale,
-    E* __restrict__ o) {
+    E* __restrict__ o, EpilogueArgs ep) {
     constexpr int NCG = DV / 4;          // float4 column groups per row
     constexpr int NT = NCG * RG;         // threads
     constexpr int RPT = DK / RG;         // rows per thread
@@ -36,6 +42,7 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
     __shared__ float qs[DK];
     __shared__ float ks[DK];
     __shared__ f32x4 part[RG][NCG];
+    __shared__ float red[NT / 64 + 1];    // epilogue: gate logit, per-wave sums of squares
 
     const int unit = blockIdx.x;         // n * H + h
     const int h = unit % H;
@@ -81,28 +88,68 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
         __builtin_nontemporal_store(s, Sp + (size_t)r * NCG + cg);
     }
     part[rg][cg] = acc;
+    if constexpr (EPI) {
+        // gate logit q . (a_h (.) k) by the first wave (a = 0 without aug_a)
+        if (t < 64) {
+            float zp = 0.f;
+            if (ep.aug_a)
+                for (int i = t; i < DK; i += 64) zp += qs[i] * ep.aug_a[(size_t)h * DK + i] * ks[i];
+            zp = wave_sum(zp);
+            if (t == 0) red[NT / 64] = zp;
+        }
+    }
     __syncthreads();
-    for (int c = t; c < DV; c += NT) {
-        float sum = 0.f;
+    if constexpr (!EPI) {
+        for (int c = t; c < DV; c += NT) {
+            float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < RG; ++j) sum += part[j][c / 4][c % 4];
-        o[(size_t)unit * DV + c] = from_f32<E>(scale * sum);
+            for (int j = 0; j < RG; ++j) sum += part[j][c / 4][c % 4];
+            o[(size_t)unit * DV + c] = from_f32<E>(scale * sum);
+        }
+    } else {
+        static_assert(DV <= NT, "one output column per thread");
+        const float s = 1.f / (1.f + expf(-red[NT / 64]));
+        float x = 0.f;
+        if (t < DV) {
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < RG; ++j) sum += part[j][t / 4][t % 4];
+            x = scale * sum + s * to_f32(v[(size_t)unit * DV + t]);
+        }
+        const float ssw = wave_sum(x * x);
+        __syncthreads();  // the gate logit has been read
+        if (t % 64 == 0) red[t / 64] = ssw;
+        __syncthreads();
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) ss += red[w];
+        if (t < DV) {
+            const float inv = 1.f / sqrtf(ss / DV + ep.eps);
+            const float gc = to_f32(static_cast<const E*>(ep.g)[(size_t)unit * DV + t]);
+            o[(size_t)unit * DV + t] =
+                from_f32<E>(gc / (1.f + expf(-gc)) * x * inv * ep.norm_w[(size_t)ep.tier[h] * DV + t]);
+        }
     }
 }
 
 template <typename E, int DK, int DV, int RG>
 static hipError_t launch_decode_t(int N, int H, const void* q, const void* k, const void* v,
                                   const float* lambda, float* S, const int* slots, int P, float scale, void* o,
-                                  hipStream_t stream) {
+                                  const EpilogueArgs* epi, hipStream_t stream) {
     const int units = N * H;
-    if (slots)
-        hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG, true>), dim3(units), dim3((DV / 4) * RG), 0, stream,
-                           H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
-                           lambda, S, slots, P, scale, static_cast<E*>(o));
-    else
-        hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG, false>), dim3(units), dim3((DV / 4) * RG), 0, stream,
-                           H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
-                           lambda, S, nullptr, 0, scale, static_cast<E*>(o));
+    const EpilogueArgs ep = epi ? *epi : EpilogueArgs{};
+#define GLA_DEC(POOL_, EPI_)                                                                                     \
+    hipLaunchKernelGGL((decode_kernel<E, DK, DV, RG, POOL_, EPI_>), dim3(units), dim3((DV / 4) * RG), 0, stream, \
+                       H, static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), lambda,  \
+                       S, slots, P, scale, static_cast<E*>(o), ep)
+    if (slots) {
+        if (epi) GLA_DEC(true, true);
+        else GLA_DEC(true, false);
+    } else {
+        if (epi) GLA_DEC(false, true);
+        else GLA_DEC(false, false);
+    }
+#undef GLA_DEC
     return hipGetLastError();
 }
 
@@ -112,13 +159,14 @@ bool decode_supported(int dk, int dv) {
 
 hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
                          const void* v, const float* lambda, float* S, const int* slots, int P, float scale,
-                         void* o, hipStream_t stream) {
+                         void* o, const EpilogueArgs* epi, hipStream_t stream) {
     if (dk == 96 && dv == 192) {
-        return bf16_io ? launch_decode_t<bf16, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream)
-                       : launch_decode_t<float, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream);
+        return bf16_io
+                   ? launch_decode_t<bf16, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, epi, stream)
+                   : launch_decode_t<float, 96, 192, 4>(N, H, q, k, v, lambda, S, slots, P, scale, o, epi, stream);
     }
-    return bf16_io ? launch_decode_t<bf16, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream)
-                   : launch_decode_t<float, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, stream);
+    return bf16_io ? launch_decode_t<bf16, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, epi, stream)
+                   : launch_decode_t<float, 16, 32, 16>(N, H, q, k, v, lambda, S, slots, P, scale, o, epi, stream);
 }
 
 }  // namespace gla

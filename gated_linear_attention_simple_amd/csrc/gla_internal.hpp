@@ -115,9 +115,32 @@ hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, in
                       float* dS0, void* ws, hipStream_t stream);
 
 bool decode_supported(int dk, int dv);
+// Mixer epilogue: device pointers, the tier map travels by value.
+constexpr int kEpiMaxHeads = 64;
+
+struct EpilogueArgs {
+    long units;           // rows * H
+    int H;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* g;
+    void* y;
+    const float* aug_a;
+    const float* norm_w;
+    float eps;
+    int tier[kEpiMaxHeads];
+};
+
+bool epilogue_supported(int dk, int dv);
+hipError_t launch_epilogue(bool bf16_io, int dk, int dv, const EpilogueArgs& a, hipStream_t stream);
+
 // slots == nullptr: row n uses page n of S; else page slots[n] of a P-page pool.
+// epi == nullptr: o is the readout; else o receives the epilogue output y
+// (epi->g the gate; q, k, v, o, y fields of epi unused).
 hipError_t launch_decode(bool bf16_io, int N, int H, int dk, int dv, const void* q, const void* k,
                          const void* v, const float* lambda, float* S, const int* slots, int P, float scale,
-                         void* o, hipStream_t stream);
+                         void* o, const EpilogueArgs* epi, hipStream_t stream);
 
 }  // namespace gla

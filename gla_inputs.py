@@ -17,7 +17,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-_TID = {"q": 0, "k": 1, "v": 2, "do": 3, "S0": 4, "state": 5, "dS": 6}
+_TID = {"q": 0, "k": 1, "v": 2, "do": 3, "S0": 4, "state": 5, "dS": 6, "g": 7, "aug": 8, "normw": 9}
 
 
 def laplace_lambdas(H: int = 16):
@@ -141,3 +141,23 @@ def decode_state(w: Workload, device, seed: int, layer: int, N=None, out=None):
     N = w.B if N is None else N
     return normal((N, w.H, w.dk, w.dv), w.s0_var, torch.float32, device, seed,
                   "state", layer, 0, out=out)
+
+
+def contiguous_tiers(H: int, n_tiers: int):
+    """Head h -> tier h * n_tiers // H: contiguous groups of heads in decay order."""
+    return [h * n_tiers // H for h in range(H)]
+
+
+def epilogue_inputs(w: Workload, device, seed: int, lead, n_tiers=4, aug_var=None, layer=0, step=0):
+    """Epilogue parameters and gate for rows `lead` (a shape tuple): g [*lead, H, dv] ~ N(0, 1)
+    in the workload dtype; fp32 aug_a [H, dk] ~ N(0, aug_var) (default dk, which makes the
+    gate logit q . (a k) about N(0, 1) for q, k ~ N(0, 1/dk)); fp32 norm_w [n_tiers, dv] =
+    1 + N(0, 0.1); the contiguous tier map."""
+    dt = torch_dtype(w.dtype)
+    av = float(w.dk) if aug_var is None else aug_var
+    return {
+        "g": normal(tuple(lead) + (w.H, w.dv), 1.0, dt, device, seed, "g", layer, step),
+        "aug_a": normal((w.H, w.dk), av, torch.float32, device, seed, "aug"),
+        "norm_w": normal((n_tiers, w.dv), 0.1, torch.float32, device, seed, "normw") + 1.0,
+        "tier": contiguous_tiers(w.H, n_tiers),
+    }

@@ -163,6 +163,61 @@ int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv,
                          const float* lambda, float* pool, int P, const int* slots,
                          float scale, void* o, void* stream);
 
+/*
+ * Mixer epilogue (Laplace 3B post, section "i14 and the Laplace 3B
+ * architecture", paragraph "GLA mixer", the sentences after the readout): a
+ * value copy gated by a self-augmentation sigmoid, a head RMSNorm shared by the
+ * heads of one decay tier, and a SiLU output gate.  For every row m and head h:
+ *       s = sigmoid( q[m,h] . (aug_a[h] (.) k[m,h]) )
+ *       x = o[m,h] + s * v[m,h]
+ *       y[m,h] = silu(g[m,h]) (.) x / sqrt(mean_j x_j^2 + eps) (.) norm_w[head_tier[h]]
+ * q and k enter unscaled (the readout's scale is already inside o).  With
+ * aug_a == NULL the gate is sigmoid(0) = 1/2: a half-strength value skip.
+ * The head concatenation is the [..][H][dv] layout itself.
+ */
+#define GLA_EPI_MAX_HEADS 64
+
+typedef struct {
+    const float* aug_a;      /* [H][dk] fp32 device, self-augmentation vectors; NULL = 0 */
+    const float* norm_w;     /* [n_tiers][dv] fp32 device, RMSNorm weight of each tier */
+    const int* head_tier;    /* [H] int32 HOST array: the tier of head h, in [0, n_tiers);
+                                read during the call only */
+    int n_tiers;             /* >= 1 */
+    float eps;               /* >= 0, finite; added to the mean square */
+} gla_epilogue_params;
+
+/*
+ *   q, k       [M][H][dk] (dtype)        the mixer inputs of the rows
+ *   v, o, g    [M][H][dv] (dtype)        values, the readout, the output-gate logits
+ *   y          [M][H][dv] (dtype)        output; may alias o (each element of o
+ *                                         is read before y's element is written)
+ * M = B * T for a prefill (token rows), N for a decode batch.  H <= 64.
+ * Supported (dk, dv): (96, 192), (16, 32).  One kernel launch, no workspace.
+ * Errors: NULL ep, a NULL/misaligned tensor, n_tiers < 1, a head_tier entry
+ * out of range, a negative or non-finite eps, M < 0 -> GLA_ERR_INVALID_ARG;
+ * H > 64 or another (dk, dv) -> GLA_ERR_UNSUPPORTED.  M == 0 enqueues nothing.
+ */
+int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv,
+                       const void* q, const void* k, const void* v,
+                       const void* o, const void* g,
+                       const gla_epilogue_params* ep, void* y, void* stream);
+
+/*
+ * Decode step with the epilogue fused into it: the state update and readout of
+ * gla_decode_step (slots == NULL, S holds N pages [N][H][dk][dv]) or of
+ * gla_decode_step_pool (slots != NULL, S is a pool of P pages), then the
+ * epilogue above on the readout; only y is written (the readout o is never
+ * stored).  A padding row (slot outside [0, P)) gives a zero y row.
+ *   g   [N][H][dv] (dtype) output-gate logits;  y  [N][H][dv] (dtype) output
+ * Other arguments and errors: as gla_decode_step(_pool) and gla_mixer_epilogue
+ * (P is ignored when slots == NULL).  One kernel launch, no workspace.
+ */
+int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const float* lambda, float* S, int P, const int* slots,
+                             float scale, const gla_epilogue_params* ep, void* y,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

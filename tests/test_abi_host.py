@@ -29,7 +29,7 @@ def test_library_loads_and_exports_header_symbols():
     for name in decl:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert set(gla.SYMBOLS) <= set(decl)
-    assert lib.gla_abi_version() == 2
+    assert lib.gla_abi_version() == 3
 
 
 def test_status_strings():
@@ -99,6 +99,62 @@ def test_decode_pool_rejects_bad_arguments():
     assert d(slots=MIS) == gla.GLA_ERR_INVALID_ARG
     assert d(pool=None) == gla.GLA_ERR_INVALID_ARG
     assert d(N=0, slots=None) == gla.GLA_OK
+
+
+def _epi(H=16, n_tiers=4, tiers=None, eps=1e-6, w=P, a=None):
+    tiers = [h % n_tiers for h in range(H)] if tiers is None else tiers
+    arr = (ctypes.c_int * max(len(tiers), 1))(*tiers)
+    val = lambda x: None if x is None else x.value
+    return gla.EpilogueParams(val(a), val(w), ctypes.cast(arr, ctypes.POINTER(ctypes.c_int)), n_tiers, eps), arr
+
+
+def test_mixer_epilogue_rejects_bad_arguments():
+    lib = gla.load()
+
+    def e(dtype=1, M=8, H=16, dk=96, dv=192, q=P, g=P, y=P, **kw):
+        p, keep = _epi(H=H, **kw)
+        return lib.gla_mixer_epilogue(dtype, M, H, dk, dv, q, P, P, P, g, ctypes.byref(p), y, None)
+
+    assert e(dtype=7) == gla.GLA_ERR_INVALID_ARG
+    assert e(M=-1) == gla.GLA_ERR_INVALID_ARG
+    assert e(dk=64) == gla.GLA_ERR_UNSUPPORTED
+    assert e(H=65) == gla.GLA_ERR_UNSUPPORTED
+    assert e(tiers=[0] * 15 + [4]) == gla.GLA_ERR_INVALID_ARG      # tier out of range
+    assert e(tiers=[-1] + [0] * 15) == gla.GLA_ERR_INVALID_ARG
+    assert e(n_tiers=0, tiers=[0] * 16) == gla.GLA_ERR_INVALID_ARG
+    assert e(eps=-1.0) == gla.GLA_ERR_INVALID_ARG
+    assert e(eps=float("nan")) == gla.GLA_ERR_INVALID_ARG
+    assert e(eps=float("inf")) == gla.GLA_ERR_INVALID_ARG
+    assert e(w=None) == gla.GLA_ERR_INVALID_ARG
+    assert e(w=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert e(a=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert e(q=None) == gla.GLA_ERR_INVALID_ARG
+    assert e(g=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert e(y=None) == gla.GLA_ERR_INVALID_ARG
+    assert e(M=0, q=None) == gla.GLA_OK
+    assert lib.gla_mixer_epilogue(1, 8, 16, 96, 192, P, P, P, P, P, None, P, None) == gla.GLA_ERR_INVALID_ARG
+
+
+def test_decode_epilogue_rejects_bad_arguments():
+    lib = gla.load()
+
+    def d(dtype=1, N=4, H=16, dk=96, dv=192, S=P, Pn=8, slots=None, g=P, y=P, **kw):
+        p, keep = _epi(H=H, **kw)
+        return lib.gla_decode_step_epilogue(dtype, N, H, dk, dv, P, P, P, g, P, S, Pn, slots, 1.0,
+                                            ctypes.byref(p), y, None)
+
+    assert d(dtype=2) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=-3) == gla.GLA_ERR_INVALID_ARG
+    assert d(dk=32) == gla.GLA_ERR_UNSUPPORTED
+    assert d(H=70) == gla.GLA_ERR_UNSUPPORTED
+    assert d(slots=P, Pn=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(slots=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert d(S=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(slots=P, Pn=0, S=None, N=0) == gla.GLA_OK
+    assert d(g=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(y=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert d(tiers=[9] * 16) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=0, g=None) == gla.GLA_OK
 
 
 def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,
