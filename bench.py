@@ -59,6 +59,10 @@ def train_flops_per_token_head(C, dk=96, dv=192):
 
 DEC_BYTES_PER_SEQ_HEAD = 2 * 96 * 192 * 4 + 2 * (96 + 96 + 192 + 192)   # state R+W + q,k,v,o bf16
 DEC_FLOPS_PER_SEQ_HEAD = 4 * 96 * 192
+# Mixer epilogue: q, k in (dk each), v, o, g in and y out (dv each), bf16
+EPI_BYTES_PER_TOKEN_HEAD = 2 * (2 * 96 + 4 * 192)
+# Decode with the epilogue fused: the decode step's bytes plus the gate g (y replaces o)
+DEC_EPI_BYTES_PER_SEQ_HEAD = DEC_BYTES_PER_SEQ_HEAD + 2 * 192
 
 
 def src_digest():
@@ -173,6 +177,39 @@ class TrainLeg:
                 raise RuntimeError(f"{name}: {self.gla.status_str(st)}")
 
 
+def epi_params(gla, e):
+    """gla_epilogue_params for seeded epilogue inputs; returns (struct, tier array) to keep alive."""
+    tiers = (ctypes.c_int * len(e["tier"]))(*e["tier"])
+    p = gla.EpilogueParams(e["aug_a"].data_ptr(), e["norm_w"].data_ptr(),
+                           ctypes.cast(tiers, ctypes.POINTER(ctypes.c_int)), e["norm_w"].shape[0], 1e-6)
+    return p, tiers
+
+
+class EpilogueLeg:
+    """Pre-marshalled gla_mixer_epilogue over B*T token rows of the mixer shape (bf16)."""
+
+    def __init__(self, gla, gi, torch, w, seed):
+        dev = torch.device("cuda:0")
+        x = gi.fwd_inputs(w, dev, seed, with_do=True)
+        e = gi.epilogue_inputs(w, dev, seed, (w.B, w.T))
+        self.keep = (x, e)
+        self.y = torch.empty_like(x["v"])
+        self.token_heads = w.B * w.T * w.H
+        self.params, self.tiers = epi_params(gla, e)
+        self.stream = torch.cuda.current_stream()
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        # the readout o is stood in for by another N(0, 1) tensor of its shape
+        self.args = (gla.GLA_BF16, w.B * w.T, w.H, w.dk, w.dv, p(x["q"]), p(x["k"]), p(x["v"]), p(x["do"]),
+                     p(e["g"]), ctypes.byref(self.params), p(self.y), ctypes.c_void_p(self.stream.cuda_stream))
+        self.fn = gla.load().gla_mixer_epilogue
+        self.gla = gla
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"gla_mixer_epilogue: {self.gla.status_str(st)}")
+
+
 class DecodeLeg:
     """The 1,280-sequence x 24-layer decode workload with its fp32 state pool on the GPU."""
 
@@ -206,10 +243,24 @@ class DecodeLeg:
                             p(self.pool[layer]), w.B, p(self.slots), ctypes.c_float(w.scale), p(self.o),
                             ctypes.c_void_p(self.stream.cuda_stream)) for d in self.inputs[layer]]
                           for layer in range(L)]
+        # epilogue-fused form on the direct pages: gate g per (layer, input), shared parameters
+        e = gi.epilogue_inputs(w, dev, seed, (w.B,))
+        self.epi_keep = [e] + [gi.epilogue_inputs(w, dev, seed, (w.B,), layer=layer, step=s)["g"]
+                               for layer in range(L) for s in range(n_inputs)]
+        self.params, self.tiers = epi_params(gla, e)
+        self.fn_epi = gla.load().gla_decode_step_epilogue
+        self.args_epi = [[(gla.GLA_BF16, w.B, w.H, w.dk, w.dv, p(d["q"]), p(d["k"]), p(d["v"]),
+                           p(self.epi_keep[1 + layer * n_inputs + s]), p(self.lam), p(self.pool[layer]), 0, None,
+                           ctypes.c_float(w.scale), ctypes.byref(self.params), p(self.o),
+                           ctypes.c_void_p(self.stream.cuda_stream)) for s, d in enumerate(self.inputs[layer])]
+                         for layer in range(L)]
         self.use_pool = False
+        self.use_epi = False
 
     def launch(self, layer, step):
-        if self.use_pool:
+        if self.use_epi:
+            st = self.fn_epi(*self.args_epi[layer][step % self.n_inputs])
+        elif self.use_pool:
             st = self.fn_pool(*self.args_pool[layer][step % self.n_inputs])
         else:
             st = self.fn(*self.args[layer][step % self.n_inputs])
@@ -455,9 +506,32 @@ def main():
             "ms_per_step": p_wall / K * 1e3, "avg_launch_us": p_avg * 1e6,
             "achieved": per_launch_bytes / p_avg / 1e9, "unit": "GB/s",
             "frac": per_launch_bytes / p_avg / 1e9 / HBM_PEAK_GBS}
+        # the same steps with the mixer epilogue fused into the decode kernel
+        dleg.use_pool, dleg.use_epi = False, True
+        e_wall, e_gpu = time_decode(torch, dleg, K, W)
+        e_avg = e_gpu / (K * w4.decode_layers)
+        eb = DEC_EPI_BYTES_PER_SEQ_HEAD * w4.B * w4.H
+        result["decode"]["epilogue_fused"] = {
+            "kernel": "gla_decode_step_epilogue (decode + gated value copy, tier RMSNorm, SiLU gate)",
+            "ms_per_step": e_wall / K * 1e3, "avg_launch_us": e_avg * 1e6, "alg_bytes_per_launch": eb,
+            "achieved": eb / e_avg / 1e9, "unit": "GB/s", "frac": eb / e_avg / 1e9 / HBM_PEAK_GBS}
         del dleg
         torch.cuda.empty_cache()
     result["ms_per_step"] = f_ms + t_ms + d_ms
+
+    # ---- mixer epilogue pass (not part of the step): the layer's prefill rows and the training width
+    result["epilogue"] = {}
+    for name, wk in (("layer", w1), ("train_width", w2)):
+        eleg = EpilogueLeg(gla, gi, torch, wk, 7)
+        e_wall, e_gpu = time_region(torch, eleg.stream, eleg, K, W)
+        e_avg = e_gpu / K
+        eb = EPI_BYTES_PER_TOKEN_HEAD * eleg.token_heads
+        result["epilogue"][name] = {
+            "kernel": "gla_mixer_epilogue", "rows": wk.B * wk.T, "avg_launch_us": e_avg * 1e6,
+            "alg_bytes_per_launch": eb, "achieved": eb / e_avg / 1e9, "unit": "GB/s",
+            "frac": eb / e_avg / 1e9 / HBM_PEAK_GBS}
+        del eleg
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline_fwd(gi, w1, 1)

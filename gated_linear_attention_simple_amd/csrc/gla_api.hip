@@ -47,7 +47,7 @@ int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
 // (tier map by value).  Tensor pointers are checked by the callers.
 int epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::EpilogueArgs* a) {
     if (ep == nullptr || !ok_ptr(ep->norm_w) || !ok_opt(ep->aug_a) || ep->head_tier == nullptr ||
-        ep->n_tiers < 1 || !(ep->eps >= 0.f) || !std::isfinite(ep->eps))
+        ep->n_tiers < 1 || ep->n_tiers > GLA_EPI_MAX_HEADS || !(ep->eps >= 0.f) || !std::isfinite(ep->eps))
         return GLA_ERR_INVALID_ARG;
     if (H > GLA_EPI_MAX_HEADS || !gla::epilogue_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
     *a = gla::EpilogueArgs{};
@@ -59,6 +59,7 @@ int epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::Epilogue
     a->H = H;
     a->aug_a = ep->aug_a;
     a->norm_w = ep->norm_w;
+    a->n_tiers = ep->n_tiers;
     a->eps = ep->eps;
     return GLA_OK;
 }

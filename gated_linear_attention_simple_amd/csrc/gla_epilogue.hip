@@ -8,10 +8,14 @@
 // i.e. the value copy, the head RMSNorm of the head's decay tier, and the SiLU
 // gate; concatenating the heads is the [M][H][dv] layout itself.
 //
-// One wave per (row, head): lanes stride the dk and dv features, the two sums
-// (gate logit and sum of squares) are butterfly reductions in a fixed order.
-// 2 * dk + 4 * dv elements move per (row, head) for 7 dv + 2 dk flops-ish, so
-// the pass is bound by HBM.
+// A group of LPU lanes per (row, head) (a power of two, 4..64): lane l holds the
+// 16-byte pieces l of the row's q, k (dk) and v, o, g, y (dv).  Every tensor
+// moves in 16-byte buffer loads and stores whose range is the workgroup's own
+// rows, so lanes past a row's end and rows past the last read zeros without a
+// branch, and all loads of a lane (the two parameter rows included) are issued
+// back to back before any arithmetic.  The two sums (gate logit, sum of
+// squares) are butterfly reductions inside the group, in a fixed order.
+// 2 dk + 4 dv elements move per (row, head) for ~10 dv flops: bound by HBM.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
@@ -19,47 +23,185 @@
 namespace gla {
 namespace {
 
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
-    const int lane = threadIdx.x % 64;
-    const long unit = (long)blockIdx.x * 4 + threadIdx.x / 64;  // m * H + h
-    if (unit >= a.units) return;                                  // whole wave
-    const int h = (int)(unit % a.H);
-    const E* q = static_cast<const E*>(a.q) + unit * DK;
-    const E* k = static_cast<const E*>(a.k) + unit * DK;
-    const E* v = static_cast<const E*>(a.v) + unit * DV;
-    const E* o = static_cast<const E*>(a.o) + unit * DV;
-    const E* g = static_cast<const E*>(a.g) + unit * DV;
-    E* y = static_cast<E*>(a.y) + unit * DV;
+// Sum over aligned groups of LPU lanes, every lane of a group receiving the
+// group's sum; a fixed pairing order, so the result is deterministic.  Inside
+// a 16-lane row the pairs come from DPP lane permutations (quad swaps, then
+// the half-row and row mirrors); rows pair up through a 32-lane swizzle, and
+// the two halves of a wave through lane reads.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+template <int LPU>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(LPU == 4 || LPU == 8 || LPU == 16 || LPU == 32 || LPU == 64, "power-of-two group");
+    x += dpp<0xB1>(x);                                  // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);                                  // quad_perm [2,3,0,1]
+    if constexpr (LPU >= 8) x += dpp<0x141>(x);         // row_half_mirror
+    if constexpr (LPU >= 16) x += dpp<0x140>(x);        // row_mirror
+    if constexpr (LPU >= 32)                            // swap the two rows of each 32-lane half
+        x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+    if constexpr (LPU == 64)
+        x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    return x;
+}
 
-    float z = 0.f;
-    if (a.aug_a) {
-        const float* ah = a.aug_a + (size_t)h * DK;
-#pragma unroll
-        for (int i = lane; i < DK; i += 64) z += to_f32(q[i]) * ah[i] * to_f32(k[i]);
-    }
-    z = wave_sum(z);
-    const float s = 1.f / (1.f + expf(-z));
+constexpr int lanes_for(int n) { return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+constexpr int kEpiThreads = 256;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-    constexpr int NC = (DV + 63) / 64;
-    float x[NC];
-    float ss = 0.f;
+// 16-byte piece <-> VEC floats
+template <typename E> struct Piece;
+template <> struct Piece<bf16> {
+    static constexpr int N = 8;
+    __device__ static void unpack(uint4 u, float* f) {
+        const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        const int c = lane + 64 * j;
-        x[j] = c < DV ? to_f32(o[c]) + s * to_f32(v[c]) : 0.f;
-        ss += x[j] * x[j];
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.f / sqrtf(ss / DV + a.eps);
-    const float* w = a.norm_w + (size_t)a.tier[h] * DV;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        const int c = lane + 64 * j;
-        if (c < DV) {
-            const float gc = to_f32(g[c]);
-            y[c] = from_f32<E>(gc / (1.f + expf(-gc)) * x[j] * inv * w[c]);
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
         }
+    }
+    __device__ static uint4 pack(const float* f) {
+        unsigned w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned lo = __builtin_bit_cast(unsigned short, to_bf16(f[2 * i]));
+            const unsigned hi = __builtin_bit_cast(unsigned short, to_bf16(f[2 * i + 1]));
+            w[i] = lo | (hi << 16);
+        }
+        return uint4{w[0], w[1], w[2], w[3]};
+    }
+};
+template <> struct Piece<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(uint4 u, float* f) {
+        f[0] = __builtin_bit_cast(float, u.x);
+        f[1] = __builtin_bit_cast(float, u.y);
+        f[2] = __builtin_bit_cast(float, u.z);
+        f[3] = __builtin_bit_cast(float, u.w);
+    }
+    __device__ static uint4 pack(const float* f) {
+        return uint4{__builtin_bit_cast(unsigned, f[0]), __builtin_bit_cast(unsigned, f[1]),
+                     __builtin_bit_cast(unsigned, f[2]), __builtin_bit_cast(unsigned, f[3])};
+    }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int range) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, __builtin_amdgcn_readfirstlane(range),
+                                             kBufWord3);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <typename E, int DK, int DV>
+struct EpiShape {
+    static constexpr int VEC = Piece<E>::N;
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int NVL = DV / VEC;        // lanes holding a piece of a dv row
+    static constexpr int NKL = DK / VEC;        // lanes holding a piece of a dk row
+    static constexpr int LPU = lanes_for(NVL);  // lanes per (row, head)
+    static constexpr int UPB = kEpiThreads / LPU;  // (row, head) units per batch
+    static_assert(DV % VEC == 0 && DK % VEC == 0 && NVL <= 64 && NKL <= LPU, "row pieces must fit the group");
+};
+
+// sigmoid and SiLU on the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float fast_sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+// Workgroup w takes the batches w, w + G, w + 2G, ... of UPB consecutive units
+// (G = gridDim.x, a multiple of H, so a thread keeps one head throughout and
+// loads its parameter rows once).  The next batch's five row loads are issued
+// before the current batch's arithmetic, into the other of two register sets;
+// a batch past the end has an empty range: it reads zeros and stores nothing.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
+    using Sh = EpiShape<E, DK, DV>;
+    constexpr int VEC = Sh::VEC, ES = Sh::ES, NVL = Sh::NVL, NKL = Sh::NKL, LPU = Sh::LPU, UPB = Sh::UPB;
+    const int lane = threadIdx.x % LPU;
+    const int lu = threadIdx.x / LPU;                       // unit within a batch
+    const long nb = (a.units + UPB - 1) / UPB;              // batches
+    const long G = gridDim.x;
+    const int h = (int)(((long)blockIdx.x * UPB % a.H + lu) % a.H);
+
+    // tier of head h: the map sits in the kernel arguments, so select, never index
+    int tier = 0;
+#pragma unroll
+    for (int i = 0; i < kEpiMaxHeads; ++i) tier = (h == i) ? a.tier[i] : tier;
+
+    // parameter rows: aug_a [H][DK] (absent -> empty range -> zeros), norm_w [tiers][DV]
+    const __amdgpu_buffer_rsrc_t ra = rsrc(a.aug_a, a.aug_a ? a.H * DK * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.norm_w, a.n_tiers * DV * 4);
+    const int oa = lane < NKL ? (h * DK + lane * VEC) * 4 : a.H * DK * 4;
+    const int ow = (tier * DV + (lane < NVL ? lane : 0) * VEC) * 4;
+    float av[VEC], w[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) {
+        Piece<float>::unpack(ld16(ra, oa + 16 * j), av + 4 * j);
+        Piece<float>::unpack(ld16(rw, ow + 16 * j), w + 4 * j);
+    }
+
+    // units of batch b: UPB, fewer in the last batch, 0 past the end
+    auto batch_units = [&](long b) -> int {
+        const long left = a.units - b * UPB;
+        return left <= 0 ? 0 : left < UPB ? (int)left : UPB;
+    };
+    // row loads of batch b: q, k, v, o, g pieces (zeros past the rows' ends)
+    auto load = [&](long b, uint4* r) {
+        const int nu = batch_units(b);
+        const int rk = nu * DK * ES, rv = nu * DV * ES;
+        const int ok = lane < NKL ? (lu * DK + lane * VEC) * ES : rk;
+        const int ov = lane < NVL ? (lu * DV + lane * VEC) * ES : rv;
+        const long u0 = b * UPB;
+        r[0] = ld16(rsrc(static_cast<const E*>(a.q) + u0 * DK, rk), ok);
+        r[1] = ld16(rsrc(static_cast<const E*>(a.k) + u0 * DK, rk), ok);
+        r[2] = ld16(rsrc(static_cast<const E*>(a.v) + u0 * DV, rv), ov);
+        r[3] = ld16(rsrc(static_cast<const E*>(a.o) + u0 * DV, rv), ov);
+        r[4] = ld16(rsrc(static_cast<const E*>(a.g) + u0 * DV, rv), ov);
+    };
+    // one batch: issue the loads of batch b + G into `nxt`, then finish batch b from `cur`
+    auto step = [&](long b, const uint4* cur, uint4* nxt) {
+        load(b + G, nxt);
+        __builtin_amdgcn_sched_barrier(0);   // next batch's loads ahead of this batch's arithmetic
+        float q[VEC], k[VEC], v[VEC], o[VEC], g[VEC];
+        Piece<E>::unpack(cur[0], q);
+        Piece<E>::unpack(cur[1], k);
+        Piece<E>::unpack(cur[2], v);
+        Piece<E>::unpack(cur[3], o);
+        Piece<E>::unpack(cur[4], g);
+
+        float z = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) z += q[e] * av[e] * k[e];
+        const float s = fast_sigmoid(group_sum<LPU>(z));
+
+        float x[VEC];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            x[e] = o[e] + s * v[e];
+            ss += x[e] * x[e];
+        }
+        const float inv = __builtin_amdgcn_rsqf(group_sum<LPU>(ss) * (1.f / DV) + a.eps);
+        float y[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[e] = g[e] * fast_sigmoid(g[e]) * x[e] * inv * w[e];
+        const int rv = batch_units(b) * DV * ES;              // 0 past the end: the store is dropped
+        const int ov = lane < NVL ? (lu * DV + lane * VEC) * ES : rv;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Piece<E>::pack(y)),
+                                               rsrc(static_cast<E*>(a.y) + b * UPB * DV, rv), ov, 0, 0);
+    };
+
+    // two register sets in turn (no copies between them); the loop body is two
+    // whole steps, the second of which may be a past-the-end batch
+    uint4 ra0[5], ra1[5];
+    load(blockIdx.x, ra0);
+    for (long b = blockIdx.x; b < nb; b += 2 * G) {
+        step(b, ra0, ra1);
+        step(b + G, ra1, ra0);
     }
 }
 
@@ -67,10 +209,21 @@ __global__ __launch_bounds__(256) void epilogue_kernel(EpilogueArgs a) {
 
 bool epilogue_supported(int dk, int dv) { return (dk == 96 && dv == 192) || (dk == 16 && dv == 32); }
 
+// Workgroups: about kEpiWgPerCu per compute unit (fewer for small inputs),
+// rounded up to a multiple of H.
+constexpr long kEpiWgPerCu = 8;
+static unsigned epi_grid(long nb, int H) {
+    const long want = nb < 256 * kEpiWgPerCu ? nb : 256 * kEpiWgPerCu;
+    return (unsigned)((want + H - 1) / H * H);
+}
+
 hipError_t launch_epilogue(bool bf16_io, int dk, int dv, const EpilogueArgs& a, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((a.units + 3) / 4);
-#define GLA_EPI(E_, DK_, DV_) \
-    hipLaunchKernelGGL((epilogue_kernel<E_, DK_, DV_>), dim3(blocks), dim3(256), 0, stream, a)
+#define GLA_EPI(E_, DK_, DV_)                                                                            \
+    do {                                                                                                 \
+        const long nb = (a.units + EpiShape<E_, DK_, DV_>::UPB - 1) / EpiShape<E_, DK_, DV_>::UPB;     \
+        hipLaunchKernelGGL((epilogue_kernel<E_, DK_, DV_>), dim3(epi_grid(nb, a.H)), dim3(kEpiThreads), 0, \
+                           stream, a);                                                                   \
+    } while (0)
     if (dk == 96 && dv == 192) {
         if (bf16_io) GLA_EPI(bf16, 96, 192);
         else GLA_EPI(float, 96, 192);

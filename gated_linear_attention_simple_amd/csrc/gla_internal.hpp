@@ -128,7 +128,8 @@ struct EpilogueArgs {
     const void* g;
     void* y;
     const float* aug_a;
-    const float* norm_w;
+    const float* norm_w;  // [n_tiers][dv]
+    int n_tiers;
     float eps;
     int tier[kEpiMaxHeads];
 };

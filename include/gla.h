@@ -182,7 +182,7 @@ typedef struct {
     const float* norm_w;     /* [n_tiers][dv] fp32 device, RMSNorm weight of each tier */
     const int* head_tier;    /* [H] int32 HOST array: the tier of head h, in [0, n_tiers);
                                 read during the call only */
-    int n_tiers;             /* >= 1 */
+    int n_tiers;             /* 1 .. 64 */
     float eps;               /* >= 0, finite; added to the mean square */
 } gla_epilogue_params;
 
@@ -193,7 +193,7 @@ typedef struct {
  *                                         is read before y's element is written)
  * M = B * T for a prefill (token rows), N for a decode batch.  H <= 64.
  * Supported (dk, dv): (96, 192), (16, 32).  One kernel launch, no workspace.
- * Errors: NULL ep, a NULL/misaligned tensor, n_tiers < 1, a head_tier entry
+ * Errors: NULL ep, a NULL/misaligned tensor, n_tiers outside [1, 64], a head_tier entry
  * out of range, a negative or non-finite eps, M < 0 -> GLA_ERR_INVALID_ARG;
  * H > 64 or another (dk, dv) -> GLA_ERR_UNSUPPORTED.  M == 0 enqueues nothing.
  */

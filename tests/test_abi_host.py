@@ -122,6 +122,7 @@ def test_mixer_epilogue_rejects_bad_arguments():
     assert e(tiers=[0] * 15 + [4]) == gla.GLA_ERR_INVALID_ARG      # tier out of range
     assert e(tiers=[-1] + [0] * 15) == gla.GLA_ERR_INVALID_ARG
     assert e(n_tiers=0, tiers=[0] * 16) == gla.GLA_ERR_INVALID_ARG
+    assert e(n_tiers=65, tiers=[0] * 16) == gla.GLA_ERR_INVALID_ARG
     assert e(eps=-1.0) == gla.GLA_ERR_INVALID_ARG
     assert e(eps=float("nan")) == gla.GLA_ERR_INVALID_ARG
     assert e(eps=float("inf")) == gla.GLA_ERR_INVALID_ARG

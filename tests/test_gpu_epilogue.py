@@ -99,6 +99,23 @@ def test_epilogue_in_place_and_empty():
     assert out.shape == (0, w.H, w.dv)
 
 
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 96, 192), ("bf16", 16, 32), ("f32", 16, 32)])
+@pytest.mark.parametrize("rows", [1, 37, 1000])
+def test_epilogue_writes_only_its_rows(dtype, dk, dv, rows):
+    """y is a view at the start of a larger buffer: the guard rows after it (more than
+    the workgroups' strided batches reach) keep their bits."""
+    w = _wl(dtype, dk, dv)
+    q, k, v, o = _rows(w, 40 + rows, (rows,))
+    e = gi.epilogue_inputs(w, DEV, 40 + rows, (rows,))
+    guard = 8192
+    big = torch.full((rows + guard, w.H, w.dv), 7.0, dtype=q.dtype, device=DEV)
+    _say(f"epilogue guard {dtype} dk={dk} dv={dv} rows={rows}")
+    y = gla.mixer_epilogue(q, k, v, o, e["g"], e["norm_w"], e["tier"], aug_a=e["aug_a"], y=big[:rows])
+    torch.cuda.synchronize()
+    assert_close(f64(y), _ref(q, k, v, o, e), dtype, "y")
+    assert bool((big[rows:] == 7.0).all()), "epilogue wrote past its rows"
+
+
 @pytest.mark.parametrize("dtype,chunk", [("bf16", 128), ("bf16", 64)])
 def test_forward_then_epilogue_full_layer(dtype, chunk):
     """The Laplace layer's prefill (B=1, T=2048, H=16, 96x192): the forward's output
