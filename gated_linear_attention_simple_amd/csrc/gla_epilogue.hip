@@ -209,11 +209,11 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
 
 bool epilogue_supported(int dk, int dv) { return (dk == 96 && dv == 192) || (dk == 16 && dv == 32); }
 
-// Workgroups: about kEpiWgPerCu per compute unit (fewer for small inputs),
-// rounded up to a multiple of H.
-constexpr long kEpiWgPerCu = 8;
+// Workgroups: about kEpiBatchesPerWg batches each (enough to amortise a
+// workgroup's set-up and first exposed load), rounded up to a multiple of H.
+constexpr long kEpiBatchesPerWg = 4;
 static unsigned epi_grid(long nb, int H) {
-    const long want = nb < 256 * kEpiWgPerCu ? nb : 256 * kEpiWgPerCu;
+    const long want = (nb + kEpiBatchesPerWg - 1) / kEpiBatchesPerWg;
     return (unsigned)((want + H - 1) / H * H);
 }
 
