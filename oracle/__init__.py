@@ -21,6 +21,10 @@ Parity status of each function (what pins it is in tests/test_oracle.py):
           sign * w of its tier, a one-hot value with a gate of sigmoid(ln 3)
           = 3/4 gives the 7/4 channel ratio, a = 0 gives the half skip,
           silu(ln 3) = (3/4) ln 3, a zero vector stays zero (eps > 0).
+  conv1d, conv1d_decode  pinned: fp64 torch grouped conv1d (the library's
+          cross-correlation with K-1 left padding, or the window prepended),
+          the impulse response w reversed through silu, decode steps == prefill,
+          split/resume through the window, the window carry itself.
 """
 from __future__ import annotations
 
@@ -64,8 +68,10 @@ def _bind(lib):
                                       ctypes.c_double, _D, i]
     lib.gla_oracle_epilogue.argtypes = [i, i, i, i, _D, _D, _D, _D, _D, _D, _D,
                                         ctypes.POINTER(ctypes.c_int), i, ctypes.c_double, _D, i]
+    lib.gla_oracle_conv1d.argtypes = [i, i, i, i, _D, _D, _D, _D, _D, _D, i]
+    lib.gla_oracle_conv1d_decode.argtypes = [i, i, i, _D, _D, _D, _D, _D, i]
     for f in (lib.gla_oracle_fwd, lib.gla_oracle_bwd, lib.gla_oracle_decode,
-              lib.gla_oracle_epilogue):
+              lib.gla_oracle_epilogue, lib.gla_oracle_conv1d, lib.gla_oracle_conv1d_decode):
         f.restype = ctypes.c_int
     lib.gla_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -183,6 +189,35 @@ def epilogue(q, k, v, o, g, a, w, tier, eps=1e-6, nthreads=0, _lib_=None):
     return y
 
 
+def conv1d(x, w, bias=None, win=None, nthreads=0, _lib_=None):
+    """Depth-wise causal conv + SiLU: x [B, T, D], w [D, K], bias [D] or None,
+    win [B, K, D] or None (zeros) -> (y [B, T, D], window after the last token [B, K, D])."""
+    x, w, bias, win = map(_f64, (x, w, bias, win))
+    B, T, D = x.shape
+    K = w.shape[1]
+    y = np.zeros((B, T, D))
+    wo = np.zeros((B, K, D))
+    rc = (_lib_ or _load()).gla_oracle_conv1d(B, T, D, K, _p(x), _p(w), _p(bias), _p(win), _p(y), _p(wo),
+                                              int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_conv1d failed")
+    return y, wo
+
+
+def conv1d_decode(x, w, bias, win, nthreads=0, _lib_=None):
+    """One token per sequence: x [N, D], win [N, K, D] -> (y [N, D], new window)."""
+    x, w, bias = map(_f64, (x, w, bias))
+    win = np.array(win, dtype=np.float64, copy=True, order="C")
+    N, D = x.shape
+    K = w.shape[1]
+    y = np.zeros((N, D))
+    rc = (_lib_ or _load()).gla_oracle_conv1d_decode(N, D, K, _p(x), _p(w), _p(bias), _p(win), _p(y),
+                                                     int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gla_oracle_conv1d_decode failed")
+    return y, win
+
+
 class _Variant:
     def __init__(self, lib):
         self.lib = lib
@@ -198,3 +233,9 @@ class _Variant:
 
     def epilogue(self, *a, **kw):
         return epilogue(*a, _lib_=self.lib, **kw)
+
+    def conv1d(self, *a, **kw):
+        return conv1d(*a, _lib_=self.lib, **kw)
+
+    def conv1d_decode(self, *a, **kw):
+        return conv1d_decode(*a, _lib_=self.lib, **kw)

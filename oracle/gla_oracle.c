@@ -28,6 +28,11 @@
  *     skip); each head's output then goes through the RMSNorm of its decay
  *     tier, the heads are concatenated and gated by SiLU(g).  The equation
  *     image is missing; the readings are written at the function.
+ *   - Same section, paragraph "Normalization and convolution", and the
+ *     parameter table row "Conv" (gla_oracle_conv1d, gla_oracle_conv1d_decode):
+ *     before the mixer each channel of the residual stream goes through a
+ *     depth-wise causal convolution of width 4 followed by SiLU, a summary of
+ *     the last 4 tokens.  Readings at the functions.
  *
  * Everything is the plain per-token recurrence: no chunking, no blocking, no
  * reassociation.  The reverse-mode routine is the textbook adjoint of that
@@ -41,6 +46,7 @@
  *   decode: q, k [N][H][dk], v, o [N][H][dv], S [N][H][dk][dv]
  *   epilogue: q, k [M][H][dk], v, o, g, y [M][H][dv] (M = rows, e.g. B*T),
  *             a [H][dk], w [n_tiers][dv], tier [H]
+ *   conv: x, y [B][T][D] (decode: [N][D]), w [D][K], bias [D], window [B][K][D]
  */
 #include <math.h>
 #include <stdlib.h>
@@ -292,6 +298,65 @@ int gla_oracle_epilogue(int M, int H, int dk, int dv, const double* q, const dou
             y[(size_t)u * dv + c] = gc * sigmoid(gc) * x[c] * inv * wt[c];
         }
         free(x);
+    }
+    return 0;
+}
+
+/*
+ * Depth-wise causal convolution of width K with SiLU, per channel d:
+ *   u_t[d] = bias[d] + sum_{j=0..K-1} w[d][j] * x_{t-(K-1)+j}[d],   y_t[d] = silu(u_t[d])
+ * so w[d][K-1] weighs the current token (the cross-correlation of a Conv1d with
+ * K-1 zeros of left padding).  Readings of what the page leaves open:
+ *   - bias == NULL means no bias;
+ *   - inputs before the first token come from a window of the K most recent
+ *     earlier inputs, win_in[b][s][d] = x_{s-K}[d] (oldest first); win_in ==
+ *     NULL means zeros (a fresh sequence);
+ *   - win_out (if not NULL) receives the window after the last token,
+ *     x_{T-K..T-1}, the carry a decode step or the next prefill continues from.
+ * win_out may alias win_in (every window value is read before any is written).
+ */
+static double x_at(const double* x, const double* win_in, int b, int t, int d, int T, int D, int K) {
+    if (t >= 0) return x[((size_t)b * T + t) * D + d];
+    return win_in ? win_in[((size_t)b * K + (K + t)) * D + d] : 0.0;
+}
+
+int gla_oracle_conv1d(int B, int T, int D, int K, const double* x, const double* w, const double* bias,
+                      const double* win_in, double* y, double* win_out, int nthreads) {
+    if (B < 0 || T < 0 || D < 1 || K < 1 || K > 64) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (long bd = 0; bd < (long)B * D; ++bd) {
+        const int b = (int)(bd / D), d = (int)(bd % D);
+        double carry[64];  /* the window of this channel, read before anything is written */
+        for (int s2 = 0; s2 < K; ++s2) carry[s2] = x_at(x, win_in, b, T - K + s2, d, T, D, K);
+        for (int t = 0; t < T; ++t) {
+            double u = bias ? bias[d] : 0.0;
+            for (int j = 0; j < K; ++j) u += w[(size_t)d * K + j] * x_at(x, win_in, b, t - (K - 1) + j, d, T, D, K);
+            y[((size_t)b * T + t) * D + d] = u * sigmoid(u);
+        }
+        if (win_out)
+            for (int s2 = 0; s2 < K; ++s2) win_out[((size_t)b * K + s2) * D + d] = carry[s2];
+    }
+    return 0;
+}
+
+/*
+ * One decode token per sequence: the window [N][K][D] drops its oldest input
+ * and appends x_n, then y_n = silu(bias + sum_j w[d][j] * window[j]).
+ */
+int gla_oracle_conv1d_decode(int N, int D, int K, const double* x, const double* w, const double* bias,
+                             double* win, double* y, int nthreads) {
+    if (N < 0 || D < 1 || K < 1) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (long nd = 0; nd < (long)N * D; ++nd) {
+        const int n = (int)(nd / D), d = (int)(nd % D);
+        double* wn = win + (size_t)n * K * D + d;
+        for (int s2 = 0; s2 + 1 < K; ++s2) wn[(size_t)s2 * D] = wn[(size_t)(s2 + 1) * D];
+        wn[(size_t)(K - 1) * D] = x[(size_t)n * D + d];
+        double u = bias ? bias[d] : 0.0;
+        for (int j = 0; j < K; ++j) u += w[(size_t)d * K + j] * wn[(size_t)j * D];
+        y[(size_t)n * D + d] = u * sigmoid(u);
     }
     return 0;
 }

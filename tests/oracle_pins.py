@@ -376,3 +376,100 @@ ALL_PINS.update({
     "epilogue_gate_ratio": pin_epilogue_gate_ratio,
     "epilogue_zero_and_scale": pin_epilogue_zero_and_scale,
 })
+
+
+# ---------------------------------------------------------------- conv1d
+
+
+def _conv_case(B=2, T=11, D=5, K=4, seed=RNG_SEED + 11):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(B, T, D)), rng.normal(size=(D, K)), rng.normal(size=D),
+            rng.normal(size=(B, K, D)))
+
+
+def _silu(u):
+    return u / (1.0 + np.exp(-u))
+
+
+def pin_conv_torch(orc, tol=1e-12):
+    """fp64 torch grouped conv1d (cross-correlation; K-1 zeros of left padding for a
+    fresh sequence, the window's last K-1 inputs prepended otherwise), then SiLU."""
+    import torch
+    x, w, b, win = _conv_case()
+    B, T, D = x.shape
+    K = w.shape[1]
+    wt = torch.from_numpy(w).reshape(D, 1, K)
+    bt = torch.from_numpy(b)
+    xt = torch.from_numpy(x).transpose(1, 2)                     # [B, D, T]
+    fresh = torch.nn.functional.conv1d(torch.nn.functional.pad(xt, (K - 1, 0)), wt, bt, groups=D)
+    ctx = torch.cat([torch.from_numpy(win[:, 1:, :]).transpose(1, 2), xt], dim=2)
+    carried = torch.nn.functional.conv1d(ctx, wt, bt, groups=D)
+    y0, _ = orc.conv1d(x, w, b)
+    y1, _ = orc.conv1d(x, w, b, win)
+    ok0 = rel(y0, _silu(fresh.transpose(1, 2).numpy())) < tol
+    ok1 = rel(y1, _silu(carried.transpose(1, 2).numpy())) < tol
+    return bool(ok0 and ok1)
+
+
+def pin_conv_impulse(orc, tol=1e-14):
+    """A unit impulse at token t0 of channel d, no bias: u_{t0+m}[d] = w[d][K-1-m]
+    for m < K and 0 elsewhere, other channels stay 0."""
+    x, w, _, _ = _conv_case(B=1, T=12, D=3)
+    K = w.shape[1]
+    t0, d = 5, 1
+    x = np.zeros_like(x)
+    x[0, t0, d] = 1.0
+    y, _ = orc.conv1d(x, w, None)
+    want = np.zeros_like(y)
+    for m in range(K):
+        want[0, t0 + m, d] = _silu(w[d, K - 1 - m])
+    return bool(np.abs(y - want).max() < tol)
+
+
+def pin_conv_decode_equals_prefill(orc, tol=1e-12):
+    """T decode steps from a window equal one prefill over the same T tokens, and
+    both leave the same window."""
+    x, w, b, win = _conv_case()
+    y, wo = orc.conv1d(x, w, b, win)
+    cur = win.copy()
+    ys = []
+    for t in range(x.shape[1]):
+        yt, cur = orc.conv1d_decode(x[:, t], w, b, cur)
+        ys.append(yt)
+    return bool(rel(np.stack(ys, 1), y) < tol and rel(cur, wo) < tol)
+
+
+def pin_conv_split_resume(orc, tol=0.0):
+    """Prefill of tokens [0, T1) then [T1, T) through the window equals one prefill
+    (exactly: the same products in the same order), for T1 below and above K."""
+    x, w, b, win = _conv_case(T=13)
+    y, wo = orc.conv1d(x, w, b, win)
+    ok = True
+    for t1 in (2, 7):
+        ya, wa = orc.conv1d(x[:, :t1], w, b, win)
+        yb, wb = orc.conv1d(x[:, t1:], w, b, wa)
+        ok &= rel(np.concatenate([ya, yb], 1), y) <= tol and rel(wb, wo) <= tol
+    return bool(ok)
+
+
+def pin_conv_window_carry(orc, tol=0.0):
+    """The window after a prefill is the last K inputs, oldest first; with T < K its
+    head is the end of the previous window; T = 0 returns the window unchanged."""
+    x, w, b, win = _conv_case(T=9)
+    K = w.shape[1]
+    _, wo = orc.conv1d(x, w, b, win)
+    _, w2 = orc.conv1d(x[:, :2], w, b, win)
+    _, w0 = orc.conv1d(x[:, :0], w, b, win)
+    ok = np.array_equal(wo, x[:, -K:, :])
+    ok &= np.array_equal(w2, np.concatenate([win[:, 2:, :], x[:, :2, :]], 1))
+    ok &= np.array_equal(w0, win)
+    return bool(ok)
+
+
+ALL_PINS.update({
+    "conv_torch": pin_conv_torch,
+    "conv_impulse": pin_conv_impulse,
+    "conv_decode_equals_prefill": pin_conv_decode_equals_prefill,
+    "conv_split_resume": pin_conv_split_resume,
+    "conv_window_carry": pin_conv_window_carry,
+})

@@ -141,6 +141,19 @@ MUTANTS = [
     ("epi_silu_is_identity", "y[(size_t)u * dv + c] = gc * sigmoid(gc) * x[c] * inv * wt[c];",
      "y[(size_t)u * dv + c] = gc * x[c] * inv * wt[c];"),
     ("epi_wrong_tier", "const double* wt = w + (size_t)tier[h] * dv;", "const double* wt = w;"),
+    ("conv_taps_reversed", "u += w[(size_t)d * K + j] * x_at(x, win_in, b, t - (K - 1) + j, d, T, D, K);",
+     "u += w[(size_t)d * K + j] * x_at(x, win_in, b, t - j, d, T, D, K);"),
+    ("conv_excludes_current", "u += w[(size_t)d * K + j] * x_at(x, win_in, b, t - (K - 1) + j, d, T, D, K);",
+     "u += w[(size_t)d * K + j] * x_at(x, win_in, b, t - K + j, d, T, D, K);"),
+    ("conv_no_silu", "y[((size_t)b * T + t) * D + d] = u * sigmoid(u);", "y[((size_t)b * T + t) * D + d] = u;"),
+    ("conv_bias_dropped", "            double u = bias ? bias[d] : 0.0;", "            double u = 0.0;"),
+    ("conv_decode_bias_dropped", "double u = bias ? bias[d] : 0.0;\n        for (int j = 0; j < K; ++j) u += w[(size_t)d * K + j] * wn",
+     "double u = 0.0;\n        for (int j = 0; j < K; ++j) u += w[(size_t)d * K + j] * wn"),
+    ("conv_window_newest_first", "return win_in ? win_in[((size_t)b * K + (K + t)) * D + d] : 0.0;",
+     "return win_in ? win_in[((size_t)b * K + (-1 - t)) * D + d] : 0.0;"),
+    ("conv_decode_no_shift", "for (int s2 = 0; s2 + 1 < K; ++s2) wn[(size_t)s2 * D] = wn[(size_t)(s2 + 1) * D];", ""),
+    ("conv_decode_channel_slip", "u += w[(size_t)d * K + j] * wn[(size_t)j * D];",
+     "u += w[(size_t)((d + 1) % D) * K + j] * wn[(size_t)j * D];"),
 ]
 
 CHEAP_PINS = [n for n in P.ALL_PINS if n != "autograd_quadratic"]
