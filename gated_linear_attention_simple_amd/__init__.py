@@ -29,6 +29,8 @@ SYMBOLS = (
     "gla_decode_step_pool",
     "gla_mixer_epilogue",
     "gla_decode_step_epilogue",
+    "gla_conv1d_silu",
+    "gla_conv1d_silu_decode",
 )
 
 _lib = None
@@ -75,6 +77,10 @@ def load():
         lib.gla_mixer_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, ep, vp, vp]
         lib.gla_decode_step_epilogue.restype = i
         lib.gla_decode_step_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, vp, i, vp, f, ep, vp, vp]
+        lib.gla_conv1d_silu.restype = i
+        lib.gla_conv1d_silu.argtypes = [i] * 5 + [vp] * 7
+        lib.gla_conv1d_silu_decode.restype = i
+        lib.gla_conv1d_silu_decode.argtypes = [i] * 4 + [vp, vp, vp, vp, i, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -297,4 +303,61 @@ def decode_step_epilogue(q, k, v, g, lam, S, norm_w, head_tier, aug_a=None, eps=
                                       _stream(stream))
     if st != GLA_OK:
         raise GlaError(st, "gla_decode_step_epilogue")
+    return y
+
+
+def conv1d_silu(x, w, bias=None, win_in=None, win_out=True, y=None, stream=None):
+    """Depth-wise causal conv (width 4) + SiLU: x [B, T, D]; w [D, 4] fp32; bias [D] or None;
+    win_in [B, 4, D] fp32 or None (zeros).  Returns (y, win_out): win_out=True allocates the
+    window after the last token, False skips it, a tensor (win_in itself allowed) is written."""
+    lib = load()
+    B, T, D = x.shape
+    K = w.shape[1]
+    dev = x.device
+    _check(x, "x", (B, T, D), x.dtype, dev)
+    _check(w, "w", (D, K), torch.float32, dev)
+    if bias is not None:
+        _check(bias, "bias", (D,), torch.float32, dev)
+    if win_in is not None:
+        _check(win_in, "win_in", (B, K, D), torch.float32, dev)
+    if win_out is True:
+        win_out = torch.empty((B, K, D), dtype=torch.float32, device=dev)
+    elif win_out is False:
+        win_out = None
+    if win_out is not None:
+        _check(win_out, "win_out", (B, K, D), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (B, T, D), x.dtype, dev)
+    st = lib.gla_conv1d_silu(_dt(x), B, T, D, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(win_in), _ptr(y),
+                             _ptr(win_out), _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_conv1d_silu")
+    return y, win_out
+
+
+def conv1d_silu_decode(x, w, bias, win, slots=None, y=None, stream=None):
+    """One token per row: x [N, D]; win [N, 4, D] fp32 (or a pool [P, 4, D] indexed by
+    int32 `slots`), updated in place.  Returns y [N, D]."""
+    lib = load()
+    N, D = x.shape
+    K = w.shape[1]
+    dev = x.device
+    _check(x, "x", (N, D), x.dtype, dev)
+    _check(w, "w", (D, K), torch.float32, dev)
+    if bias is not None:
+        _check(bias, "bias", (D,), torch.float32, dev)
+    P = win.shape[0]
+    if slots is None:
+        _check(win, "win", (N, K, D), torch.float32, dev)
+    else:
+        _check(win, "win", (P, K, D), torch.float32, dev)
+        _check(slots, "slots", (N,), torch.int32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", (N, D), x.dtype, dev)
+    st = lib.gla_conv1d_silu_decode(_dt(x), N, D, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(win), P, _ptr(slots),
+                                    _ptr(y), _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_conv1d_silu_decode")
     return y

@@ -199,4 +199,52 @@ int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv, const void
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 
+int gla_conv1d_silu(int dtype, int B, int T, int D, int K, const void* x, const float* w, const float* bias,
+                    const float* win_in, void* y, float* win_out, void* stream) {
+    if (!ok_dtype(dtype) || B < 0 || T < 0 || D < 1 || K < 1) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(B, T, D, 1) || !sane_count(B, K, D, 1)) return GLA_ERR_INVALID_ARG;
+    if (!gla::conv_supported(D, K)) return GLA_ERR_UNSUPPORTED;
+    if (T > 65535L * 32 || B > 65535) return GLA_ERR_UNSUPPORTED;
+    if (B == 0 || (T == 0 && win_out == nullptr)) return GLA_OK;
+    if (!ok_ptr(w) || !ok_opt(bias) || !ok_opt(win_in) || !ok_opt(win_out)) return GLA_ERR_INVALID_ARG;
+    if (T > 0 && (!ok_ptr(x) || !ok_ptr(y))) return GLA_ERR_INVALID_ARG;
+    gla::ConvArgs a{};
+    a.B = B;
+    a.T = T;
+    a.D = D;
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.win_in = win_in;
+    a.y = y;
+    a.win_out = win_out;
+    const hipError_t err = gla::launch_conv_prefill(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_conv1d_silu_decode(int dtype, int N, int D, int K, const void* x, const float* w, const float* bias,
+                           float* win, int P, const int* slots, void* y, void* stream) {
+    if (!ok_dtype(dtype) || N < 0 || D < 1 || K < 1) return GLA_ERR_INVALID_ARG;
+    if (slots != nullptr && P < 0) return GLA_ERR_INVALID_ARG;
+    if (!sane_count(N, K, D, 1) || (slots != nullptr && !sane_count(P, K, D, 1))) return GLA_ERR_INVALID_ARG;
+    if (!gla::conv_supported(D, K)) return GLA_ERR_UNSUPPORTED;
+    if (N > 65535) return GLA_ERR_UNSUPPORTED;
+    if (N == 0) return GLA_OK;
+    if (!ok_ptr(x) || !ok_ptr(y) || !ok_ptr(w) || !ok_opt(bias) || !ok_opt(slots)) return GLA_ERR_INVALID_ARG;
+    if ((slots == nullptr || P > 0) && !ok_ptr(win)) return GLA_ERR_INVALID_ARG;
+    gla::ConvArgs a{};
+    a.B = N;
+    a.T = 1;
+    a.D = D;
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.y = y;
+    a.win_out = win;
+    a.slots = slots;
+    a.P = slots ? P : 0;
+    const hipError_t err = gla::launch_conv_decode(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
 }  // extern "C"

@@ -137,6 +137,26 @@ struct EpilogueArgs {
 bool epilogue_supported(int dk, int dv);
 hipError_t launch_epilogue(bool bf16_io, int dk, int dv, const EpilogueArgs& a, hipStream_t stream);
 
+// Depth-wise causal conv + SiLU (width 4).  Prefill: x, y [B][T][D], windows
+// [B][4][D] fp32 (win_in nullable).  Decode: x, y [N = B][D], win_out is the
+// in/out window [N or P][4][D]; slots nullable (row n -> window slots[n]).
+struct ConvArgs {
+    int B;
+    long T;
+    int D;
+    const void* x;
+    const float* w;       // [D][4]
+    const float* bias;    // [D] or nullptr
+    const float* win_in;
+    void* y;
+    float* win_out;
+    const int* slots;
+    int P;
+};
+bool conv_supported(int D, int K);
+hipError_t launch_conv_prefill(bool bf16_io, const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_decode(bool bf16_io, const ConvArgs& a, hipStream_t stream);
+
 // slots == nullptr: row n uses page n of S; else page slots[n] of a P-page pool.
 // epi == nullptr: o is the readout; else o receives the epilogue output y
 // (epi->g the gate; q, k, v, o, y fields of epi unused).

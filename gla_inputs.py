@@ -17,7 +17,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-_TID = {"q": 0, "k": 1, "v": 2, "do": 3, "S0": 4, "state": 5, "dS": 6, "g": 7, "aug": 8, "normw": 9}
+_TID = {"q": 0, "k": 1, "v": 2, "do": 3, "S0": 4, "state": 5, "dS": 6, "g": 7, "aug": 8, "normw": 9,
+        "cx": 10, "cw": 11, "cb": 12, "cwin": 13}
 
 
 def laplace_lambdas(H: int = 16):
@@ -160,4 +161,17 @@ def epilogue_inputs(w: Workload, device, seed: int, lead, n_tiers=4, aug_var=Non
         "aug_a": normal((w.H, w.dk), av, torch.float32, device, seed, "aug"),
         "norm_w": normal((n_tiers, w.dv), 0.1, torch.float32, device, seed, "normw") + 1.0,
         "tier": contiguous_tiers(w.H, n_tiers),
+    }
+
+
+def conv_inputs(B: int, T: int, D: int, dtype: str, device, seed: int, K: int = 4, layer=0, step=0):
+    """Depth-wise conv inputs: x [B, T, D] ~ N(0, 1) in `dtype`; fp32 taps w [D, K] ~ N(0, 1/K),
+    bias [D] ~ N(0, 0.01), and a carried window [B, K, D] of earlier inputs (N(0, 1) rounded
+    to `dtype`, as a window of that dtype's inputs holds)."""
+    dt = torch_dtype(dtype)
+    return {
+        "x": normal((B, T, D), 1.0, dt, device, seed, "cx", layer, step),
+        "w": normal((D, K), 1.0 / K, torch.float32, device, seed, "cw"),
+        "bias": normal((D,), 0.01, torch.float32, device, seed, "cb"),
+        "win": normal((B, K, D), 1.0, dt, device, seed, "cwin", layer).float(),
     }

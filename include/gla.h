@@ -218,6 +218,42 @@ int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv,
                              float scale, const gla_epilogue_params* ep, void* y,
                              void* stream);
 
+/*
+ * Depth-wise causal convolution of width K = 4 with SiLU, the step before the
+ * mixer (Laplace 3B post, section "i14 and the Laplace 3B architecture",
+ * paragraph "Normalization and convolution"; the "Conv" row of the parameter
+ * table).  Every channel d is filtered on its own:
+ *       u_t[d] = bias[d] + sum_{j<K} w[d][j] * x_{t-(K-1)+j}[d],    y_t[d] = silu(u_t[d])
+ * (w[d][K-1] weighs the current token), with inputs before the first token
+ * taken from a per-sequence window of the K most recent earlier inputs.
+ *   x, y      [B][T][D] (dtype)
+ *   w         [D][K] fp32;   bias  [D] fp32 or NULL (no bias)
+ *   win_in    [B][K][D] fp32: win_in[b][s] = x_{s-K} (oldest first); NULL = zeros
+ *   win_out   [B][K][D] fp32 or NULL: the window after the last token,
+ *             x_{T-K..T-1} (the decode carry); may alias win_in (in place)
+ * Supported: K == 4, D a multiple of 8 (D <= 2^20).  T == 0 passes the window
+ * through.  One kernel launch, no workspace.
+ * Errors: a NULL/misaligned required pointer, negative sizes -> GLA_ERR_INVALID_ARG;
+ * another K or D -> GLA_ERR_UNSUPPORTED.
+ */
+int gla_conv1d_silu(int dtype, int B, int T, int D, int K,
+                    const void* x, const float* w, const float* bias,
+                    const float* win_in, void* y, float* win_out, void* stream);
+
+/*
+ * One decode token per sequence through the same convolution: the window of
+ * row n drops its oldest input and appends x[n], then y[n] = silu(bias + w . window).
+ *   x, y   [N][D] (dtype)
+ *   win    fp32, updated in place: [N][K][D] (slots == NULL), or a pool of P
+ *          windows [P][K][D] with row n using window slots[n] (device int32 [N]);
+ *          a slot outside [0, P) is a padding row: zero output, no window touched.
+ * Each row is computed on its own (bit-identical whatever batch it is in).
+ * Errors and support: as gla_conv1d_silu; P < 0 with slots -> GLA_ERR_INVALID_ARG.
+ */
+int gla_conv1d_silu_decode(int dtype, int N, int D, int K,
+                           const void* x, const float* w, const float* bias,
+                           float* win, int P, const int* slots, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

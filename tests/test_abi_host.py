@@ -158,6 +158,36 @@ def test_decode_epilogue_rejects_bad_arguments():
     assert d(N=0, g=None) == gla.GLA_OK
 
 
+def test_conv_rejects_bad_arguments():
+    lib = gla.load()
+
+    def c(dtype=1, B=2, T=10, D=3072, K=4, x=P, w=P, bias=None, wi=None, y=P, wo=None):
+        return lib.gla_conv1d_silu(dtype, B, T, D, K, x, w, bias, wi, y, wo, None)
+
+    assert c(dtype=4) == gla.GLA_ERR_INVALID_ARG
+    assert c(B=-1) == gla.GLA_ERR_INVALID_ARG
+    assert c(T=-2) == gla.GLA_ERR_INVALID_ARG
+    assert c(K=3) == gla.GLA_ERR_UNSUPPORTED
+    assert c(D=3070) == gla.GLA_ERR_UNSUPPORTED
+    assert c(w=None) == gla.GLA_ERR_INVALID_ARG
+    assert c(x=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert c(bias=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert c(wo=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert c(B=0, x=None) == gla.GLA_OK
+    assert c(T=0, x=None, y=None) == gla.GLA_OK          # nothing to write
+
+    def d(dtype=1, N=3, D=3072, K=4, x=P, w=P, win=P, Pn=0, slots=None, y=P):
+        return lib.gla_conv1d_silu_decode(dtype, N, D, K, x, w, None, win, Pn, slots, y, None)
+
+    assert d(N=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(K=5) == gla.GLA_ERR_UNSUPPORTED
+    assert d(win=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(slots=P, Pn=-1) == gla.GLA_ERR_INVALID_ARG
+    assert d(slots=MIS, Pn=4) == gla.GLA_ERR_INVALID_ARG
+    assert d(y=None) == gla.GLA_ERR_INVALID_ARG
+    assert d(N=0, x=None) == gla.GLA_OK
+
+
 def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,
         dq=P, dk_=P, dv_=P, dl=None, dS0=None, ws=None, wsb=0):
     return gla.load().gla_bwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, do, dST, dq, dk_, dv_,
