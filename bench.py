@@ -63,6 +63,11 @@ DEC_FLOPS_PER_SEQ_HEAD = 4 * 96 * 192
 EPI_BYTES_PER_TOKEN_HEAD = 2 * (2 * 96 + 4 * 192)
 # Decode with the epilogue fused: the decode step's bytes plus the gate g (y replaces o)
 DEC_EPI_BYTES_PER_SEQ_HEAD = DEC_BYTES_PER_SEQ_HEAD + 2 * 192
+# Depth-wise conv (width 4), per channel: prefill x in + y out (bf16) per token; decode
+# x in + y out (bf16) + 3 fp32 window slots read + 4 written per row
+CONV_BYTES_PER_TOKEN_CHANNEL = 2 + 2
+CONV_DEC_BYTES_PER_ROW_CHANNEL = 2 + 2 + 4 * 3 + 4 * 4
+CONV_D = 3072
 
 
 def src_digest():
@@ -208,6 +213,38 @@ class EpilogueLeg:
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError(f"gla_mixer_epilogue: {self.gla.status_str(st)}")
+
+
+class ConvLeg:
+    """Pre-marshalled depth-wise conv prefill (B, T, D=3,072 bf16) or decode step (N rows)."""
+
+    def __init__(self, gla, gi, torch, B, T, seed, decode=False):
+        dev = torch.device("cuda:0")
+        c = gi.conv_inputs(B, T, CONV_D, "bf16", dev, seed)
+        self.keep = c
+        self.stream = torch.cuda.current_stream()
+        st = ctypes.c_void_p(self.stream.cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        lib = gla.load()
+        if decode:
+            self.y = torch.empty((B, CONV_D), dtype=torch.bfloat16, device=dev)
+            self.fn = lib.gla_conv1d_silu_decode
+            self.args = (gla.GLA_BF16, B, CONV_D, 4, p(c["x"][:, 0]), p(c["w"]), p(c["bias"]), p(c["win"]), 0,
+                         None, p(self.y), st)
+            self.bytes = CONV_DEC_BYTES_PER_ROW_CHANNEL * B * CONV_D
+        else:
+            self.y = torch.empty_like(c["x"])
+            self.wo = torch.empty_like(c["win"])
+            self.fn = lib.gla_conv1d_silu
+            self.args = (gla.GLA_BF16, B, T, CONV_D, 4, p(c["x"]), p(c["w"]), p(c["bias"]), p(c["win"]), p(self.y),
+                         p(self.wo), st)
+            self.bytes = CONV_BYTES_PER_TOKEN_CHANNEL * B * T * CONV_D
+        self.gla = gla
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"conv: {self.gla.status_str(st)}")
 
 
 class DecodeLeg:
@@ -518,6 +555,20 @@ def main():
         del dleg
         torch.cuda.empty_cache()
     result["ms_per_step"] = f_ms + t_ms + d_ms
+
+    # ---- depth-wise conv (not part of the step): training-width prefill, decode rows of one layer
+    result["conv"] = {}
+    for name, B, T, dec in (("prefill", w2.B, w2.T, False), ("decode", ws[4].B, 1, True)):
+        cleg = ConvLeg(gla, gi, torch, B, T, 11, decode=dec)
+        c_wall, c_gpu = time_region(torch, cleg.stream, cleg, K, W)
+        c_avg = c_gpu / K
+        result["conv"][name] = {
+            "kernel": "gla_conv1d_silu_decode" if dec else "gla_conv1d_silu",
+            "workload": f"{'N' if dec else 'B'}={B}" + ("" if dec else f" T={T}") + f" D={CONV_D} bf16, width 4",
+            "avg_launch_us": c_avg * 1e6, "alg_bytes_per_launch": cleg.bytes,
+            "achieved": cleg.bytes / c_avg / 1e9, "unit": "GB/s", "frac": cleg.bytes / c_avg / 1e9 / HBM_PEAK_GBS}
+        del cleg
+        torch.cuda.empty_cache()
 
     # ---- mixer epilogue pass (not part of the step): the layer's prefill rows and the training width
     result["epilogue"] = {}

@@ -22,7 +22,7 @@ namespace {
 constexpr int kConvK = 4;
 constexpr int kConvThreads = 128;
 constexpr int kConvRun = 32;     // tokens per thread in the prefill
-constexpr int kConvGroup = 8;    // tokens whose loads are issued together
+constexpr int kConvGroup = 16;   // tokens whose loads are issued together
 
 template <typename E> struct CPiece;
 template <> struct CPiece<bf16> {
