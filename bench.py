@@ -215,6 +215,36 @@ class EpilogueLeg:
             raise RuntimeError(f"gla_mixer_epilogue: {self.gla.status_str(st)}")
 
 
+class FwdEpilogueLeg:
+    """Pre-marshalled gla_fwd_chunked_epilogue on the Laplace layer (the epilogue fused into
+    the forward's output kernel there)."""
+
+    def __init__(self, gla, gi, torch, w, seed, chunk):
+        dev = torch.device("cuda:0")
+        x = gi.fwd_inputs(w, dev, seed)
+        e = gi.epilogue_inputs(w, dev, seed, (w.B, w.T))
+        self.keep = (x, e)
+        B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+        self.token_heads = B * T * H
+        self.y = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        self.S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        need = gla.fwd_workspace_bytes(gla.GLA_BF16, B, T, H, dk, dv, chunk)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.params, self.tiers = epi_params(gla, e)
+        self.stream = torch.cuda.current_stream()
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.args = (gla.GLA_BF16, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None,
+                     ctypes.c_float(x["scale"]), p(e["g"]), ctypes.byref(self.params), p(self.y), p(self.S),
+                     p(self.ws), ctypes.c_size_t(need), ctypes.c_void_p(self.stream.cuda_stream))
+        self.fn = gla.load().gla_fwd_chunked_epilogue
+        self.gla = gla
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"gla_fwd_chunked_epilogue: {self.gla.status_str(st)}")
+
+
 class ConvLeg:
     """Pre-marshalled depth-wise conv prefill (B, T, D=3,072 bf16) or decode step (N rows)."""
 
@@ -583,6 +613,18 @@ def main():
             "frac": eb / e_avg / 1e9 / HBM_PEAK_GBS}
         del eleg
         torch.cuda.empty_cache()
+    # the forward with the epilogue in its output kernel, Laplace layer
+    fe = FwdEpilogueLeg(gla, gi, torch, w1, 1, args.chunk)
+    fe_wall, fe_gpu = time_region(torch, fe.stream, fe, K, W)
+    fe_avg = fe_gpu / K
+    fe_bytes = (FWD_BYTES_PER_TOKEN_HEAD["bf16"] + 2 * 192) * fe.token_heads   # + the gate g
+    result["epilogue"]["fwd_fused_layer"] = {
+        "kernel": "gla_fwd_chunked_epilogue (chain + output kernel with the epilogue in its store)",
+        "avg_call_us": fe_avg * 1e6, "tokens_per_s": K * w1.B * w1.T / fe_wall,
+        "alg_bytes_per_call": fe_bytes, "achieved": fe_bytes / fe_avg / 1e9, "unit": "GB/s",
+        "frac": fe_bytes / fe_avg / 1e9 / HBM_PEAK_GBS}
+    del fe
+    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline_fwd(gi, w1, 1)

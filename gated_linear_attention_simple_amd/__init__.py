@@ -28,6 +28,7 @@ SYMBOLS = (
     "gla_decode_step",
     "gla_decode_step_pool",
     "gla_mixer_epilogue",
+    "gla_fwd_chunked_epilogue",
     "gla_decode_step_epilogue",
     "gla_conv1d_silu",
     "gla_conv1d_silu_decode",
@@ -75,6 +76,8 @@ def load():
         ep = ctypes.POINTER(EpilogueParams)
         lib.gla_mixer_epilogue.restype = i
         lib.gla_mixer_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, ep, vp, vp]
+        lib.gla_fwd_chunked_epilogue.restype = i
+        lib.gla_fwd_chunked_epilogue.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, ep, vp, vp, vp, sz, vp]
         lib.gla_decode_step_epilogue.restype = i
         lib.gla_decode_step_epilogue.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, vp, i, vp, f, ep, vp, vp]
         lib.gla_conv1d_silu.restype = i
@@ -361,3 +364,40 @@ def conv1d_silu_decode(x, w, bias, win, slots=None, y=None, stream=None):
     if st != GLA_OK:
         raise GlaError(st, "gla_conv1d_silu_decode")
     return y
+
+
+def fwd_chunked_epilogue(q, k, v, lam, g, norm_w, head_tier, aug_a=None, eps=1e-6, S0=None, scale=1.0,
+                         chunk=128, y=None, S_final=True, workspace=None, stream=None):
+    """y, S_final: the forward followed by the mixer epilogue (y in place of o)."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(g, "g", (B, T, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(y, "y", (B, T, H, dv), q.dtype, dev)
+    if S_final is True:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_final is False:
+        S_final = None
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    dt = _dt(q)
+    need = lib.gla_fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p, _keep = _epi_params(H, dk, dv, aug_a, norm_w, head_tier, eps, dev)
+    st = lib.gla_fwd_chunked_epilogue(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S0),
+                                      float(scale), _ptr(g), ctypes.byref(p), _ptr(y), _ptr(S_final),
+                                      _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_fwd_chunked_epilogue")
+    return y, S_final

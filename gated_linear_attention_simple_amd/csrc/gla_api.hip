@@ -177,6 +177,41 @@ int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv, const void* q, c
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 
+int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                             const void* v, const float* lambda, const float* S0, float scale, const void* g,
+                             const gla_epilogue_params* ep, void* y, float* S_final, void* ws, size_t ws_bytes,
+                             void* stream) {
+    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (st != GLA_OK) return st;
+    gla::EpilogueArgs a;
+    st = epi_fill(ep, H, dk, dv, &a);
+    if (st != GLA_OK) return st;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(y) || !ok_ptr(g) || !ok_ptr(lambda)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
+    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
+    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    a.units = (long)B * T * H;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = y;
+    a.g = g;
+    a.y = y;
+    if (dtype == GLA_BF16 && T > 0) {
+        const hipError_t err = gla::launch_fwd_bf16_epilogue(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, y,
+                                                             S_final, ws, a, s);
+        if (err == hipSuccess) return GLA_OK;
+        if (err != hipErrorNotSupported) return GLA_ERR_DEVICE;
+    }
+    // other plans: the readout into y, then the epilogue pass over y in place
+    hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, y,
+                                     S_final, ws, s);
+    if (err == hipSuccess && a.units > 0) err = gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, s);
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
 int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
                              const void* g, const float* lambda, float* S, int P, const int* slots, float scale,
                              const gla_epilogue_params* ep, void* y, void* stream) {

@@ -40,6 +40,11 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// sigmoid on the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float fast_sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 // A wave-uniform fp32 value moved to a scalar register (bit pattern preserved;
 // the readfirstlane builtin itself operates on 32-bit integers).
 __device__ __forceinline__ float uniform_f32(float x) {

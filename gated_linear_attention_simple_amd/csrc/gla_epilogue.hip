@@ -107,11 +107,6 @@ struct EpiShape {
     static_assert(DV % VEC == 0 && DK % VEC == 0 && NVL <= 64 && NKL <= LPU, "row pieces must fit the group");
 };
 
-// sigmoid and SiLU on the hardware exp2 and reciprocal (about 1 ulp each)
-__device__ __forceinline__ float fast_sigmoid(float x) {
-    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
-}
-
 // Workgroup w takes the batches w, w + G, w + 2G, ... of UPB consecutive units
 // (G = gridDim.x, a multiple of H, so a thread keeps one head throughout and
 // loads its parameter rows once).  The next batch's five row loads are issued

@@ -179,10 +179,9 @@ __device__ __forceinline__ void score_blocks_to_lds(const bf16* Qs, const bf16* 
 // column block cb: this wave's state block (16 rows) paired with the partner's,
 // rows 32p + 4g + r from the h = 0 wave, rows 32p + 16 + 4g + r from h = 1.
 // `pws[x + 1]` = scale * lam^x and the score blocks already carry `scale`.
-template <int C, int LDK, int NCB, int K, typename SopF>
-__device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, SopF sop, const bf16x8 (&vf)[NCB][C / 32],
-                                         const float* pws, bf16* ob, size_t tokV, int t0, int ceff, int colbase,
-                                         int n, int g) {
+template <int C, int LDK, int NCB, int K, typename SopF, typename EmitF>
+__device__ __forceinline__ void out_strip(const bf16* Qs, const bf16* As, SopF sop, const bf16x8 (&vf)[NCB][C / 32],
+                                          const float* pws, int n, int g, EmitF emit) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         f32x4 OT[NCB];
@@ -209,14 +208,22 @@ __device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, SopF so
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf[cb][p], aop, OT[cb]);
         }
-        const int irow = 32 * K + 16 * u + n;
+        emit(u, 32 * K + 16 * u + n, OT);
+    }
+}
+
+// Output strip K stored as bf16: row irow, columns colbase + 16 cb + 4 g + r.
+template <int C, int LDK, int NCB, int K, typename SopF>
+__device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, SopF sop, const bf16x8 (&vf)[NCB][C / 32],
+                                         const float* pws, bf16* ob, size_t tokV, int t0, int ceff, int colbase,
+                                         int n, int g) {
+    out_strip<C, LDK, NCB, K>(Qs, As, sop, vf, pws, n, g, [&](int, int irow, const f32x4(&OT)[NCB]) {
         if (irow < ceff) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb)
                 store4<bf16>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT[cb]);
-            }
         }
-    }
+    });
 }
 
 template <int C, int LDK, int NCB, bool SO>
@@ -536,8 +543,8 @@ __global__ __launch_bounds__(256) void seg_scan_frag_kernel(const float* __restr
 // state update and without the pair exchange: both halves of a wave pair's
 // S^T operand come straight from the snapshot.  q and k are staged first, so
 // the score blocks overlap the arrival of the values and the start state.
-template <int C, int LDK, int NCB>
-__global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdArgs a) {
+template <int C, int LDK, int NCB, bool EPI>
+__global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdArgs a, EpilogueArgs ep) {
     using L = F8<C, LDK, NCB>;
     constexpr int NT = L::NT, NP = L::NP, LDV = L::LDV, NCG = L::NCG;
     __shared__ __align__(16) bf16 Qs[C * LDK];
@@ -545,6 +552,11 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     __shared__ __align__(16) bf16 Vs[C * LDV];
     __shared__ __align__(16) bf16 As[L::AS_BYTES / 2];
     __shared__ float pws[C + 2];  // pws[0] = 0, pws[x + 1] = scale * lam^x (x = 0..C)
+    // epilogue: the head's self-augmentation vector, each row's gate, and each
+    // row's partial sums of squares from the NCG column groups
+    __shared__ float augs[EPI ? kDK : 1];
+    __shared__ float sg[EPI ? C : 1];
+    __shared__ float red[EPI ? C * NCG : 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -577,6 +589,11 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
 
     using StageK = std::conditional_t<NT % (kDK / 8) == 0, RowStage<C, kDK, NT>, BufStage<C, kDK, NT>>;
     using StageV = std::conditional_t<NT % (kDV / 8) == 0, RowStage<C, kDV, NT>, BufStage<C, kDV, NT>>;
+    // (epilogue) the augmentation vector is requested before the tiles, so
+    // that waiting for it waits for no tile
+    float augv = 0.f;
+    if constexpr (EPI)
+        if (ep.aug_a && tid < kDK) augv = ep.aug_a[(size_t)hd * kDK + tid];
     StageK tq, tk;
     StageV tv;
     tq.load(qb, tokK, ceff, tid);
@@ -592,16 +609,56 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
             so[i][cb] = sn[((wave * 3 + i) * NCB + cb) * 64 + lane];
             sp[i][cb] = sn[((partner * 3 + i) * NCB + cb) * 64 + lane];
         }
+    // (epilogue) the output gate of this lane's rows and the tier's norm
+    // weights of its columns, requested last: they are used last
+    constexpr int NSTRIP = C == 128 ? 2 : 1;
+    uint2 gq[NSTRIP][2][NCB];
+    f32x4 wn[NCB];
+    if constexpr (EPI) {
+        const bf16* gb = static_cast<const bf16*>(ep.g) + tok0 * kDV;   // row t0 of this (b, h)
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(gb), 0,
+                                                          __builtin_amdgcn_readfirstlane(ceff * tokV * 2), kBufWord3);
+#pragma unroll
+        for (int j = 0; j < NSTRIP; ++j)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const int K = C == 128 ? (h == 0 ? 3 * j : 1 + j) : h;
+                    const int irow = 32 * K + 16 * u + n;
+                    gq[j][u][cb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                                 rg, (irow * tokV + colbase + 16 * cb + 4 * g) * 2, 0, 0));
+                }
+        const float* wt = ep.norm_w + (size_t)ep.tier[hd] * kDV + colbase + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) wn[cb] = *reinterpret_cast<const f32x4*>(wt + 16 * cb);
+    }
 
     const float lam = a.lambda[hd];
     if (tid < C + 2) pws[tid] = tid == 0 ? 0.f : a.scale * pow_int(lam, tid - 1);
+    if constexpr (EPI)
+        if (tid < kDK) augs[tid] = augv;
 
     tq.template store<LDK>(Qs, tid);
     tk.template store<LDK>(Ks, tid);
     __syncthreads();  // q, k, decay table
+    if constexpr (EPI) {
+        // gate of row tid: sigmoid(q . (a (.) k)) with the raw q and k
+        if (tid < C) {
+            float z = 0.f;
+#pragma unroll
+            for (int i8 = 0; i8 < kDK; i8 += 8) {
+                const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Qs + tid * LDK + i8);
+                const bf16x8 kv = *reinterpret_cast<const bf16x8*>(Ks + tid * LDK + i8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z += to_f32(qv[e]) * augs[i8 + e] * to_f32(kv[e]);
+            }
+            sg[tid] = fast_sigmoid(z);
+        }
+    }
     score_blocks_to_lds<C, LDK, L::NW, NS>(Qs, Ks, As, pws, blk, sa, sb, use_b, n, g);
     tv.template store<LDV>(Vs, tid);
-    __syncthreads();  // score blocks, values
+    __syncthreads();  // score blocks, values (and the gates)
 
     bf16x8 vf[NCB][NP];  // vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
 #pragma unroll
@@ -614,17 +671,80 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
         return h == 0 ? __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7)
                       : __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    if constexpr (C == 128) {
-        if (h == 0) {
-            out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-            out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+    if constexpr (!EPI) {
+        if constexpr (C == 128) {
+            if (h == 0) {
+                out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            } else {
+                out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            }
         } else {
-            out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-            out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
         }
     } else {
-        if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-        else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+        // Epilogue: x = o + s v per row; each row's sum of squares is spread
+        // over the NCG column groups of the waves that own the row's strip, so
+        // it goes through LDS; then y = silu(g) x / sqrt(mean x^2 + eps) w.
+        const int cgp = wave % NCG;
+        f32x4 X[NSTRIP][2][NCB];
+        auto collect = [&](int j) {
+            return [&, j](int u, int irow, const f32x4(&OT)[NCB]) {
+                const float sv = sg[irow];
+                float ss = 0.f;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(Vs + irow * LDV + colbase + 16 * cb + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        X[j][u][cb][r] = fmaf(sv, to_f32(v4[r]), OT[cb][r]);
+                        ss = fmaf(X[j][u][cb][r], X[j][u][cb][r], ss);
+                    }
+                }
+                ss += __shfl_xor(ss, 16, 64);   // the four lanes of row irow
+                ss += __shfl_xor(ss, 32, 64);
+                if (g == 0) red[irow * NCG + cgp] = ss;
+            };
+        };
+        if constexpr (C == 128) {
+            if (h == 0) {
+                out_strip<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, n, g, collect(0));
+                out_strip<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, n, g, collect(1));
+            } else {
+                out_strip<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, n, g, collect(0));
+                out_strip<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, n, g, collect(1));
+            }
+        } else {
+            if (h == 0) out_strip<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, n, g, collect(0));
+            else out_strip<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, n, g, collect(0));
+        }
+        __syncthreads();  // every row's partial sums of squares
+#pragma unroll
+        for (int j = 0; j < NSTRIP; ++j)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int K = C == 128 ? (h == 0 ? 3 * j : 1 + j) : h;
+                const int irow = 32 * K + 16 * u + n;
+                float tot = 0.f;
+#pragma unroll
+                for (int q = 0; q < NCG; ++q) tot += red[irow * NCG + q];
+                const float inv = __builtin_amdgcn_rsqf(tot * (1.f / kDV) + ep.eps);
+                if (irow < ceff) {
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const bf16x4 g4 = __builtin_bit_cast(bf16x4, gq[j][u][cb]);
+                        f32x4 y;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float gc = to_f32(g4[r]);
+                            y[r] = gc * fast_sigmoid(gc) * X[j][u][cb][r] * inv * wn[cb][r];
+                        }
+                        store4<bf16>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, y);
+                    }
+                }
+            }
     }
 }
 
@@ -889,7 +1009,7 @@ hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, cons
 template <int C, int LDK, int NCB>
 hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k, const void* v,
                     const float* lambda, const float* S0, float scale, void* o, float* S_final, void* ws,
-                    hipStream_t stream) {
+                    const EpilogueArgs* ep, hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
     a.H = H;
@@ -915,10 +1035,15 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
         a.U = nullptr;
         a.Ub = ws;
         a.S_final = nullptr;
-        hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT), 0, stream,
-                           a);
+        if (ep)
+            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, true>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT),
+                               0, stream, a, *ep);
+        else
+            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, false>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT),
+                               0, stream, a, EpilogueArgs{});
         return hipGetLastError();
     }
+    if (ep) return hipErrorNotSupported;   // the epilogue is fused into the chain form only
     if (plan.nseg > 1) {
         hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, true>), dim3(plan.nseg - 1, units), dim3(F8<C, LDK, NCB>::NT),
                            0, stream, a);
@@ -945,13 +1070,23 @@ hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, 
     if (const char* e = getenv("GLA_FWD_NCB")) ncb = atoi(e) == 3 ? 3 : 2;  // tuning override (sweeps)
 #define GLA_CASE(C_, NCB_)                                                                                          \
     if (chunk == C_ && ncb == NCB_)                                                                                  \
-        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, stream);
+        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, nullptr, stream);
     GLA_CASE(128, 2)
     GLA_CASE(128, 3)
     GLA_CASE(64, 2)
     GLA_CASE(64, 3)
 #undef GLA_CASE
     return hipErrorInvalidValue;
+}
+
+// The forward with the mixer epilogue applied in the output kernel's store
+// (the tiled-chain form only; hipErrorNotSupported otherwise, the caller then
+// runs the forward and the epilogue pass).
+hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
+                                    const void* v, const float* lambda, const float* S0, float scale, void* y,
+                                    float* S_final, void* ws, const EpilogueArgs& ep, hipStream_t stream) {
+    if (!plan.chain || chunk != 128) return hipErrorNotSupported;
+    return launch_c<128, 104, 2>(plan, B, T, H, q, k, v, lambda, S0, scale, y, S_final, ws, &ep, stream);
 }
 
 }  // namespace gla

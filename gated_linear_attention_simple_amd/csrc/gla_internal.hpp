@@ -136,6 +136,11 @@ struct EpilogueArgs {
 
 bool epilogue_supported(int dk, int dv);
 hipError_t launch_epilogue(bool bf16_io, int dk, int dv, const EpilogueArgs& a, hipStream_t stream);
+// bf16 forward with the epilogue in the output kernel (tiled-chain plans only;
+// hipErrorNotSupported for other plans)
+hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
+                                    const void* v, const float* lambda, const float* S0, float scale, void* y,
+                                    float* S_final, void* ws, const EpilogueArgs& ep, hipStream_t stream);
 
 // Depth-wise causal conv + SiLU (width 4).  Prefill: x, y [B][T][D], windows
 // [B][4][D] fp32 (win_in nullable).  Decode: x, y [N = B][D], win_out is the

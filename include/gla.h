@@ -203,6 +203,23 @@ int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv,
                        const gla_epilogue_params* ep, void* y, void* stream);
 
 /*
+ * The forward (gla_fwd_chunked) followed by the epilogue above, with y in place
+ * of o: y[b,t,h] = epilogue(q, k, v, o, g)[b,t,h] for the readout o the forward
+ * defines (o itself is not stored).  For bf16 plans that run the tiled state
+ * chain (128-token chunks, B*H <= 16, as at B = 1, H = 16) the epilogue is
+ * applied in the output kernel's store, on the fp32 readout; other plans run the
+ * forward into y and the epilogue pass over y in place.
+ *   g      [B][T][H][dv] (dtype) output-gate logits;   y  [B][T][H][dv] (dtype) output
+ *   ws     as gla_fwd_chunked (gla_fwd_workspace_bytes of the same sizes)
+ *   others as gla_fwd_chunked and gla_mixer_epilogue; the errors of both.
+ */
+int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                             const void* q, const void* k, const void* v,
+                             const float* lambda, const float* S0, float scale,
+                             const void* g, const gla_epilogue_params* ep, void* y,
+                             float* S_final, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Decode step with the epilogue fused into it: the state update and readout of
  * gla_decode_step (slots == NULL, S holds N pages [N][H][dk][dv]) or of
  * gla_decode_step_pool (slots != NULL, S is a pool of P pages), then the
