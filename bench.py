@@ -144,9 +144,11 @@ class FwdLeg:
 
 
 class TrainLeg:
-    """Pre-marshalled forward + backward (dq, dk, dv, dlambda) on the mixer-train workload."""
+    """Pre-marshalled forward + backward (dq, dk, dv, dlambda) on the mixer-train workload:
+    the forward saving every chunk's start state and the backward reading them
+    (saved=True), or the plain pair whose backward recomputes them."""
 
-    def __init__(self, gla, gi, torch, w, seed, chunk):
+    def __init__(self, gla, gi, torch, w, seed, chunk, saved=True):
         dev = torch.device("cuda:0")
         x = gi.fwd_inputs(w, dev, seed, with_do=True)
         self.x = x
@@ -166,13 +168,23 @@ class TrainLeg:
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         st = ctypes.c_void_p(self.stream.cuda_stream)
         lib = gla.load()
-        self.f, self.b = lib.gla_fwd_chunked, lib.gla_bwd_chunked
         sc = ctypes.c_float(x["scale"])
-        self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
-                      p(self.o), None, p(self.wsf), ctypes.c_size_t(nf), st)
-        self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
-                      p(x["do"]), None, p(self.dq), p(self.dk), p(self.dv), p(self.dl), None, p(self.wsb),
-                      ctypes.c_size_t(nb), st)
+        if saved:
+            self.states = torch.empty(lib.gla_fwd_states_bytes(dt, B, T, H, dk, dv, chunk), dtype=torch.uint8,
+                                      device=dev)
+            self.f, self.b = lib.gla_fwd_chunked_states, lib.gla_bwd_chunked_states
+            self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                          p(self.o), None, p(self.states), p(self.wsf), ctypes.c_size_t(nf), st)
+            self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                          p(x["do"]), None, p(self.states), p(self.dq), p(self.dk), p(self.dv), p(self.dl), None,
+                          p(self.wsb), ctypes.c_size_t(nb), st)
+        else:
+            self.f, self.b = lib.gla_fwd_chunked, lib.gla_bwd_chunked
+            self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                          p(self.o), None, p(self.wsf), ctypes.c_size_t(nf), st)
+            self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
+                          p(x["do"]), None, p(self.dq), p(self.dk), p(self.dv), p(self.dl), None, p(self.wsb),
+                          ctypes.c_size_t(nb), st)
         self.gla = gla
 
     def __call__(self):
@@ -536,9 +548,17 @@ def main():
         tf = train_flops_per_token_head(C) * tleg.token_heads
         leg = {"value": K * tleg.tokens / t_wall, "unit": "tokens/s", "ms_per_step": t_wall / K * 1e3,
                "workload": f"mixer-train B=8 H=16 T=2048 dk=96 dv=192 C={C} bf16, fwd + bwd (dq,dk,dv,dlambda)",
+               "calls": "gla_fwd_chunked_states + gla_bwd_chunked_states (chunk states saved by the forward)",
                "avg_step_us": t_avg * 1e6, "alg_bytes_per_step": tb, "alg_flops_per_step": tf,
                "hbm_gbs": tb / t_avg / 1e9, "hbm_frac": tb / t_avg / 1e9 / HBM_PEAK_GBS,
                "mfma_tflops": tf / t_avg / 1e12, "mfma_frac": tf / t_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        del tleg
+        torch.cuda.empty_cache()
+        rleg = TrainLeg(gla, gi, torch, w2, 2, C, saved=False)
+        r_wall, r_gpu = time_region(torch, rleg.stream, rleg, K, W)
+        leg["recompute"] = {"calls": "gla_fwd_chunked + gla_bwd_chunked (the backward recomputes the states)",
+                            "avg_step_us": r_gpu / K * 1e6, "value": K * rleg.tokens / r_wall}
+        tleg = rleg
         result["train"][f"chunk{C}"] = leg
         if C == 128:
             t_ms = leg["ms_per_step"]

@@ -25,6 +25,9 @@ SYMBOLS = (
     "gla_fwd_chunked",
     "gla_bwd_workspace_bytes",
     "gla_bwd_chunked",
+    "gla_fwd_states_bytes",
+    "gla_fwd_chunked_states",
+    "gla_bwd_chunked_states",
     "gla_decode_step",
     "gla_decode_step_pool",
     "gla_mixer_epilogue",
@@ -69,6 +72,12 @@ def load():
         lib.gla_bwd_workspace_bytes.argtypes = [i] * 7
         lib.gla_bwd_chunked.restype = i
         lib.gla_bwd_chunked.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.gla_fwd_states_bytes.restype = sz
+        lib.gla_fwd_states_bytes.argtypes = [i] * 7
+        lib.gla_fwd_chunked_states.restype = i
+        lib.gla_fwd_chunked_states.argtypes = [i] * 7 + [vp, vp, vp, vp, vp, f, vp, vp, vp, vp, sz, vp]
+        lib.gla_bwd_chunked_states.restype = i
+        lib.gla_bwd_chunked_states.argtypes = [i] * 7 + [vp] * 5 + [f] + [vp] * 9 + [sz, vp]
         lib.gla_decode_step.restype = i
         lib.gla_decode_step.argtypes = [i] * 5 + [vp, vp, vp, vp, vp, f, vp, vp]
         lib.gla_decode_step_pool.restype = i
@@ -401,3 +410,63 @@ def fwd_chunked_epilogue(q, k, v, lam, g, norm_w, head_tier, aug_a=None, eps=1e-
     if st != GLA_OK:
         raise GlaError(st, "gla_fwd_chunked_epilogue")
     return y, S_final
+
+
+def fwd_chunked_states(q, k, v, lam, S0=None, scale=1.0, chunk=128, S_final=True, workspace=None, stream=None):
+    """o, S_final, states = the forward, also saving every chunk's start state for the backward."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, T, H, dk), q.dtype, dev)
+    _check(k, "k", (B, T, H, dk), q.dtype, dev)
+    _check(v, "v", (B, T, H, dv), q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if S_final else None
+    nc = (T + chunk - 1) // chunk
+    states = torch.empty((B, H, nc, dk, dv), dtype=q.dtype, device=dev)
+    dt = _dt(q)
+    need = lib.gla_fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gla_fwd_chunked_states(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S0),
+                                    float(scale), _ptr(o), _ptr(S_final), _ptr(states), _ptr(workspace), ws_bytes,
+                                    _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_fwd_chunked_states")
+    return o, S_final, states
+
+
+def bwd_chunked_states(q, k, v, lam, d_o, states, S0=None, dS_final=None, scale=1.0, chunk=128,
+                       dlambda=True, dS0=True, workspace=None, stream=None):
+    """dq, dk, dv, dlambda, dS0 from the chunk start states saved by fwd_chunked_states."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    nc = (T + chunk - 1) // chunk
+    for t, name, shape in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv)),
+                           (d_o, "do", (B, T, H, dv)), (states, "states", (B, H, nc, dk, dv))):
+        _check(t, name, shape, q.dtype, dev)
+    _check(lam, "lambda", (H,), torch.float32, dev)
+    for t, name in ((S0, "S0"), (dS_final, "dS_final")):
+        if t is not None:
+            _check(t, name, (B, H, dk, dv), torch.float32, dev)
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dl = torch.empty(H, dtype=torch.float32, device=dev) if dlambda else None
+    ds0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if dS0 else None
+    dt = _dt(q)
+    need = lib.gla_bwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gla_bwd_chunked_states(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S0),
+                                    float(scale), _ptr(d_o), _ptr(dS_final), _ptr(states), _ptr(dq), _ptr(dkk),
+                                    _ptr(dvv), _ptr(dl), _ptr(ds0), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != GLA_OK:
+        raise GlaError(st, "gla_bwd_chunked_states")
+    return dq, dkk, dvv, dl, ds0

@@ -99,7 +99,7 @@ int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, c
     const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
     if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
     const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
-                                           scale, o, S_final, ws, static_cast<hipStream_t>(stream));
+                                           scale, o, S_final, nullptr, ws, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 
@@ -122,7 +122,49 @@ int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, c
     if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
     const hipError_t err =
         gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final,
-                        dq, dk_out, dv_out, dlambda, dS0, ws, static_cast<hipStream_t>(stream));
+                        dq, dk_out, dv_out, dlambda, dS0, nullptr, ws, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+size_t gla_fwd_states_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
+    const size_t nc = ((size_t)T + chunk - 1) / chunk;
+    return (size_t)B * H * nc * dk * dv * (dtype == GLA_BF16 ? 2 : 4);
+}
+
+int gla_fwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                           void* states, void* ws, size_t ws_bytes, void* stream) {
+    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (st != GLA_OK) return st;
+    if (!gla::bwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda) || !ok_ptr(states)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
+    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
+    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
+                                           scale, o, S_final, T > 0 ? states : nullptr, ws,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+}
+
+int gla_bwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                           const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
+                           const float* dS_final, const void* states, void* dq, void* dk_out, void* dv_out,
+                           float* dlambda, float* dS0, void* ws, size_t ws_bytes, void* stream) {
+    int st = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (st != GLA_OK) return st;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(d_o) || !ok_ptr(dq) ||
+                  !ok_ptr(dk_out) || !ok_ptr(dv_out) || !ok_ptr(states)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(dS_final) || !ok_opt(dlambda) || !ok_opt(dS0)) return GLA_ERR_INVALID_ARG;
+    const gla::BwdPlan plan = gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
+    if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    const hipError_t err =
+        gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final,
+                        dq, dk_out, dv_out, dlambda, dS0, T > 0 ? states : nullptr, ws,
+                        static_cast<hipStream_t>(stream));
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }
 
@@ -207,7 +249,7 @@ int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int
     }
     // other plans: the readout into y, then the epilogue pass over y in place
     hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, y,
-                                     S_final, ws, s);
+                                     S_final, nullptr, ws, s);
     if (err == hipSuccess && a.units > 0) err = gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, s);
     return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
 }

@@ -635,11 +635,11 @@ template <typename E, int DK, int DV, int C>
 static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const void* q, const void* k,
                                const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
                                const float* dST, void* dq, void* dk, void* dv, float* dlambda, float* dS0,
-                               void* ws, hipStream_t stream) {
+                               const void* sbar_in, void* ws, hipStream_t stream) {
     constexpr int NW = DV / 16 >= 4 ? 4 : DV / 16;
     constexpr int dkdv = DK * DV;
     char* w = static_cast<char*>(ws);
-    void* sbar = w;
+    void* sbar = sbar_in ? const_cast<void*>(sbar_in) : w;
     void* gbar = w + plan.snap_bytes;
     float* U = reinterpret_cast<float*>(w + 2 * plan.snap_bytes);
     float* part = reinterpret_cast<float*>(w + 2 * plan.snap_bytes + plan.u_bytes);
@@ -681,12 +681,15 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
             return hipGetLastError();
         }
     };
-    if (nseg > 1) {
-        if ((err = chain(false, false, nseg - 1)) != hipSuccess) return err;
-        if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) != hipSuccess)
-            return err;
+    if (!sbar_in) {   // the forward's chunk start states were not saved: recompute them
+        if (nseg > 1) {
+            if ((err = chain(false, false, nseg - 1)) != hipSuccess) return err;
+            if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) !=
+                hipSuccess)
+                return err;
+        }
+        if ((err = chain(false, true, nseg)) != hipSuccess) return err;
     }
-    if ((err = chain(false, true, nseg)) != hipSuccess) return err;
     // reverse chain: snapshots Gbar, dS0, <Gbar, Sbar> partials
     s.x = q;
     s.y = d_o;
@@ -741,7 +744,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
 hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
                       const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
                       const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
-                      float* dS0, void* ws, hipStream_t stream) {
+                      float* dS0, const void* sbar_in, void* ws, hipStream_t stream) {
     if (T == 0) {
         const size_t n = (size_t)B * H * dk * dv;
         hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
@@ -750,13 +753,13 @@ hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, in
     }
     if (bf16_io && dk == 96 && dv == 192 && chunk == 128)
         return launch_bwd_t<bf16, 96, 192, 128>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                                dv_out, dlambda, dS0, ws, stream);
+                                                dv_out, dlambda, dS0, sbar_in, ws, stream);
     if (bf16_io && dk == 96 && dv == 192 && chunk == 64)
         return launch_bwd_t<bf16, 96, 192, 64>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                               dv_out, dlambda, dS0, ws, stream);
+                                               dv_out, dlambda, dS0, sbar_in, ws, stream);
     if (!bf16_io && dk == 16 && dv == 32 && chunk == 32)
         return launch_bwd_t<float, 16, 32, 32>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                               dv_out, dlambda, dS0, ws, stream);
+                                               dv_out, dlambda, dS0, sbar_in, ws, stream);
     return hipErrorInvalidValue;
 }
 

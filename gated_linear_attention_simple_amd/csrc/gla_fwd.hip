@@ -125,6 +125,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_f32_kernel(FwdArgs a) {
     for (int c = c_begin; c < c_end; ++c) {
         const int t0 = c * C;
         const int ceff = min(C, T - t0);
+        if constexpr (!STATE_ONLY) {
+            if (a.sbar) {  // the chunk's start state, for the backward
+                E* sb = static_cast<E*>(a.sbar) + ((size_t)bh * a.nc + c) * DK * DV;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sb[sidx(db, cb, r)] = Sacc[db][cb][r];
+            }
+        }
         if (!STATE_ONLY) tq.load(qb + (size_t)t0 * tokK, tokK, T - t0, tid);
         tk.load(kb + (size_t)t0 * tokK, tokK, T - t0, tid);
         tv.load(vb + (size_t)t0 * tokV, tokV, T - t0, tid);
@@ -333,7 +344,7 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
 template <int DK, int DV, int C, int NW>
 static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k,
                                  const void* v, const float* lambda, const float* S0, float scale, void* o,
-                                 float* S_final, void* ws, hipStream_t stream) {
+                                 float* S_final, void* sbar, void* ws, hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
     a.H = H;
@@ -346,6 +357,7 @@ static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const
     a.o = o;
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
+    a.sbar = sbar;
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
     a.nc = plan.nc;
@@ -364,7 +376,7 @@ static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const
 
 hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
                       const void* q, const void* k, const void* v, const float* lambda, const float* S0,
-                      float scale, void* o, float* S_final, void* ws, hipStream_t stream) {
+                      float scale, void* o, float* S_final, void* sbar, void* ws, hipStream_t stream) {
     if (B == 0 || H == 0) return hipSuccess;
     if (T == 0) {
         if (!S_final) return hipSuccess;
@@ -375,13 +387,13 @@ hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, in
     }
     if (bf16_io) {
         if (dk == 96 && dv == 192)
-            return launch_fwd_bf16(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, o, S_final, ws, stream);
+            return launch_fwd_bf16(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, o, S_final, sbar, ws, stream);
         return hipErrorInvalidValue;
     }
 #define GLA_FWD_CASE(DK_, DV_, C_, NW_)                                                                   \
     if (dk == DK_ && dv == DV_ && chunk == C_)                                                             \
-        return launch_fwd_f32<DK_, DV_, C_, NW_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, \
-                                                 stream);
+        return launch_fwd_f32<DK_, DV_, C_, NW_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, sbar, \
+                                                 ws, stream);
     GLA_FWD_CASE(96, 192, 64, 4)
     GLA_FWD_CASE(16, 32, 32, 2)
 #undef GLA_FWD_CASE

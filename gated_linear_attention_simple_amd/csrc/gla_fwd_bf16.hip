@@ -396,6 +396,16 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                 for (int cb = 0; cb < NCB; ++cb)
                     *xs_at(wave, i, cb) = bf16x4{to_bf16(Sacc[i][cb][0]), to_bf16(Sacc[i][cb][1]),
                                                  to_bf16(Sacc[i][cb][2]), to_bf16(Sacc[i][cb][3])};
+            if (a.sbar) {  // the chunk's start state, for the backward (row-major, bf16)
+                bf16* sb = static_cast<bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)   // (this chunk's lane-derived n, g)
+                            sb[(16 * (2 * i + h) + 4 * g + r) * kDV + colbase + 16 * cb + n] = to_bf16(Sacc[i][cb][r]);
+            }
         } else {
             // state only: keys are needed only scaled, K^T diag(c)
             tk.template store_scaled<LDK>(Ks, tid, [&](int row) { return cjc[row]; });
@@ -683,6 +693,20 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
         } else {
             if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
             else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+        }
+        if (a.sbar) {
+            // the chunk's start state for the backward, row-major: this wave's
+            // half (16-row blocks 2i + h), columns colbase + 16 cb + n
+            bf16* sb = static_cast<bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV;
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const bf16x4 s4 = __builtin_bit_cast(bf16x4, so[i][cb]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sb[(size_t)(16 * (2 * i + h) + 4 * g + r) * kDV + colbase + 16 * cb + n] = s4[r];
+                }
         }
     } else {
         // Epilogue: x = o + s v per row; each row's sum of squares is spread
@@ -1008,7 +1032,7 @@ hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, cons
 
 template <int C, int LDK, int NCB>
 hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k, const void* v,
-                    const float* lambda, const float* S0, float scale, void* o, float* S_final, void* ws,
+                    const float* lambda, const float* S0, float scale, void* o, float* S_final, void* sbar, void* ws,
                     const EpilogueArgs* ep, hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
@@ -1023,6 +1047,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
     a.Ub = static_cast<char*>(ws) + (size_t)B * H * (plan.nseg > 1 ? plan.nseg - 1 : 0) * kDK * kDV * sizeof(float);
+    a.sbar = sbar;
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
     a.nc = plan.nc;
@@ -1064,13 +1089,14 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
 
 hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
                            const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                           void* ws, hipStream_t stream) {
+                           void* sbar, void* ws, hipStream_t stream) {
     // Waves per workgroup: 12 (two 16-column blocks each) or 8 (three each).
     int ncb = 2;
     if (const char* e = getenv("GLA_FWD_NCB")) ncb = atoi(e) == 3 ? 3 : 2;  // tuning override (sweeps)
 #define GLA_CASE(C_, NCB_)                                                                                          \
     if (chunk == C_ && ncb == NCB_)                                                                                  \
-        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, ws, nullptr, stream);
+        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, sbar, ws, nullptr, \
+                                       stream);
     GLA_CASE(128, 2)
     GLA_CASE(128, 3)
     GLA_CASE(64, 2)
@@ -1086,7 +1112,7 @@ hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, in
                                     const void* v, const float* lambda, const float* S0, float scale, void* y,
                                     float* S_final, void* ws, const EpilogueArgs& ep, hipStream_t stream) {
     if (!plan.chain || chunk != 128) return hipErrorNotSupported;
-    return launch_c<128, 104, 2>(plan, B, T, H, q, k, v, lambda, S0, scale, y, S_final, ws, &ep, stream);
+    return launch_c<128, 104, 2>(plan, B, T, H, q, k, v, lambda, S0, scale, y, S_final, nullptr, ws, &ep, stream);
 }
 
 }  // namespace gla

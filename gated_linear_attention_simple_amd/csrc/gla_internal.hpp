@@ -18,6 +18,7 @@ struct FwdArgs {
     float* S_final;
     float* U;          // [B*H][nseg-1][DK*DV]: segment-local end states, then segment start states
     void* Ub;          // bf16 copies of the start states (bf16 path, one-chunk segments), or null
+    void* sbar;        // optional: every chunk's start state, [B*H][nc][DK][DV] in the input dtype
     int nseg, seg_chunks, nc;
 };
 
@@ -36,15 +37,17 @@ constexpr int kChainMaxChunks = 64;
 
 bool fwd_supported(bool bf16_io, int dk, int dv, int chunk);
 FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+// sbar (nullable): also store every chunk's start state, [B*H][nc][dk][dv] in
+// the input dtype (the snapshots the backward consumes).
 hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv,
                       int chunk, const void* q, const void* k, const void* v, const float* lambda,
-                      const float* S0, float scale, void* o, float* S_final, void* ws,
+                      const float* S0, float scale, void* o, float* S_final, void* sbar, void* ws,
                       hipStream_t stream);
 
 // bf16 forward (dk = 96, dv = 192, chunk 64 or 128): prologue, scan and main launches.
 hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
                            const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                           void* ws, hipStream_t stream);
+                           void* sbar, void* ws, hipStream_t stream);
 
 // Sequence segments run in parallel (at most this many per sequence).
 constexpr int kMaxSegments = 16;
@@ -109,10 +112,12 @@ struct BwdPlan {
 };
 bool bwd_supported(bool bf16_io, int dk, int dv, int chunk);
 BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+// sbar_in (nullable): the chunk start states saved by the forward; the
+// backward then skips its own forward state pass.
 hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
                       const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
                       const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
-                      float* dS0, void* ws, hipStream_t stream);
+                      float* dS0, const void* sbar_in, void* ws, hipStream_t stream);
 
 bool decode_supported(int dk, int dv);
 // Mixer epilogue: device pointers, the tier map travels by value.

@@ -128,6 +128,38 @@ int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Training pair: a forward that also saves the state entering every chunk, and
+ * a backward that reads those states instead of re-running the forward state
+ * chain (Laplace 3B post, section "Challenge 3": the backward walks the chunk
+ * chain; its forward half is exactly what the forward already computed).
+ *   states  [B][H][ceil(T/chunk)][dk][dv] in the dtype of q (bf16 or fp32):
+ *           states[b][h][c] = the state before chunk c (S0 or 0 for c = 0),
+ *           rounded to the dtype; gla_fwd_states_bytes gives its size.
+ * gla_fwd_chunked_states: as gla_fwd_chunked, plus `states` (written).  Only for
+ * shapes gla_bwd_chunked supports (else GLA_ERR_UNSUPPORTED); same workspace.
+ * gla_bwd_chunked_states: as gla_bwd_chunked, plus `states` (read), which must
+ * come from gla_fwd_chunked_states over the same q, k, v, lambda, S0 and sizes;
+ * same workspace size (gla_bwd_workspace_bytes).  The gradients agree with
+ * gla_bwd_chunked's within rounding (the saved states are rounded as the
+ * backward's own are, from a differently ordered but equal fp32 recurrence).
+ */
+size_t gla_fwd_states_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+int gla_fwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                           const void* q, const void* k, const void* v,
+                           const float* lambda, const float* S0, float scale,
+                           void* o, float* S_final, void* states,
+                           void* ws, size_t ws_bytes, void* stream);
+
+int gla_bwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                           const void* q, const void* k, const void* v,
+                           const float* lambda, const float* S0, float scale,
+                           const void* d_o, const float* dS_final, const void* states,
+                           void* dq, void* dk_out, void* dv_out,
+                           float* dlambda, float* dS0,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Batched single-token decode step (Laplace 3B post, section "Optimizing
  * inference on Trainium2": one fixed state page per sequence, read and written
  * once per generated token).  For every sequence n and head h, in place:

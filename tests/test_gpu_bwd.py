@@ -96,3 +96,63 @@ def test_page_decay_schedule(chunk):
     w = gi.Workload(w.name + "-page-decay", w.B, w.T, w.H, w.dk, w.dv, w.chunk, w.dtype,
                     tuple(gi.page_lambdas(w.H)), w.scale)
     _run(w, seed=90 + chunk, B=2, T=600, chunk=chunk, s0_var=0.01)
+
+
+def _states_case(w, seed, B, T, chunk, s0_var, chain=None, monkeypatch=None):
+    if chain is not None:
+        monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+    x = gi.fwd_inputs(w, DEV, seed, B=B, T=T, with_do=True, with_dS=True, s0_var=s0_var)
+    _say(f"fwd/bwd with saved states {w.name} B={B} T={T} C={chunk} chain={chain}")
+    o, S, states = gla.fwd_chunked_states(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"],
+                                          chunk=chunk)
+    g = gla.bwd_chunked_states(x["q"], x["k"], x["v"], x["lam"], x["do"], states, S0=x["S0"], dS_final=x["dS"],
+                               scale=x["scale"], chunk=chunk)
+    torch.cuda.synchronize()
+    return x, o, S, states, g
+
+
+@pytest.mark.parametrize("wi,B,T,chunk,chain", [(1, 2, 700, 128, None), (1, 2, 700, 64, None),
+                                                (1, 1, 2048, 128, "1"), (1, 1, 2048, 128, "0"),
+                                                (1, 1, 300, 128, "1"), (0, 2, 200, 32, None)])
+def test_saved_states_and_backward_match_oracle(wi, B, T, chunk, chain, monkeypatch):
+    """gla_fwd_chunked_states writes the state before every chunk (checked against the
+    oracle's state after each prefix of whole chunks), and gla_bwd_chunked_states'
+    gradients from them match the oracle's reverse mode."""
+    w = gi.workloads()[wi]
+    x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 90 + T + chunk, B, T, chunk, 0.01, chain, monkeypatch)
+    nc = (T + chunk - 1) // chunk
+    c64 = lambda name: f64(x[name])
+    for c in range(nc):
+        if c == 0:
+            ref = c64("S0")
+        else:
+            _, ref = oracle.fwd(c64("q")[:, :c * chunk], c64("k")[:, :c * chunk], c64("v")[:, :c * chunk],
+                                c64("lam"), S0=c64("S0"), scale=x["scale"])
+        assert_close(f64(states[:, :, c]), ref, w.dtype, f"state before chunk {c}")
+    ro, rS = oracle.fwd(c64("q"), c64("k"), c64("v"), c64("lam"), S0=c64("S0"), scale=x["scale"])
+    assert_close(f64(o), ro, w.dtype, "o")
+    assert_close(f64(S), rS, w.dtype, "S_final")
+    r = oracle.bwd(c64("q"), c64("k"), c64("v"), c64("lam"), c64("do"), S0=c64("S0"), dS_T=c64("dS"),
+                   scale=x["scale"])
+    for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
+        assert_close(f64(got), ref, w.dtype, name)
+    assert_close(f64(dl), r[3], w.dtype, "dlambda", batch_axis=None)
+
+
+def test_saved_states_training_width_sampled():
+    """The training step's shape (B=8, T=2048, C=128) through the saved-state pair: the
+    gradients of two sequences against the oracle, and every gradient against the
+    recomputing backward's within the bf16 bar."""
+    w = gi.workloads()[2]
+    x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 7, 8, 2048, 128, 0.0)
+    g2 = gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"], dS_final=x["dS"], scale=x["scale"],
+                         chunk=128)
+    torch.cuda.synchronize()
+    for a, b, name in zip((dq, dk, dv, dl, dS0), g2, ("dq", "dk", "dv", "dlambda", "dS0")):
+        assert_close(f64(a), f64(b), "bf16", f"{name} vs recomputing backward", batch_axis=None)
+    for bi in (1, 6):
+        sl = slice(bi, bi + 1)
+        r = oracle.bwd(f64(x["q"][sl]), f64(x["k"][sl]), f64(x["v"][sl]), f64(x["lam"]), f64(x["do"][sl]),
+                       dS_T=f64(x["dS"][sl]), scale=x["scale"])
+        for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
+            assert_close(f64(got[sl]), ref, "bf16", f"{name}[{bi}]")
