@@ -188,6 +188,29 @@ def test_conv_rejects_bad_arguments():
     assert d(N=0, x=None) == gla.GLA_OK
 
 
+def test_saved_state_entry_points_validate():
+    lib = gla.load()
+    assert lib.gla_fwd_states_bytes(1, 8, 2048, 16, 96, 192, 128) == 8 * 16 * 16 * 96 * 192 * 2
+    assert lib.gla_fwd_states_bytes(0, 1, 33, 2, 16, 32, 32) == 1 * 2 * 2 * 16 * 32 * 4
+    assert lib.gla_fwd_states_bytes(1, 1, 100, 16, 80, 192, 128) == 0
+
+    def f(dtype=1, B=1, T=256, dk=96, dv=192, C=128, states=P, ws=P, wsb=1 << 30):
+        return lib.gla_fwd_chunked_states(dtype, B, T, 16, dk, dv, C, P, P, P, P, None, 1.0, P, None, states, ws,
+                                          wsb, None)
+
+    assert f(dtype=0) == gla.GLA_ERR_UNSUPPORTED           # fp32 96/192: no backward, so no saved states
+    assert f(states=None) == gla.GLA_ERR_INVALID_ARG
+    assert f(states=MIS) == gla.GLA_ERR_INVALID_ARG
+    assert f(ws=None) == gla.GLA_ERR_WORKSPACE
+
+    def b(states=P, ws=None, wsb=0, T=256):
+        return lib.gla_bwd_chunked_states(1, 1, T, 16, 96, 192, 128, P, P, P, P, None, 1.0, P, None, states, P, P, P,
+                                          None, None, ws, wsb, None)
+
+    assert b(states=None) == gla.GLA_ERR_INVALID_ARG
+    assert b() == gla.GLA_ERR_WORKSPACE
+
+
 def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,
         dq=P, dk_=P, dv_=P, dl=None, dS0=None, ws=None, wsb=0):
     return gla.load().gla_bwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, do, dST, dq, dk_, dv_,
