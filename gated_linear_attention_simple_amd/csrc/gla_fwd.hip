@@ -328,10 +328,12 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     p.ws_bytes = (size_t)units * (p.nseg - 1) * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
     // bf16, short sequence: a tiled state chain can emit every chunk's start
     // state for one output workgroup per chunk.  Measured on gfx950 it beats the
-    // segment split only for 128-token chunks and at most 16 (batch, head)
-    // units (by ~4% at 16 units x 2,048 tokens; its passes are bound by LDS
-    // transposed reads, ~0.7 us each).
-    p.chain = bf16_io && chunk == 128 && units <= 16 && p.nseg > 1 && p.nc <= kChainMaxChunks;
+    // segment split only for 128-token chunks, at most 16 (batch, head) units
+    // and at most 16 chunks (16 units: 21.1 vs 23.7 us at 512 tokens, 21.5 vs
+    // 24.8 at 1,024, 30.9 vs 31.6 at 2,048; 8 units x 4,096 tokens: 38.4 vs
+    // 32.2, its 32 passes being sequential at ~0.7 us each, bound by LDS
+    // transposed reads).
+    p.chain = bf16_io && chunk == 128 && units <= 16 && p.nseg > 1 && p.nc <= 16;
     if (const char* e = getenv("GLA_FWD_CHAIN")) {  // tuning override (sweeps, tests)
         const int forced = atoi(e);
         if (forced == 0) p.chain = 0;
