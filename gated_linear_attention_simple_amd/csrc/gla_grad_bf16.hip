@@ -22,6 +22,8 @@
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
 
+#include <stdlib.h>
+
 namespace gla {
 namespace {
 
@@ -327,16 +329,285 @@ __global__ __launch_bounds__(kNT, 2) void grad_dq_bf16(GradArgs a) {
     if (tid == 0) *part = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+
+// All three gradients of one chunk of C = 128 or 64 tokens (one workgroup of
+// 8 waves per (chunk, unit)): every operand tile is read once, where the
+// two-kernel form reads the tiles and both snapshots twice.  Wave w owns key
+// block w (keys 16w .. 16w+15, if the chunk has them) for dK, dV and one
+// 16-query block of dQ.  LDS holds K and V whole, one snapshot (Sbar, then
+// Gbar) and the queries and output gradients of one 64-query half at a time:
+// ~157 KB at C = 128 (~116 KB at 64), one workgroup per CU.
+//   A (queries 0..63):   waves 0..3 add the intra-chunk terms of their key
+//                        blocks; waves 4..7 form dQ of query blocks 0..3.
+//   B (queries 64..127, C = 128 only): waves 4..7 form dQ of query blocks
+//                        4..7, then every wave adds its key block's terms.
+//   C (Gbar):            the waves with key blocks add the inter-chunk terms
+//                        of dK, dV.
+// No wave holds dQ and dK/dV accumulators at the same time (waves 4..7 start
+// their key blocks, which only see queries 64..127, after their dQ blocks).
+constexpr int kFNW = 8, kFNT = 512;
+constexpr int kFHalf = 64;  // query rows per half
+
+template <int C>
+__global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
+    static_assert(C == 128 || C == 64, "one or two 64-query halves");
+    constexpr int NSUB = C / kST;
+    constexpr int NKB = C / 16;  // key blocks (waves that own one)
+    __shared__ __align__(16) bf16 Ks[C * kLDK];
+    __shared__ __align__(16) bf16 Vs[C * kLDV];
+    __shared__ __align__(16) bf16 Xs[kDK * kLDV];            // Sbar, then Gbar
+    __shared__ __align__(16) bf16 Qs[kFHalf * kLDK];         // one half's queries
+    __shared__ __align__(16) bf16 Ds[kFHalf * kLDV];         // and output gradients
+    __shared__ float pw[C + 2], dpw[C + 2];
+    __shared__ float red[2][kFNW];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int cid = blockIdx.x, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int hd = bh % H, b = bh / H;
+    const int t0 = cid * C;
+    const int ceff = min(C, T - t0);
+    float* part = a.part + ((size_t)bh * a.nc + cid) * kNPart + kChainSlots;
+    fill_decay_tables<C>(pw, dpw, a.lambda[hd], tid);
+
+    const int tokK = H * kDK, tokV = H * kDV;
+    const size_t tok0 = (size_t)b * T * H + hd;
+    const size_t snap = ((size_t)bh * a.nc + cid) * kDK * kDV;
+    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK + (size_t)t0 * tokK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK + (size_t)t0 * tokK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV + (size_t)t0 * tokV;
+    const bf16* db_ = static_cast<const bf16*>(a.d_o) + tok0 * kDV + (size_t)t0 * tokV;
+    BufStage<kFHalf, kDK, kFNT> tq;
+    BufStage<kFHalf, kDV, kFNT> td;
+    {
+        BufStage<C, kDK, kFNT> tk;
+        BufStage<C, kDV, kFNT> tv;
+        BufStage<kDK, kDV, kFNT> ts;
+        tk.load(kb, tokK, ceff, tid);
+        tv.load(vb, tokV, ceff, tid);
+        ts.load(static_cast<const bf16*>(a.sbar) + snap, kDV, kDK, tid);
+        tq.load(qb, tokK, ceff, tid);
+        td.load(db_, tokV, ceff, tid);
+        tk.template store<kLDK>(Ks, tid);
+        tv.template store<kLDV>(Vs, tid);
+        ts.template store<kLDV>(Xs, tid);
+        tq.template store<kLDK>(Qs, tid);
+        td.template store<kLDV>(Ds, tid);
+    }
+    // the second half's queries and output gradients, in registers meanwhile
+    if (kFHalf < ceff) {
+        tq.load(qb + (size_t)kFHalf * tokK, tokK, ceff - kFHalf, tid);
+        td.load(db_ + (size_t)kFHalf * tokV, tokV, ceff - kFHalf, tid);
+    }
+    __syncthreads();
+
+    const int jb = wave;
+    const float sc = a.scale;
+    f32x4 dKT[kDK / 16], dVT[kDV / 16];
+#pragma unroll
+    for (int d = 0; d < kDK / 16; ++d) dKT[d] = zero4();
+#pragma unroll
+    for (int c = 0; c < kDV / 16; ++c) dVT[c] = zero4();
+    float t4 = 0.f, t3 = 0.f;
+
+    // Intra-chunk terms of key block jb from the query pairs of the half at
+    // qt0 at or below the diagonal: Abar = (Q K^T) (.) D and dP = (dO V^T) (.) D
+    // blocks, then dV^T += dO-side products, dK^T += Q-side products.
+    auto key_terms = [&](int qt0) {
+        const int jl = jb * 16 + n;  // chunk-local key index of this lane's column
+#pragma unroll
+        for (int pr = 0; pr < kFHalf / 32; ++pr) {
+            if (qt0 + 32 * pr + 31 < jb * 16) continue;  // pair entirely above the diagonal (uniform)
+            f32x4 Ab[2], Pb[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ib = pr * 2 + u;      // block within the half
+                const int il0 = qt0 + ib * 16;  // chunk-local first query of the block
+                Ab[u] = zero4();
+                Pb[u] = zero4();
+                if (il0 + 15 < jb * 16) continue;  // block entirely above the diagonal (uniform)
+#pragma unroll
+                for (int p = 0; p < kDK / 32; ++p)
+                    Ab[u] = mfma(op_row8(Qs, kLDK, ib * 16 + n, 32 * p + 8 * g),
+                                 op_row8(Ks, kLDK, jb * 16 + n, 32 * p + 8 * g), Ab[u]);
+#pragma unroll
+                for (int p = 0; p < kDV / 32; ++p)
+                    Pb[u] = mfma(op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g),
+                                 op_row8(Vs, kLDV, jb * 16 + n, 32 * p + 8 * g), Pb[u]);
+                // Ab[u][r] = q_i . k_j, Pb[u][r] = do_i . v_j for i = il0 + 4g + r, j = jl
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int di = decay_index(il0 + 4 * g + r - jl);
+                    const float f = sc * pw[di];
+                    t4 = fmaf(dpw[di] * Ab[u][r], Pb[u][r], t4);
+                    Ab[u][r] *= f;
+                    Pb[u][r] *= f;
+                }
+            }
+            const bf16x8 ab = pack_acc(Ab[0], Ab[1]);
+            const bf16x8 pb = pack_acc(Pb[0], Pb[1]);
+#pragma unroll
+            for (int c = 0; c < kDV / 16; ++c) dVT[c] = mfma(op_col_pair(Ds, kLDV, 32 * pr, c * 16, n, g), ab, dVT[c]);
+#pragma unroll
+            for (int d = 0; d < kDK / 16; ++d) dKT[d] = mfma(op_col_pair(Qs, kLDK, 32 * pr, d * 16, n, g), pb, dKT[d]);
+        }
+    };
+    // dQ of query block ib of the half at qt0, stored:
+    //   dQ = scale (b_i Sbar do_i + sum_{j <= i} dP_ij k_j);
+    // scale b'_i q_i . (Sbar do_i) feeds dlam.
+    auto query_block = [&](int qt0, int ib) {
+        const int il = qt0 + ib * 16 + n;  // chunk-local query index of this lane's column
+        const float bi = pw[il + 2];       // lam^(il+1)
+        const float dbi = dpw[il + 2];     // (il+1) lam^il
+        f32x4 dQT[kDK / 16];
+#pragma unroll
+        for (int d = 0; d < kDK / 16; ++d) {
+            dQT[d] = zero4();
+#pragma unroll
+            for (int p = 0; p < kDV / 32; ++p)
+                dQT[d] = mfma(op_row8(Xs, kLDV, d * 16 + n, 32 * p + 8 * g),
+                              op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g), dQT[d]);
+            const f32x4 qi = load4<bf16>(Qs + (ib * 16 + n) * kLDK + d * 16 + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                t3 = fmaf(dbi * qi[r], dQT[d][r], t3);
+                dQT[d][r] *= sc * bi;
+            }
+        }
+#pragma unroll
+        for (int pr = 0; pr < C / 32; ++pr) {
+            if (32 * pr > qt0 + ib * 16 + 15) continue;  // pair entirely above the diagonal (uniform)
+            f32x4 Pt[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int kb2 = pr * 2 + u;
+                const int jl0 = kb2 * 16;  // chunk-local first key of the block
+                Pt[u] = zero4();
+                if (jl0 > qt0 + ib * 16 + 15) continue;  // block entirely above the diagonal (uniform)
+#pragma unroll
+                for (int p = 0; p < kDV / 32; ++p)
+                    Pt[u] = mfma(op_row8(Vs, kLDV, kb2 * 16 + n, 32 * p + 8 * g),
+                                 op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g), Pt[u]);
+                // Pt[u][r] = v_j . do_i for j = jl0 + 4g + r, i = il
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Pt[u][r] *= sc * pw[decay_index(il - (jl0 + 4 * g + r))];
+            }
+            const bf16x8 pt = pack_acc(Pt[0], Pt[1]);
+#pragma unroll
+            for (int d = 0; d < kDK / 16; ++d) dQT[d] = mfma(op_col_pair(Ks, kLDK, 32 * pr, d * 16, n, g), pt, dQT[d]);
+        }
+        if (il < ceff) {
+            bf16* dqr = static_cast<bf16*>(a.dq) + tok0 * kDK + (size_t)(t0 + il) * tokK;
+#pragma unroll
+            for (int d = 0; d < kDK / 16; ++d) store4<bf16>(dqr + d * 16 + 4 * g, dQT[d]);
+        }
+    };
+
+    // A: queries 0..63
+    if (wave < 4) key_terms(0);
+    else query_block(0, wave - 4);
+    // B: queries 64..127 (Gbar requested for C meanwhile)
+    BufStage<kDK, kDV, kFNT> tg;
+    if (C > kFHalf && kFHalf < ceff) {
+        __syncthreads();  // half 0 reads are done
+        tq.template store<kLDK>(Qs, tid);
+        td.template store<kLDV>(Ds, tid);
+        __syncthreads();
+        tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
+        if (wave >= 4) query_block(kFHalf, wave - 4);
+        key_terms(kFHalf);
+    } else {
+        tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
+    }
+    // C: inter-chunk terms.  dK^T[d][j] += c_j sum_c Gbar[d][c] v_j[c];
+    // dV^T[c][j] += c_j X[c][j], X = sum_d Gbar[d][c] k_j[d]; c'_j v_j . X_j feeds dlam.
+    __syncthreads();  // Sbar reads are done
+    tg.template store<kLDV>(Xs, tid);
+    __syncthreads();
+    int tid_v = threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int lane2 = tid_v % 64, n2 = lane2 % 16, g2 = lane2 / 16;
+    const int jl = jb * 16 + n2;
+    const float cj = pw[decay_index(ceff - 1 - jl)];
+    const float dcj = dpw[decay_index(ceff - 1 - jl)];
+    float t2 = 0.f;
+    if (jb < NKB) {
+#pragma unroll
+    for (int d = 0; d < kDK / 16; ++d) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int p = 0; p < kDV / 32; ++p)
+            x = mfma(op_row8(Xs, kLDV, d * 16 + n2, 32 * p + 8 * g2), op_row8(Vs, kLDV, jb * 16 + n2, 32 * p + 8 * g2), x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dKT[d][r] = fmaf(cj, x[r], dKT[d][r]);
+    }
+#pragma unroll
+    for (int c = 0; c < kDV / 16; ++c) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int p = 0; p < kDK / 32; ++p)
+            x = mfma(op_col8(Xs, kLDV, 32 * p, c * 16, n2, g2), op_row8(Ks, kLDK, jb * 16 + n2, 32 * p + 8 * g2), x);
+        const f32x4 vj = load4<bf16>(Vs + (jb * 16 + n2) * kLDV + c * 16 + 4 * g2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            t2 = fmaf(dcj * vj[r], x[r], t2);
+            dVT[c][r] = fmaf(cj, x[r], dVT[c][r]);
+        }
+    }
+    }
+
+    if (jl < ceff) {
+        bf16* dkr = static_cast<bf16*>(a.dk) + tok0 * kDK + (size_t)(t0 + jl) * tokK;
+        bf16* dvr = static_cast<bf16*>(a.dv) + tok0 * kDV + (size_t)(t0 + jl) * tokV;
+#pragma unroll
+        for (int d = 0; d < kDK / 16; ++d) store4<bf16>(dkr + d * 16 + 4 * g2, dKT[d]);
+#pragma unroll
+        for (int c = 0; c < kDV / 16; ++c) store4<bf16>(dvr + c * 16 + 4 * g2, dVT[c]);
+    }
+    // dlam partials: the key-side terms (t2 + scale t4) and the query-side term
+    // (scale t3), each summed over the waves in a fixed order
+    t2 = wave_sum(t2 + sc * t4);
+    t3 = wave_sum(sc * t3);
+    if (lane2 == 0) {
+        red[0][wave] = t2;
+        red[1][wave] = t3;
+    }
+    __syncthreads();
+    // slots kChainSlots + [0, NSUB): key side (here all in the first),
+    // + [NSUB, 2 NSUB): query side, as the two-kernel form lays them out
+    if (tid_v < 2 * NSUB) {
+        float s = 0.f;
+        if (tid_v % NSUB == 0)
+#pragma unroll
+            for (int w = 0; w < kFNW; ++w) s += red[tid_v / NSUB][w];
+        part[tid_v] = s;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipStream_t stream) {
     if (chunk != 128 && chunk != 64) return hipErrorInvalidValue;
     const unsigned tiles = (unsigned)ga.nc * (unsigned)(chunk / kST);
     if (chunk == 128) {
+        // one kernel for all three gradients (the two-kernel form moves about
+        // twice the bytes); GLA_GRAD_SPLIT=1 selects the two kernels (tests, sweeps)
+        const char* e = getenv("GLA_GRAD_SPLIT");
+        if (!(e && atoi(e) == 1)) {
+            hipLaunchKernelGGL(grad_fused_bf16<128>, dim3((unsigned)ga.nc, units), dim3(kFNT), 0, stream, ga);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL(grad_dkdv_bf16<128>, dim3(tiles, units), dim3(kNT), 0, stream, ga);
         if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
         hipLaunchKernelGGL(grad_dq_bf16<128>, dim3(tiles, units), dim3(kNT), 0, stream, ga);
     } else {
+        const char* e = getenv("GLA_GRAD_SPLIT");
+        if (!(e && atoi(e) == 1)) {
+            hipLaunchKernelGGL(grad_fused_bf16<64>, dim3((unsigned)ga.nc, units), dim3(kFNT), 0, stream, ga);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL(grad_dkdv_bf16<64>, dim3(tiles, units), dim3(kNT), 0, stream, ga);
         if (hipError_t err = hipGetLastError(); err != hipSuccess) return err;
         hipLaunchKernelGGL(grad_dq_bf16<64>, dim3(tiles, units), dim3(kNT), 0, stream, ga);
