@@ -417,6 +417,12 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     // blocks, then dV^T += dO-side products, dK^T += Q-side products.
     auto key_terms = [&](int qt0) {
         const int jl = jb * 16 + n;  // chunk-local key index of this lane's column
+        // this key block's row operands, read once for every query pair
+        bf16x8 kr[kDK / 32], vr[kDV / 32];
+#pragma unroll
+        for (int p = 0; p < kDK / 32; ++p) kr[p] = op_row8(Ks, kLDK, jb * 16 + n, 32 * p + 8 * g);
+#pragma unroll
+        for (int p = 0; p < kDV / 32; ++p) vr[p] = op_row8(Vs, kLDV, jb * 16 + n, 32 * p + 8 * g);
 #pragma unroll
         for (int pr = 0; pr < kFHalf / 32; ++pr) {
             if (qt0 + 32 * pr + 31 < jb * 16) continue;  // pair entirely above the diagonal (uniform)
@@ -430,12 +436,10 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
                 if (il0 + 15 < jb * 16) continue;  // block entirely above the diagonal (uniform)
 #pragma unroll
                 for (int p = 0; p < kDK / 32; ++p)
-                    Ab[u] = mfma(op_row8(Qs, kLDK, ib * 16 + n, 32 * p + 8 * g),
-                                 op_row8(Ks, kLDK, jb * 16 + n, 32 * p + 8 * g), Ab[u]);
+                    Ab[u] = mfma(op_row8(Qs, kLDK, ib * 16 + n, 32 * p + 8 * g), kr[p], Ab[u]);
 #pragma unroll
                 for (int p = 0; p < kDV / 32; ++p)
-                    Pb[u] = mfma(op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g),
-                                 op_row8(Vs, kLDV, jb * 16 + n, 32 * p + 8 * g), Pb[u]);
+                    Pb[u] = mfma(op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g), vr[p], Pb[u]);
                 // Ab[u][r] = q_i . k_j, Pb[u][r] = do_i . v_j for i = il0 + 4g + r, j = jl
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -461,14 +465,16 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         const int il = qt0 + ib * 16 + n;  // chunk-local query index of this lane's column
         const float bi = pw[il + 2];       // lam^(il+1)
         const float dbi = dpw[il + 2];     // (il+1) lam^il
+        // this query block's output-gradient row operands, read once
+        bf16x8 dr[kDV / 32];
+#pragma unroll
+        for (int p = 0; p < kDV / 32; ++p) dr[p] = op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g);
         f32x4 dQT[kDK / 16];
 #pragma unroll
         for (int d = 0; d < kDK / 16; ++d) {
             dQT[d] = zero4();
 #pragma unroll
-            for (int p = 0; p < kDV / 32; ++p)
-                dQT[d] = mfma(op_row8(Xs, kLDV, d * 16 + n, 32 * p + 8 * g),
-                              op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g), dQT[d]);
+            for (int p = 0; p < kDV / 32; ++p) dQT[d] = mfma(op_row8(Xs, kLDV, d * 16 + n, 32 * p + 8 * g), dr[p], dQT[d]);
             const f32x4 qi = load4<bf16>(Qs + (ib * 16 + n) * kLDK + d * 16 + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -487,9 +493,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
                 Pt[u] = zero4();
                 if (jl0 > qt0 + ib * 16 + 15) continue;  // block entirely above the diagonal (uniform)
 #pragma unroll
-                for (int p = 0; p < kDV / 32; ++p)
-                    Pt[u] = mfma(op_row8(Vs, kLDV, kb2 * 16 + n, 32 * p + 8 * g),
-                                 op_row8(Ds, kLDV, ib * 16 + n, 32 * p + 8 * g), Pt[u]);
+                for (int p = 0; p < kDV / 32; ++p) Pt[u] = mfma(op_row8(Vs, kLDV, kb2 * 16 + n, 32 * p + 8 * g), dr[p], Pt[u]);
                 // Pt[u][r] = v_j . do_i for j = jl0 + 4g + r, i = il
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Pt[u][r] *= sc * pw[decay_index(il - (jl0 + 4 * g + r))];
