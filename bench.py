@@ -426,16 +426,22 @@ def cpu_baseline_decode(gi, w, seed, budget_s=8.0):
 
 
 def counters_pass(torch, gla, gi, chunk):
-    """Fixed launch sequence for rocprofv3 --pmc: a 1 GiB device copy (calibration), then
+    """Fixed launch sequence for rocprofv3 --pmc: 3 training steps (mixer-train workload,
+    forward saving chunk states + backward), then a 1 GiB device copy (calibration), then
     3 forward calls and 3 decode launches on the bench workloads (decode at one layer)."""
     dev = torch.device("cuda:0")
+    ws = gi.workloads()
+    t = TrainLeg(gla, gi, torch, ws[2], 2, chunk)
+    for _ in range(3):
+        t()
+    torch.cuda.synchronize()
+    del t
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    ws = gi.workloads()
     f = FwdLeg(gla, gi, torch, ws[1], 1, chunk)
     for _ in range(3):
         f()
@@ -458,8 +464,8 @@ def ingest_counters(fetch_csv, write_csv):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         by = {}
         for r in rows:
-            by.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), 0.0)
-            by[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+            by.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), 0.0)
+            by[(int(r["Dispatch_Id"]), r["Kernel_Name"])] += float(r["Counter_Value"])
         return by
 
     out = {"src_digest": src_digest(), "kernels": {}}
@@ -467,19 +473,24 @@ def ingest_counters(fetch_csv, write_csv):
     vals = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         by = per_kernel(path, counter)
-        copies = [v for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
-        ref = max(copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
+        copies = [(d, v) for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
+        ref = max(v for d, v in copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
+        first_copy = min(d for d, v in copies if v >= 0.9 * ref)  # (other copies: torch's input casts)
         fac[counter] = (1 << 30) / (ref * 1024.0)
-        groups = {"fwd": ["fwd_bf16_kernel", "seg_scan", "fwd_chain_kernel", "fwd_out_kernel"],
-                  "decode": ["decode_kernel"]}
-        for key, pats in groups.items():
+        # the training steps run before the copies, the forward and decode calls after them
+        groups = {"fwd": (["fwd_bf16_kernel", "seg_scan", "fwd_chain_kernel", "fwd_out_kernel"], False),
+                  "decode": (["decode_kernel"], False), "grad": (["grad_fused_bf16"], True)}
+        for key, (pats, before) in groups.items():
             # per call: sum over the kernels one call launches, averaged over the 3 calls
-            tot = sum(v for (d, name), v in by.items() if any(pt in name for pt in pats))
-            vals.setdefault(key, {})[counter] = tot / 3.0 * 1024.0 * fac[counter]
+            sel = [(d, v) for (d, name), v in by.items() if any(pt in name for pt in pats)
+                   and (d < first_copy) == before]
+            vals.setdefault(key, {})[counter] = sum(v for d, v in sel) / 3.0 * 1024.0 * fac[counter]
+            vals[key]["dispatches"] = len(sel)
     for key, v in vals.items():
         out["kernels"][key] = {"src_digest": out["src_digest"], "fetch_bytes_per_launch": v["FETCH_SIZE"],
                                "write_bytes_per_launch": v["WRITE_SIZE"],
-                               "hbm_bytes_per_launch": v["FETCH_SIZE"] + v["WRITE_SIZE"]}
+                               "hbm_bytes_per_launch": v["FETCH_SIZE"] + v["WRITE_SIZE"],
+                               "dispatches_in_3_calls": v["dispatches"]}
     out["copy_calibration"] = {"fetch_factor": fac["FETCH_SIZE"], "write_factor": fac["WRITE_SIZE"]}
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
@@ -552,6 +563,12 @@ def main():
                "avg_step_us": t_avg * 1e6, "alg_bytes_per_step": tb, "alg_flops_per_step": tf,
                "hbm_gbs": tb / t_avg / 1e9, "hbm_frac": tb / t_avg / 1e9 / HBM_PEAK_GBS,
                "mfma_tflops": tf / t_avg / 1e12, "mfma_frac": tf / t_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        if C == args.chunk:
+            # the backward's gradient kernel: q, k, v, do and both chunk-state snapshots in,
+            # dq, dk, dv out, against its measured HBM traffic (rocprofv3 counters)
+            gb = (4 * w2.dk + 3 * w2.dv + 2 * w2.dk * w2.dv / C) * 2 * tleg.token_heads
+            leg["grad_kernel"] = {"kernel": f"grad_fused_bf16<{C}> (one workgroup per chunk and unit)",
+                                  "alg_bytes_per_call": gb, "traffic": stored_traffic("grad", gb)}
         del tleg
         torch.cuda.empty_cache()
         rleg = TrainLeg(gla, gi, torch, w2, 2, C, saved=False)
