@@ -20,7 +20,8 @@
 // operands are token-contracted and come from the LDS transpose read.  A
 // snapshot goes through an LDS staging tile so it leaves as coalesced 16-byte
 // row pieces; the reverse pass stages fp32 and takes the <Gbar, Sbar> product
-// from the fp32 values during that copy (one partial per wave and chunk).
+// from the fp32 values during that copy (one partial per wave and chunk), with
+// the forward snapshot's pieces requested a chunk ahead.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
@@ -105,6 +106,22 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
         ty.load(yb + (size_t)t * tokY, tokY, T - t, tid);
     };
     if (nchunks > 0) load_chunk(chunk_of(0), tid);
+    // (reverse emit) this thread's pieces of the chunk's forward snapshot for the
+    // <Gbar, Sbar> term, requested a chunk ahead: piece tid + k * kNT of 96 x 24
+    constexpr int NSP = kDK * (kDV / 8) / kNT;
+    static_assert(kDK * (kDV / 8) % kNT == 0, "snapshot pieces per thread");
+    bf16x8 sbv[STAGE32 ? NSP : 1];
+    auto load_sbar = [&](int c, int tid) {
+        if constexpr (STAGE32) {
+            const bf16* sb = static_cast<const bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV;
+#pragma unroll
+            for (int k = 0; k < NSP; ++k) {
+                const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
+                sbv[k] = *reinterpret_cast<const bf16x8*>(sb + row * kDV + col);
+            }
+        }
+    };
+    if (nchunks > 0) load_sbar(chunk_of(0), tid);
 
     for (int ci = 0; ci < nchunks; ++ci) {
         // lane-derived addresses are recomputed per chunk, not held across the loop
@@ -138,14 +155,14 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
             // Copy the snapshot out as 16-byte row pieces (96 rows x 24 pieces).
             bf16* snap = static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV;
             float dot = 0.f;
-            for (int pc = tid; pc < kDK * (kDV / 8); pc += kNT) {
-                const int row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
+#pragma unroll
+            for (int k = 0; k < NSP; ++k) {
+                const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
                 bf16x8 x;
                 if constexpr (STAGE32) {
                     const f32x4 lo = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col);
                     const f32x4 hi = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col + 4);
-                    const bf16x8 sb = *reinterpret_cast<const bf16x8*>(
-                        static_cast<const bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV + row * kDV + col);
+                    const bf16x8 sb = sbv[k];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         x[e] = to_bf16(lo[e]);
@@ -159,6 +176,7 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
                 *reinterpret_cast<bf16x8*>(snap + row * kDV + col) = x;
             }
             if constexpr (STAGE32) {
+                if (ci + 1 < nchunks) load_sbar(chunk_of(ci + 1), tid);  // the next chunk's pieces
                 dot = wave_sum(dot);
                 if (lane == 0) a.part[((size_t)bh * a.nc + c) * kNPart + wave] = (ceff == C ? dlamC : dlamTail) * dot;
             }
