@@ -238,7 +238,8 @@ int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv,
  * The forward (gla_fwd_chunked) followed by the epilogue above, with y in place
  * of o: y[b,t,h] = epilogue(q, k, v, o, g)[b,t,h] for the readout o the forward
  * defines (o itself is not stored).  For bf16 plans that run the tiled state
- * chain (128-token chunks, B*H <= 16, as at B = 1, H = 16) the epilogue is
+ * chain (128-token chunks, B*H <= 16 and at most 16 chunks, as at B = 1, H = 16,
+ * T = 2,048) the epilogue is
  * applied in the output kernel's store, on the fp32 readout; other plans run the
  * forward into y and the epilogue pass over y in place.
  *   g      [B][T][H][dv] (dtype) output-gate logits;   y  [B][T][H][dv] (dtype) output
