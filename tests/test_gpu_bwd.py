@@ -185,3 +185,59 @@ def test_saved_states_training_width_sampled():
                        dS_T=f64(x["dS"][sl]), scale=x["scale"])
         for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
             assert_close(f64(got[sl]), ref, "bf16", f"{name}[{bi}]")
+
+
+@pytest.mark.parametrize("chunk", [128, 64])
+def test_bwd_batch_position_invariant(chunk):
+    """Each (batch, head) unit's gradients are computed alone: permuting the batch
+    permutes dq, dk, dv and dS0 bit for bit (saved-state pair and recomputing form);
+    dlambda, a sum over the batch, agrees to fp32 rounding."""
+    w = gi.workloads()[1]
+    x = gi.fwd_inputs(w, DEV, 46 + chunk, B=4, T=650, with_do=True, with_dS=True, s0_var=0.01)
+    perm = torch.tensor([2, 0, 3, 1], device=DEV)
+    xp = {k: (v[perm].contiguous() if isinstance(v, torch.Tensor) and k != "lam" else v) for k, v in x.items()}
+    _say(f"bwd batch permutation B=4 T=650 C={chunk}")
+    outs = []
+    for y in (x, xp):
+        _, _, st = gla.fwd_chunked_states(y["q"], y["k"], y["v"], y["lam"], S0=y["S0"], scale=y["scale"], chunk=chunk)
+        outs.append(gla.bwd_chunked_states(y["q"], y["k"], y["v"], y["lam"], y["do"], st, S0=y["S0"],
+                                           dS_final=y["dS"], scale=y["scale"], chunk=chunk))
+        outs.append(gla.bwd_chunked(y["q"], y["k"], y["v"], y["lam"], y["do"], S0=y["S0"], dS_final=y["dS"],
+                                    scale=y["scale"], chunk=chunk))
+    torch.cuda.synchronize()
+    for base, permuted in ((outs[0], outs[2]), (outs[1], outs[3])):
+        for i, name in ((0, "dq"), (1, "dk"), (2, "dv"), (4, "dS0")):
+            assert torch.equal(permuted[i], base[i][perm]), f"{name} depends on batch position"
+        a, b = f64(base[3]), f64(permuted[3])
+        assert np.linalg.norm(a - b) <= 1e-6 * np.linalg.norm(a), "dlambda: batch order changed more than rounding"
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_fwd_bwd_shape_sweep(case):
+    """Seeded sweep of head counts, batch sizes, lengths (ragged and chunk-aligned),
+    chunk sizes and optional S0 / dS_T through the forward and the backward, against
+    the oracle: plans with one or many segments, the tiled chain, few units."""
+    rng = np.random.default_rng(9000 + case)
+    H = int(rng.choice([1, 3, 5, 16]))
+    B = int(rng.choice([1, 2, 3]))
+    chunk = int(rng.choice([64, 128]))
+    T = int(rng.choice([1, 63, 64, 129, 255, 384, 513, 777]))
+    s0 = 0.01 if rng.random() < 0.5 else None
+    lam = tuple(gi.laplace_lambdas(16))[:H] if H < 16 else tuple(gi.laplace_lambdas(16))
+    w1 = gi.workloads()[1]
+    w = gi.Workload(w1.name, B, T, H, 96, 192, chunk, "bf16", lam, w1.scale)
+    x = gi.fwd_inputs(w, DEV, 9100 + case, B=B, T=T, with_do=True, with_dS=rng.random() < 0.5, s0_var=s0)
+    _say(f"sweep case {case}: B={B} H={H} T={T} C={chunk} S0={s0 is not None} dS_T={'dS' in x}")
+    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+    dq, dk, dv, dl, dS0 = gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"],
+                                          dS_final=x.get("dS"), scale=x["scale"], chunk=chunk)
+    torch.cuda.synchronize()
+    S0r = None if x["S0"] is None else f64(x["S0"])
+    ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), S0=S0r, scale=x["scale"])
+    assert_close(f64(o), ro, "bf16", "o")
+    assert_close(f64(S), rS, "bf16", "S_final")
+    r = oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), f64(x["do"]), S0=S0r,
+                   dS_T=f64(x["dS"]) if "dS" in x else None, scale=x["scale"])
+    for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
+        assert_close(f64(got), ref, "bf16", name)
+    assert_close(f64(dl), r[3], "bf16", "dlambda", batch_axis=None)
