@@ -324,8 +324,21 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     nseg = nseg > p.nc && p.nc > 0 ? p.nc : nseg;
     p.seg_chunks = p.nc > 0 ? (p.nc + nseg - 1) / nseg : 0;
     p.nseg = p.nc > 0 ? (p.nc + p.seg_chunks - 1) / p.seg_chunks : 1;
-    // fp32 segment states; the bf16 path adds a bf16 copy of each start state
-    p.ws_bytes = (size_t)units * (p.nseg - 1) * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
+    // bf16: when the state-only prologue (one workgroup per unit and segment before
+    // the last) would occupy at most half the compute units, it runs over
+    // half-length sub-segments instead, the scan combining their states (B = 8,
+    // H = 16, T = 2,048: 256 workgroups of 4 chunks instead of 128 of 8).
+    p.psub = 1;
+    // (the scan holds at most kMaxSegments - 1 states per unit)
+    if (bf16_io && p.nseg > 1 && p.seg_chunks % 2 == 0 && units * (p.nseg - 1) * 2 <= num_cu &&
+        (p.nseg - 1) * 2 <= kMaxSegments - 1)
+        p.psub = 2;
+    if (const char* e = getenv("GLA_FWD_PSUB")) {  // tuning override (sweeps, tests)
+        if (atoi(e) == 1) p.psub = 1;
+    }
+    // fp32 segment states (psub per segment boundary); the bf16 path adds a bf16
+    // copy of each start state
+    p.ws_bytes = (size_t)units * (p.nseg - 1) * p.psub * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
     // bf16, short sequence: a tiled state chain can emit every chunk's start
     // state for one output workgroup per chunk.  Measured on gfx950 it beats the
     // segment split only for 128-token chunks, at most 16 (batch, head) units

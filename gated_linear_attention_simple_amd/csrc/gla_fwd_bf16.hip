@@ -303,7 +303,8 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                         Sacc[i][cb][r] = __builtin_bit_cast(
                             float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * sidx(i, cb, r), 0, 0));
         } else {
-            const size_t st = ((size_t)bh * (a.nseg - 1) + (seg - 1)) * kDK * kDV;
+            // (the scanned state at the segment's start: sub-segment boundary seg * psub)
+            const size_t st = ((size_t)bh * (a.nseg - 1) * a.psub + (seg * a.psub - 1)) * kDK * kDV;
             // A one-chunk segment only reads its start state as a bf16 MFMA
             // operand, unless it must also produce the final state.  The four
             // bf16 values stay packed in the first two registers for now.
@@ -1046,7 +1047,9 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     a.o = o;
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
-    a.Ub = static_cast<char*>(ws) + (size_t)B * H * (plan.nseg > 1 ? plan.nseg - 1 : 0) * kDK * kDV * sizeof(float);
+    a.Ub = static_cast<char*>(ws) +
+           (size_t)B * H * (plan.nseg > 1 ? plan.nseg - 1 : 0) * plan.psub * kDK * kDV * sizeof(float);
+    a.psub = plan.psub;
     a.sbar = sbar;
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
@@ -1070,13 +1073,19 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     }
     if (ep) return hipErrorNotSupported;   // the epilogue is fused into the chain form only
     if (plan.nseg > 1) {
-        hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, true>), dim3(plan.nseg - 1, units), dim3(F8<C, LDK, NCB>::NT),
-                           0, stream, a);
+        // state-only prologue over the psub (nseg - 1) sub-segments before the last
+        // segment, then the scan turns their local states into the states at every
+        // sub-segment boundary (fp32 whenever a segment has several chunks)
+        FwdArgs pa = a;
+        pa.nseg = (plan.nseg - 1) * plan.psub + 1;
+        pa.seg_chunks = plan.seg_chunks / plan.psub;
+        hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, true>), dim3(pa.nseg - 1, units), dim3(F8<C, LDK, NCB>::NT),
+                           0, stream, pa);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(seg_scan_frag_kernel<NCB>, dim3((kDK * kDV / 4 + 255) / 256, units), dim3(256), 0, stream,
-                           S0, a.U, static_cast<bf16*>(a.Ub), lambda, H, plan.nseg, plan.seg_chunks,
-                           plan.seg_chunks * C, S_final != nullptr ? 1 : 0);
+                           S0, a.U, static_cast<bf16*>(a.Ub), lambda, H, pa.nseg, plan.seg_chunks,
+                           pa.seg_chunks * C, S_final != nullptr ? 1 : 0);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

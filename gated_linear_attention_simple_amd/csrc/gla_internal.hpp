@@ -20,12 +20,14 @@ struct FwdArgs {
     void* Ub;          // bf16 copies of the start states (bf16 path, one-chunk segments), or null
     void* sbar;        // optional: every chunk's start state, [B*H][nc][DK][DV] in the input dtype
     int nseg, seg_chunks, nc;
+    int psub;          // segment states in U per segment boundary (sub-segment prologue), >= 1
 };
 
 struct FwdPlan {
     int nc;          // chunks in the sequence
     int nseg;        // sequence segments run in parallel
     int seg_chunks;  // chunks per segment (the last segment may hold fewer)
+    int psub;        // bf16 segments: the state-only prologue runs psub sub-segments per segment
     int chain;       // bf16 path: tiled state chain + per-chunk output instead of segments
     size_t ws_bytes; // segments: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path);
                      // chain: B*H*nc*dk*dv bf16 chunk start states

@@ -121,6 +121,38 @@ def test_chain_matches_one_chunk_segments_bitwise(ncb, chunk, T, s0, want_final,
         assert_close(b, rS, w.dtype, "S_final")
 
 
+@pytest.mark.parametrize("chunk,T,segs,s0", [(64, 1500, 2, 0.01), (128, 2048, 3, None), (128, 1000, 2, 0.01)])
+def test_prologue_sub_segments(chunk, T, segs, s0, monkeypatch):
+    """When the state-only prologue would fill at most half the compute units it runs
+    over half-length sub-segments and the scan combines their states: the start states
+    differ from one prologue workgroup per segment only by fp32 rounding, which can
+    flip the bf16 rounding of a state operand, so the outputs agree to rel L2 1e-3
+    (a tenth of the oracle tolerance); both meet the oracle."""
+    w = gi.workloads()[1]
+    monkeypatch.setenv("GLA_FWD_CHAIN", "0")
+    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(segs))
+    x = gi.fwd_inputs(w, DEV, 1700 + T + chunk, B=2, T=T, s0_var=s0)
+    _say(f"prologue sub-segments B=2 T={T} C={chunk} segments={segs}")
+    outs = []
+    for psub in ("1", "2"):
+        if psub == "1":
+            monkeypatch.setenv("GLA_FWD_PSUB", "1")
+        else:
+            monkeypatch.delenv("GLA_FWD_PSUB", raising=False)
+        outs.append(gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk))
+    torch.cuda.synchronize()
+    a, b = f64(outs[0][0]), f64(outs[1][0])
+    rel = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert rel <= 1e-3, f"o: prologue forms differ, rel L2 {rel:.3e}"
+    a, b = f64(outs[0][1]), f64(outs[1][1])
+    assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(a), "S_final: prologue forms disagree"
+    ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]),
+                        S0=None if x["S0"] is None else f64(x["S0"]), scale=x["scale"])
+    for o, S in outs:
+        assert_close(f64(o), ro, w.dtype, "o")
+        assert_close(f64(S), rS, w.dtype, "S_final")
+
+
 def test_train_batch_forward_chunk64_and_128():
     w = gi.workloads()[2]
     for chunk in (128, 64):
