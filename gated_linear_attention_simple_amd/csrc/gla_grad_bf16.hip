@@ -10,14 +10,17 @@
 //   T2 = sum_j c'_j v_j . (Gbar^T k_j),  T3 = scale sum_i b'_i q_i . (Sbar do_i),
 //   T4 = scale sum_{i>j} D'_ij (q_i . k_j)(do_i . v_j).
 //
-// One workgroup of 4 waves per (chunk, 64-token tile); wave w owns token block w
-// of the tile.  The chunk-state snapshot (Gbar or Sbar) is staged in LDS for the
-// inter-chunk terms and its space is then reused for the other operand tiles
-// of the intra-chunk terms, so a workgroup needs ~78 KB of LDS and two run per
-// CU; the first intra tile is loaded into registers during the inter-chunk
-// MFMAs, later ones during the previous tile's.  Decay factors lam^d and their
-// derivatives d lam^(d-1) come from per-workgroup tables indexed by d + 1
-// (index 0: above the diagonal, both 0).
+// Two forms.  grad_fused_bf16 (the default, below the other two) forms dQ, dK
+// and dV of a chunk in one workgroup from one set of operand tiles.  The
+// two-kernel form, grad_dkdv_bf16 then grad_dq_bf16, kept for comparison
+// (GLA_GRAD_SPLIT=1), runs one workgroup of 4 waves per (chunk, 64-token tile);
+// wave w owns token block w of the tile.  There the chunk-state snapshot (Gbar
+// or Sbar) is staged in LDS for the inter-chunk terms and its space is then
+// reused for the other operand tiles of the intra-chunk terms, so a workgroup
+// needs ~78 KB of LDS and two run per CU; the first intra tile is loaded into
+// registers during the inter-chunk MFMAs, later ones during the previous
+// tile's.  Decay factors lam^d and their derivatives d lam^(d-1) come from
+// per-workgroup tables indexed by d + 1 (index 0: above the diagonal, both 0).
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
