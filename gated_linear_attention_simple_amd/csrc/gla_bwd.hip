@@ -574,28 +574,27 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(
 }
 
 // dlam[h] = sum over batch, chunks and partial slots (chain slots [0, nchain),
-// gradient slots [kChainSlots, kChainSlots + ngrad)), in a fixed order (double).
+// gradient slots [kChainSlots, kChainSlots + ngrad)), in a fixed order (double):
+// thread t sums the (batch, chunk) rows t, t + 256, ... slot by slot, then the
+// threads' sums are combined by a fixed butterfly in each wave and the four
+// wave sums in order.
 __global__ __launch_bounds__(256) void dlambda_reduce_kernel(const float* __restrict__ part, int B, int H, int nc,
                                                              int nchain, int ngrad, float* __restrict__ dlambda) {
-    __shared__ double red[256];
+    __shared__ double red[4];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nslots = nchain + ngrad;
-    const long per_b = (long)nc * nslots;
     double s = 0.0;
-    for (long e = tid; e < (long)B * per_b; e += 256) {
-        const long bb = e / per_b, rest = e % per_b;
-        const long c = rest / nslots, k = rest % nslots;
-        const long slot = k < nchain ? k : kChainSlots + (k - nchain);
-        s += (double)part[(((size_t)bb * H + h) * nc + c) * kNPart + slot];
+    for (int p = tid; p < B * nc; p += 256) {
+        const int bb = p / nc, c = p % nc;
+        const float* row = part + (((size_t)bb * H + h) * nc + c) * kNPart;
+        for (int k = 0; k < nchain; ++k) s += (double)row[k];
+        for (int k = 0; k < ngrad; ++k) s += (double)row[kChainSlots + k];
     }
-    red[tid] = s;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (tid % 64 == 0) red[tid / 64] = s;
     __syncthreads();
-    for (int m = 128; m >= 1; m >>= 1) {
-        if (tid < m) red[tid] += red[tid + m];
-        __syncthreads();
-    }
-    if (tid == 0) dlambda[h] = (float)red[0];
+    if (tid == 0) dlambda[h] = (float)((red[0] + red[1]) + (red[2] + red[3]));
 }
 
 // T == 0: no tokens -- dS0 = dS_T (or 0), dlam = 0.
