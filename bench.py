@@ -70,10 +70,22 @@ CONV_DEC_BYTES_PER_ROW_CHANNEL = 2 + 2 + 4 * 3 + 4 * 4
 CONV_D = 3072
 
 
-def src_digest():
+# Sources whose kernels the counters of each group measure (with the shared headers and
+# the C ABI, which picks the launch plan): a change elsewhere leaves them valid.
+DIGEST_FILES = {
+    "fwd": ["gla_fwd.hip", "gla_fwd_bf16.hip"],
+    "decode": ["gla_decode.hip"],
+    "grad": ["gla_grad_bf16.hip", "gla_bwd.hip"],
+}
+DIGEST_SHARED = ["gla_api.hip", "gla_common.hpp", "gla_internal.hpp", "gla_tile.hpp"]
+
+
+def src_digest(group=None):
+    """sha256 prefix of the kernel sources a counter group depends on (all sources if None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_linear_attention_simple_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if group is None else sorted(DIGEST_FILES[group] + DIGEST_SHARED)
+    for fn in names:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
@@ -89,7 +101,7 @@ def stored_traffic(kernel: str, bytes_per_launch_alg: float):
     except (OSError, ValueError):
         return None
     rec = data.get("kernels", {}).get(kernel)
-    if not rec or rec.get("src_digest") != src_digest():
+    if not rec or rec.get("src_digest") != src_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -487,7 +499,7 @@ def ingest_counters(fetch_csv, write_csv):
             vals.setdefault(key, {})[counter] = sum(v for d, v in sel) / 3.0 * 1024.0 * fac[counter]
             vals[key]["dispatches"] = len(sel)
     for key, v in vals.items():
-        out["kernels"][key] = {"src_digest": out["src_digest"], "fetch_bytes_per_launch": v["FETCH_SIZE"],
+        out["kernels"][key] = {"src_digest": src_digest(key), "fetch_bytes_per_launch": v["FETCH_SIZE"],
                                "write_bytes_per_launch": v["WRITE_SIZE"],
                                "hbm_bytes_per_launch": v["FETCH_SIZE"] + v["WRITE_SIZE"],
                                "dispatches_in_3_calls": v["dispatches"]}
