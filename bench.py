@@ -623,6 +623,23 @@ def main():
             "ms_per_step": p_wall / K * 1e3, "avg_launch_us": p_avg * 1e6,
             "achieved": per_launch_bytes / p_avg / 1e9, "unit": "GB/s",
             "frac": per_launch_bytes / p_avg / 1e9 / HBM_PEAK_GBS}
+        # the rate depends on how far apart the pages of neighbouring rows lie, not on the
+        # indirection: the same pool with the batch in slot order, and with runs of 16 rows
+        # on consecutive pages (the runs themselves shuffled)
+        shuffled = dleg.slots.clone()
+        g = torch.Generator().manual_seed(4)
+        runs = torch.randperm(w4.B // 16, generator=g)
+        patterns = {"sorted": torch.arange(w4.B),
+                    "runs_of_16": (runs[:, None] * 16 + torch.arange(16)[None, :]).reshape(-1)}
+        result["decode"]["pool"]["slot_order"] = {}
+        for name, perm in patterns.items():
+            dleg.slots.copy_(perm.to(torch.int32))
+            s_wall, s_gpu = time_decode(torch, dleg, K, W)
+            s_avg = s_gpu / (K * w4.decode_layers)
+            result["decode"]["pool"]["slot_order"][name] = {
+                "avg_launch_us": s_avg * 1e6, "achieved": per_launch_bytes / s_avg / 1e9,
+                "frac": per_launch_bytes / s_avg / 1e9 / HBM_PEAK_GBS}
+        dleg.slots.copy_(shuffled)
         # the same steps with the mixer epilogue fused into the decode kernel
         dleg.use_pool, dleg.use_epi = False, True
         e_wall, e_gpu = time_decode(torch, dleg, K, W)

@@ -23,9 +23,11 @@
 // Launches (one stream):
 //   1-3  forward state pass: per-chunk start states Sbar_c (segment prologue,
 //        scan, emit pass -- the forward's segment scheme);
-//   4-6  reverse state pass: per-chunk Gbar_c, dS0 and the <Gbar, Sbar> term;
+//   4-6  reverse state pass: per-chunk Gbar_c and dS0 (in the fp32 path also
+//        the Lam' <Gbar, Sbar> term; the bf16 gradient kernels take it there);
 //   7    dK/dV per (chunk, 64-key tile), looping over the chunk's query tiles;
-//   8    dQ per (chunk, 64-query tile), looping over the chunk's key tiles;
+//   8    dQ per (chunk, 64-query tile), looping over the chunk's key tiles
+//        (bf16: one kernel per chunk forms all three, gla_grad_bf16.hip);
 //   9    deterministic sum of the dlam partials per head.
 // Snapshots are stored in the input dtype (they are MFMA operands); the chains
 // themselves accumulate in fp32 registers.
@@ -689,7 +691,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
         }
         if ((err = chain(false, true, nseg)) != hipSuccess) return err;
     }
-    // reverse chain: snapshots Gbar, dS0, <Gbar, Sbar> partials
+    // reverse chain: snapshots Gbar, dS0 (and, fp32 path, the <Gbar, Sbar> partials)
     s.x = q;
     s.y = d_o;
     s.xscale = scale;
@@ -734,7 +736,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     }
     if (dlambda) {
         hipLaunchKernelGGL(dlambda_reduce_kernel, dim3(H), dim3(256), 0, stream, part, B, H, plan.nc,
-                           BF ? kChainSlots : 1, 2 * GS::NSUB, dlambda);
+                           kChainSlots, 2 * GS::NSUB, dlambda);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;

@@ -6,8 +6,8 @@
 // gradient of the loss with respect to the state leaving it (Gbar_c):
 //   forward:  S <- lam^ceff S + K^T diag(c) V,                   c_j = lam^(ceff-1-j)
 //   reverse:  G <- lam^ceff G + Q^T diag(scale b) dO,            b_i = lam^(i+1)
-// plus, on the reverse emit pass, the chunk's term of dlam through lam^ceff:
-//   ceff lam^(ceff-1) <Gbar_c, Sbar_c>.
+// (the chunk's term of dlam through lam^ceff, ceff lam^(ceff-1) <Gbar_c, Sbar_c>,
+// is taken by the gradient kernel, which holds both snapshots).
 // LOCAL passes start from zero and write each segment's local result; EMIT
 // passes start from the scanned segment state and write, before each chunk's
 // update, the state as that chunk's bf16 snapshot.
@@ -18,10 +18,8 @@
 // registers; x (k or q, pre-scaled per row) and y (v or do) tiles are staged
 // row-major in LDS with buffer loads prefetched one chunk ahead; both MFMA
 // operands are token-contracted and come from the LDS transpose read.  A
-// snapshot goes through an LDS staging tile so it leaves as coalesced 16-byte
-// row pieces; the reverse pass stages fp32 and takes the <Gbar, Sbar> product
-// from the fp32 values during that copy (one partial per wave and chunk), with
-// the forward snapshot's pieces requested a chunk ahead.
+// snapshot goes through a bf16 LDS staging tile so it leaves as coalesced
+// 16-byte row pieces.
 #include "gla_common.hpp"
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
@@ -36,12 +34,9 @@ template <int C, bool REV, bool EMIT>
 __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     constexpr int NP = C / 32;
     constexpr int LDK = kDK + 8, LDV = kDV + 8;
-    constexpr bool STAGE32 = EMIT && REV;     // fp32 staging (the <Gbar, Sbar> term)
-    constexpr int LDS32 = kDV + 4;
     __shared__ __align__(16) bf16 Xs[C * LDK];
     __shared__ __align__(16) bf16 Ys[C * LDV];
-    __shared__ __align__(16) bf16 Sb[EMIT && !STAGE32 ? kDK * LDV : 8];
-    __shared__ __align__(16) float Sf[STAGE32 ? kDK * LDS32 : 4];
+    __shared__ __align__(16) bf16 Sb[EMIT ? kDK * LDV : 8];
     __shared__ __align__(16) float xc[2][C];  // row factors of x: full chunk, partial last chunk
 
     const int tid = threadIdx.x;
@@ -69,9 +64,6 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     }
     const float lamC = uniform_f32(pow_int(lam, C));
     const float lamTail = uniform_f32(pow_int(lam, ctail));
-    // d(lam^ceff)/dlam for the <Gbar, Sbar> term
-    const float dlamC = uniform_f32((float)C * pow_int(lam, C - 1));
-    const float dlamTail = uniform_f32(ctail > 0 ? (float)ctail * pow_int(lam, ctail - 1) : 0.f);
 
     const int tokX = H * kDK, tokY = H * kDV;
     const size_t tok0 = (size_t)b * T * H + hd;
@@ -106,22 +98,8 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
         ty.load(yb + (size_t)t * tokY, tokY, T - t, tid);
     };
     if (nchunks > 0) load_chunk(chunk_of(0), tid);
-    // (reverse emit) this thread's pieces of the chunk's forward snapshot for the
-    // <Gbar, Sbar> term, requested a chunk ahead: piece tid + k * kNT of 96 x 24
-    constexpr int NSP = kDK * (kDV / 8) / kNT;
+    constexpr int NSP = kDK * (kDV / 8) / kNT;   // snapshot pieces per thread
     static_assert(kDK * (kDV / 8) % kNT == 0, "snapshot pieces per thread");
-    bf16x8 sbv[STAGE32 ? NSP : 1];
-    auto load_sbar = [&](int c, int tid) {
-        if constexpr (STAGE32) {
-            const bf16* sb = static_cast<const bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV;
-#pragma unroll
-            for (int k = 0; k < NSP; ++k) {
-                const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
-                sbv[k] = *reinterpret_cast<const bf16x8*>(sb + row * kDV + col);
-            }
-        }
-    };
-    if (nchunks > 0) load_sbar(chunk_of(0), tid);
 
     for (int ci = 0; ci < nchunks; ++ci) {
         // lane-derived addresses are recomputed per chunk, not held across the loop
@@ -144,8 +122,7 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * (2 * i + h) + 4 * g + r, col = colbase + 16 * cb + n;
-                        if constexpr (STAGE32) Sf[row * LDS32 + col] = Sacc[i][cb][r];
-                        else Sb[row * LDV + col] = to_bf16(Sacc[i][cb][r]);
+                        Sb[row * LDV + col] = to_bf16(Sacc[i][cb][r]);
                     }
         }
         __syncthreads();
@@ -154,31 +131,10 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
         if constexpr (EMIT) {
             // Copy the snapshot out as 16-byte row pieces (96 rows x 24 pieces).
             bf16* snap = static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV;
-            float dot = 0.f;
 #pragma unroll
             for (int k = 0; k < NSP; ++k) {
                 const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
-                bf16x8 x;
-                if constexpr (STAGE32) {
-                    const f32x4 lo = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col);
-                    const f32x4 hi = *reinterpret_cast<const f32x4*>(Sf + row * LDS32 + col + 4);
-                    const bf16x8 sb = sbv[k];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[e] = to_bf16(lo[e]);
-                        x[e + 4] = to_bf16(hi[e]);
-                        dot = fmaf(lo[e], to_f32(sb[e]), dot);
-                        dot = fmaf(hi[e], to_f32(sb[e + 4]), dot);
-                    }
-                } else {
-                    x = *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col);
-                }
-                *reinterpret_cast<bf16x8*>(snap + row * kDV + col) = x;
-            }
-            if constexpr (STAGE32) {
-                if (ci + 1 < nchunks) load_sbar(chunk_of(ci + 1), tid);  // the next chunk's pieces
-                dot = wave_sum(dot);
-                if (lane == 0) a.part[((size_t)bh * a.nc + c) * kNPart + wave] = (ceff == C ? dlamC : dlamTail) * dot;
+                *reinterpret_cast<bf16x8*>(snap + row * kDV + col) = *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col);
             }
         }
 

@@ -8,7 +8,10 @@
 //   dQ = scale (dP K + diag(b) dO Sbar^T),
 // with Abar = (Q K^T) (.) D and dP = (dO V^T) (.) D, and the lam-derivative terms
 //   T2 = sum_j c'_j v_j . (Gbar^T k_j),  T3 = scale sum_i b'_i q_i . (Sbar do_i),
-//   T4 = scale sum_{i>j} D'_ij (q_i . k_j)(do_i . v_j).
+//   T4 = scale sum_{i>j} D'_ij (q_i . k_j)(do_i . v_j),
+// and the term through the chunk decay, T1 = ceff lam^(ceff-1) <Gbar, Sbar>,
+// from the two bf16 snapshots (each workgroup that stages one has the other's
+// pieces at hand; dlam slot 0).
 //
 // Two forms.  grad_fused_bf16 (the default, below the other two) forms dQ, dK
 // and dV of a chunk in one workgroup from one set of operand tiles.  The
@@ -48,6 +51,33 @@ __device__ __forceinline__ void fill_decay_tables(float* pw, float* dpw, float l
 }
 
 __device__ __forceinline__ int decay_index(int d) { return (d < -1 ? -1 : d) + 1; }
+
+// acc + sum of the 8 elementwise products of two 16-byte bf16 pieces, in fp32
+// (bf16 -> fp32 is exact: the element's bits in the upper half of a word).
+__device__ __forceinline__ float dot_piece(uint4 x, uint4 y, float acc) {
+    const unsigned xv[4] = {x.x, x.y, x.z, x.w}, yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__builtin_bit_cast(float, xv[j] << 16), __builtin_bit_cast(float, yv[j] << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, xv[j] & 0xffff0000u), __builtin_bit_cast(float, yv[j] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+// This thread's part of <G, S> for two dk x dv snapshots: G's pieces staged in
+// registers (BufStage<kDK, kDV, NT>), S's the same pieces of a row-major LDS
+// tile of row stride LD.
+template <int NT, int LD, typename Stage>
+__device__ __forceinline__ float snap_dot_lds(const Stage& gs, const bf16* S, int tid) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < Stage::PER; ++i) {
+        const int p = tid + NT * i;
+        if (Stage::NP % NT != 0 && p >= Stage::NP) continue;
+        acc = dot_piece(gs.r[i], *reinterpret_cast<const uint4*>(S + (p / Stage::KC) * LD + (p % Stage::KC) * 8), acc);
+    }
+    return acc;
+}
 
 // dK, dV of one 64-key tile (jt) of one chunk.
 template <int C>
@@ -214,7 +244,7 @@ __global__ __launch_bounds__(kNT, 2) void grad_dq_bf16(GradArgs a) {
     __shared__ __align__(16) bf16 Ds[kST * kLDV];
     __shared__ __align__(16) bf16 Un[kUnionElems];  // Sbar, then the key tile's k and v
     __shared__ float pw[C + 2], dpw[C + 2];
-    __shared__ float red[kNW];
+    __shared__ float red[kNW], redg[kNW];
     bf16* const Ss = Un;
     bf16* const Ks = Un;
     bf16* const Vs = Un + kST * kLDK;
@@ -251,6 +281,12 @@ __global__ __launch_bounds__(kNT, 2) void grad_dq_bf16(GradArgs a) {
         tq.template store<kLDK>(Qs, tid);
         td.template store<kLDV>(Ds, tid);
         ts.template store<kLDV>(Ss, tid);
+    }
+    float gsd = 0.f;  // first query tile: this thread's part of <Gbar, Sbar>
+    if (it == 0) {    // (against the Sbar pieces this thread has just put in LDS)
+        BufStage<kDK, kDV, kNT> tg;
+        tg.load(static_cast<const bf16*>(a.gbar) + ((size_t)bh * a.nc + cid) * kDK * kDV, kDV, kDK, tid);
+        gsd = snap_dot_lds<kNT, kLDV>(tg, Ss, tid);
     }
     // first key tile (jt = 0), in registers while the inter-chunk term runs
     BufStage<kST, kDK, kNT> tk;
@@ -327,9 +363,18 @@ __global__ __launch_bounds__(kNT, 2) void grad_dq_bf16(GradArgs a) {
         for (int d = 0; d < kDK / 16; ++d) store4<bf16>(dqr + d * 16 + 4 * g, dQT[d]);
     }
     t3 = wave_sum(sc * t3);
-    if (lane == 0) red[wave] = t3;
+    gsd = wave_sum(gsd);
+    if (lane == 0) {
+        red[wave] = t3;
+        redg[wave] = gsd;
+    }
     __syncthreads();
-    if (tid == 0) *part = (red[0] + red[1]) + (red[2] + red[3]);
+    if (tid == 0) {
+        *part = (red[0] + red[1]) + (red[2] + red[3]);
+        // the chunk's term through lam^ceff, ceff lam^(ceff-1) <Gbar, Sbar>, in slot 0
+        if (it == 0)
+            a.part[((size_t)bh * a.nc + cid) * kNPart] = dpw[ceff + 1] * ((redg[0] + redg[1]) + (redg[2] + redg[3]));
+    }
 }
 
 
@@ -362,7 +407,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     __shared__ __align__(16) bf16 Qs[kFHalf * kLDK];         // one half's queries
     __shared__ __align__(16) bf16 Ds[kFHalf * kLDV];         // and output gradients
     __shared__ float pw[C + 2], dpw[C + 2];
-    __shared__ float red[2][kFNW];
+    __shared__ float red[3][kFNW];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -528,6 +573,9 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     } else {
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
     }
+    // <Gbar, Sbar> (dlam through lam^ceff): this thread's Gbar pieces against
+    // the same pieces of Sbar, still in Xs
+    float gsd = snap_dot_lds<kFNT, kLDV>(tg, Xs, tid);
     // C: inter-chunk terms.  dK^T[d][j] += c_j sum_c Gbar[d][c] v_j[c];
     // dV^T[c][j] += c_j X[c][j], X = sum_d Gbar[d][c] k_j[d]; c'_j v_j . X_j feeds dlam.
     __syncthreads();  // Sbar reads are done
@@ -577,9 +625,11 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     // (scale t3), each summed over the waves in a fixed order
     t2 = wave_sum(t2 + sc * t4);
     t3 = wave_sum(sc * t3);
+    gsd = wave_sum(gsd);
     if (lane2 == 0) {
         red[0][wave] = t2;
         red[1][wave] = t3;
+        red[2][wave] = gsd;
     }
     __syncthreads();
     // slots kChainSlots + [0, NSUB): key side (here all in the first),
@@ -590,6 +640,12 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
 #pragma unroll
             for (int w = 0; w < kFNW; ++w) s += red[tid_v / NSUB][w];
         part[tid_v] = s;
+    } else if (tid_v == 2 * NSUB) {
+        // the chunk's term through lam^ceff, ceff lam^(ceff-1) <Gbar, Sbar>, in slot 0
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFNW; ++w) s += red[2][w];
+        a.part[((size_t)bh * a.nc + cid) * kNPart] = dpw[ceff + 1] * s;
     }
 }
 

@@ -59,11 +59,12 @@ constexpr int kMaxSegments = 16;
 hipError_t launch_seg_scan(const float* S0, float* U, const float* lambda, int H, int nseg, int seg_tokens,
                            int dkdv, unsigned units, hipStream_t stream);
 
-// dlam partials: [B*H][chunks][kNPart] fp32.  Slots [0, kChainSlots) hold the
-// chain term ceff lam^(ceff-1) <Gbar, Sbar> (one per chain wave; the fp32 chain
-// uses slot 0 only), slots [kChainSlots, kChainSlots + 2 * tiles) the gradient
-// kernels' terms.  All are summed per head in a fixed order.
-constexpr int kChainSlots = 12;
+// dlam partials: [B*H][chunks][kNPart] fp32.  Slot 0 holds the chunk's term
+// through lam^ceff, ceff lam^(ceff-1) <Gbar, Sbar> (from the fp32 path's reverse
+// chain, or from the bf16 gradient kernels, which hold both snapshots), slots
+// [kChainSlots, kChainSlots + 2 * tiles) the gradient kernels' other terms.
+// All are summed per head in a fixed order.
+constexpr int kChainSlots = 1;
 constexpr int kNPart = 16;
 
 struct StateArgs {
@@ -76,8 +77,8 @@ struct StateArgs {
     float* U;             // [BH][nseg-1][DK][DV]: segment-local states, then segment start states
     void* snap;           // [BH][NC][DK][DV] (E): per-chunk snapshots written by the emit pass
     float* S_out;         // reverse emit pass: dS0 (nullable)
-    const void* sbar;     // reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
-    float* part;          // reverse emit pass: dlam partials
+    const void* sbar;     // fp32 reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
+    float* part;          // fp32 reverse emit pass: dlam partials (slot 0)
     int nseg, seg_chunks, nc;
 };
 
