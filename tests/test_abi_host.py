@@ -240,3 +240,37 @@ def test_bwd_workspace_holds_both_snapshot_sets():
     need = lib.gla_bwd_workspace_bytes(1, B, T, H, 96, 192, C)
     snaps = 2 * B * H * (T // C) * 96 * 192 * 2
     assert snaps <= need <= snaps + 16 * 1024 * 1024
+
+
+def _excluded(rel, patterns):
+    """tar-style exclusion: './x' anchors at the top, other patterns match any path component run."""
+    import fnmatch
+    parts = rel.split("/")
+    for p in patterns:
+        if p.startswith("./"):
+            anchored = p[2:].rstrip("/")
+            if rel == anchored or rel.startswith(anchored + "/"):
+                return True
+        elif any(fnmatch.fnmatch("/".join(parts[i:]), p) or fnmatch.fnmatch(parts[i], p) for i in range(len(parts))):
+            return True
+    return False
+
+
+def test_gpu_snapshot_keeps_what_gpu_runs_load():
+    """Files the GPU tests, smoke() and bench.py read (the built library, its sources, the
+    committed counter summaries, the golden fixtures, the input generator) must not be
+    listed in .gpurunignore, or a GPU run would go without them."""
+    path = os.path.join(ROOT, ".gpurunignore")
+    if not os.path.exists(path):
+        return
+    patterns = [l.strip() for l in open(path) if l.strip() and not l.startswith("#")]
+    needed = ["gated_linear_attention_simple_amd/libgla.so", "profiles/counters.json", "bench.py",
+              "__graft_entry__.py", "gla_inputs.py", "include/gla.h"]
+    csrc = os.path.join(ROOT, "gated_linear_attention_simple_amd", "csrc")
+    needed += [f"gated_linear_attention_simple_amd/csrc/{f}" for f in os.listdir(csrc)]
+    needed += [f"tests/golden/{f}" for f in os.listdir(os.path.join(ROOT, "tests", "golden"))]
+    needed += [f"tests/{f}" for f in os.listdir(os.path.join(ROOT, "tests")) if f.endswith(".py")]
+    for rel in needed:
+        assert not _excluded(rel, patterns), f"{rel} is excluded from GPU runs by .gpurunignore"
+    # the check itself catches the pattern that excluded the counter summaries before
+    assert _excluded("profiles/counters.json", ["./profiles"])
