@@ -371,7 +371,26 @@ def pin_epilogue_zero_and_scale(orc, tol=1e-12):
     return bool(np.all(z == 0.0) and rel(y1, y2) < tol)
 
 
+def pin_epilogue_eps_inside_root(orc, tol=1e-12):
+    """Where eps enters the norm: with v = 0 and o = c on every channel, mean x^2 = c^2,
+    so y = silu(ln 3) c / sqrt(c^2 + eps) w = (3/4) ln 3 c / sqrt(c^2 + eps) w.  With
+    eps = 0.5 and |c| between 0.1 and 3 this differs from c / (|c| + eps) and from
+    sign(c) (eps outside the root, or dropped) by 3% or more on every row."""
+    rng, w, tier = _epi_case()
+    M, H, dk, dv = 5, 3, 5, 7
+    eps = 0.5
+    c = np.array([-2.5, 0.3, 1.0, -0.1, 3.0])
+    o = np.broadcast_to(c[:, None, None], (M, H, dv)).copy()
+    v = np.zeros((M, H, dv))
+    q, k = rng.normal(size=(M, H, dk)), rng.normal(size=(M, H, dk))
+    g = np.full((M, H, dv), np.log(3.0))
+    y = orc.epilogue(q, k, v, o, g, rng.normal(size=(H, dk)), w, tier, eps=eps)
+    want = (0.75 * np.log(3.0) * c / np.sqrt(c * c + eps))[:, None, None] * w[np.array(tier)][None]
+    return bool(rel(y, want) < tol)
+
+
 ALL_PINS.update({
+    "epilogue_eps_inside_root": pin_epilogue_eps_inside_root,
     "epilogue_constant_vector": pin_epilogue_constant_vector,
     "epilogue_gate_ratio": pin_epilogue_gate_ratio,
     "epilogue_zero_and_scale": pin_epilogue_zero_and_scale,

@@ -43,3 +43,23 @@ def assert_close(got, ref, dtype, name, batch_axis=0):
             if max_tol is not None:
                 assert m2 <= max_tol, f"{name}[{b}]: max err {m2:.3e}"
     return rel, mx
+
+
+def assert_close_groups(got, ref, groups, dtype, name):
+    """A per-head vector (dlambda) checked as a whole and on each group of heads on its
+    own (e.g. the lambda = 0, lambda = 1 and interior heads), so that components of a
+    small group are not hidden behind the large ones of another."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert_close(got, ref, dtype, name, batch_axis=None)
+    for label, idx in groups.items():
+        if len(idx):
+            assert_close(got[list(idx)], ref[list(idx)], dtype, f"{name}[{label}]", batch_axis=None)
+
+
+def lambda_groups(lams):
+    """Head indices with lambda == 0, lambda == 1 and the rest."""
+    lams = [float(x) for x in lams]
+    return {"zero": [h for h, x in enumerate(lams) if x == 0.0],
+            "one": [h for h, x in enumerate(lams) if x == 1.0],
+            "interior": [h for h, x in enumerate(lams) if 0.0 < x < 1.0]}

@@ -25,12 +25,13 @@ def test_decode_steps_match_oracle(dtype, dk, dv):
     w = gi.Workload(w.name, 7, 1, 16, dk, dv, 0, dtype, w.lambdas, dk ** -0.5, w.s0_var, 24)
     S = gi.decode_state(w, DEV, seed=9, layer=0)
     Sref = f64(S)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
     _say(f"decode {dtype} dk={dk} dv={dv} N=7, 6 steps")
     for step in range(6):
         d = gi.decode_token_inputs(w, DEV, seed=9, layer=0, step=step)
-        o = gla.decode_step(d["q"], d["k"], d["v"], torch.tensor(w.lambdas, device=DEV), S, scale=w.scale)
+        o = gla.decode_step(d["q"], d["k"], d["v"], lam, S, scale=w.scale)
         torch.cuda.synchronize()
-        ro, Sref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), np.array(w.lambdas), Sref, scale=w.scale)
+        ro, Sref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(lam), Sref, scale=w.scale)
         assert_close(f64(o), ro, dtype, f"o step {step}")
         assert_close(f64(S), Sref, dtype, f"S step {step}")
 
@@ -52,30 +53,35 @@ def test_decode_equals_forward_over_same_tokens():
 
 
 def test_decode_full_width_sampled():
-    """The bench's launch configuration (N=1,280 sequences, H=16, one layer's
-    1.5 GB page pool): 3 steps, checked on a seeded sample of 64 sequences."""
+    """The bench's launch configuration (N=1,280 sequences, H=16, 96x192 fp32 pages, one
+    1.5 GB pool slice per layer): 2 layers x 16 steps, the layers' launches interleaved
+    as in a decode step, every step checked on a seeded sample of 64 sequences per layer
+    against the oracle run from the regenerated initial pages."""
     w = gi.workloads()[4]
-    lam = torch.tensor(w.lambdas, device=DEV)
-    S = gi.decode_state(w, DEV, seed=4, layer=5)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
+    layers = (5, 17)
+    pools = {L: gi.decode_state(w, DEV, seed=4, layer=L) for L in layers}
     rng = np.random.default_rng(4)
-    idx = np.sort(rng.choice(w.B, 64, replace=False))
-    Sref = f64(S[idx])
-    _say("decode N=1280 full width, 3 steps")
-    for step in range(3):
-        d = gi.decode_token_inputs(w, DEV, seed=4, layer=5, step=step)
-        o = gla.decode_step(d["q"], d["k"], d["v"], lam, S, scale=w.scale)
-        torch.cuda.synchronize()
-        ro, Sref = oracle.decode(f64(d["q"][idx]), f64(d["k"][idx]), f64(d["v"][idx]), f64(lam), Sref,
-                                 scale=w.scale)
-        assert_close(f64(o[idx]), ro, "bf16", f"o step {step}")
-        assert_close(f64(S[idx]), Sref, "bf16", f"S step {step}")
-    del S
+    idx = {L: np.sort(rng.choice(w.B, 64, replace=False)) for L in layers}
+    Sref = {L: f64(pools[L][idx[L]]) for L in layers}
+    _say("decode N=1280 full width, 2 layers x 16 steps")
+    for step in range(16):
+        for L in layers:
+            d = gi.decode_token_inputs(w, DEV, seed=4, layer=L, step=step)
+            o = gla.decode_step(d["q"], d["k"], d["v"], lam, pools[L], scale=w.scale)
+            torch.cuda.synchronize()
+            i = idx[L]
+            ro, Sref[L] = oracle.decode(f64(d["q"][i]), f64(d["k"][i]), f64(d["v"][i]), f64(lam), Sref[L],
+                                        scale=w.scale)
+            assert_close(f64(o[i]), ro, "bf16", f"o layer {L} step {step}")
+            assert_close(f64(pools[L][i]), Sref[L], "bf16", f"S layer {L} step {step}")
+    del pools
     torch.cuda.empty_cache()
 
 
 def test_decode_batch_position_invariant():
     w = gi.workloads()[4]
-    lam = torch.tensor(w.lambdas, device=DEV)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
     S = gi.decode_state(w, DEV, seed=8, layer=0, N=9)
     d = gi.decode_token_inputs(w, DEV, seed=8, layer=0, step=0, N=9)
     S1 = S[4:5].clone()
@@ -98,7 +104,7 @@ def test_decode_pool_matches_oracle_with_padding(dtype):
     bit-identical."""
     w = gi.workloads()[4]
     w = gi.Workload(w.name, 23, 1, 16, 96, 192, 0, dtype, w.lambdas, 96 ** -0.5, w.s0_var, 24)
-    lam = torch.tensor(w.lambdas, device=DEV)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
     pool = gi.decode_state(w, DEV, seed=31, layer=0)                      # [23, H, dk, dv]
     untouched = pool.clone()
     rng = np.random.default_rng(31)
@@ -122,7 +128,7 @@ def test_decode_pool_matches_oracle_with_padding(dtype):
                 assert torch.count_nonzero(o[r]) == 0, f"padding row {r} step {step}"
                 continue
             ro, Sref[s] = oracle.decode(f64(d["q"][r:r + 1]), f64(d["k"][r:r + 1]), f64(d["v"][r:r + 1]),
-                                        np.array(w.lambdas), Sref[s][None], scale=w.scale)
+                                        f64(lam), Sref[s][None], scale=w.scale)
             Sref[s] = Sref[s][0]
             assert_close(f64(o[r:r + 1]), ro, dtype, f"o row {r} step {step}")
             assert_close(f64(pool[s]), Sref[s], dtype, f"page {s} step {step}")
@@ -135,7 +141,7 @@ def test_decode_pool_batch_invariant_bitwise():
     decoding it alone with gla_decode_step, whatever its row, its page slot and
     the padding around it."""
     w = gi.workloads()[4]
-    lam = torch.tensor(w.lambdas, device=DEV)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
     S = gi.decode_state(w, DEV, seed=33, layer=1, N=12)
     d = gi.decode_token_inputs(w, DEV, seed=33, layer=1, step=0, N=12)
     solo_S = S.clone()
@@ -189,11 +195,11 @@ def test_decode_page_decay_schedule():
     w = gi.Workload(w.name, 9, 1, 16, 96, 192, 0, "bf16", tuple(gi.page_lambdas(16)), 96 ** -0.5, w.s0_var, 24)
     S = gi.decode_state(w, DEV, seed=37, layer=0)
     Sref = f64(S)
-    lam = torch.tensor(w.lambdas, device=DEV)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
     for step in range(8):
         d = gi.decode_token_inputs(w, DEV, seed=37, layer=0, step=step)
         o = gla.decode_step(d["q"], d["k"], d["v"], lam, S, scale=w.scale)
         torch.cuda.synchronize()
-        ro, Sref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), np.array(w.lambdas), Sref, scale=w.scale)
+        ro, Sref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), f64(lam), Sref, scale=w.scale)
         assert_close(f64(o), ro, "bf16", f"o step {step}")
         assert_close(f64(S), Sref, "bf16", f"S step {step}")

@@ -136,6 +136,10 @@ MUTANTS = [
      "#define IDX_ST(b, h, H, DK, DV) (((size_t)(0) * (H) + (h)) * (size_t)(DK) * (DV))"),
     ("epi_gate_ignores_a", "z += qu[i] * (a ? a[(size_t)h * dk + i] : 0.0) * ku[i];", "z += qu[i] * ku[i];"),
     ("epi_norm_sum_not_mean", "const double inv = 1.0 / sqrt(ss / dv + eps);", "const double inv = 1.0 / sqrt(ss + eps);"),
+    ("epi_eps_outside_root", "const double inv = 1.0 / sqrt(ss / dv + eps);",
+     "const double inv = 1.0 / (sqrt(ss / dv) + eps);"),
+    ("epi_eps_dropped", "const double inv = 1.0 / sqrt(ss / dv + eps);",
+     "const double inv = ss > 0 ? 1.0 / sqrt(ss / dv) : 1.0 / sqrt(eps);"),
     ("epi_ungated_value", "x[c] = o[(size_t)u * dv + c] + s * v[(size_t)u * dv + c];",
      "x[c] = o[(size_t)u * dv + c] + v[(size_t)u * dv + c];"),
     ("epi_silu_is_identity", "y[(size_t)u * dv + c] = gc * sigmoid(gc) * x[c] * inv * wt[c];",
