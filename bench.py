@@ -4,15 +4,21 @@
 A step is one pass of the hot path on synthetic inputs already resident in HBM:
   * forward: one gla_fwd_chunked call on the Laplace-layer workload
     (B=1, H=16, T=2048, dk=96, dv=192, chunk 128, bf16, fp32 state);
-  * training step: gla_fwd_chunked + gla_bwd_chunked (dq, dk, dv, dlambda) on
-    the mixer-train workload (B=8, H=16, T=2048, do ~ N(0,1)), at chunk 128
-    (part of the step) and chunk 64 (timed alongside, reported separately);
+  * training step: gla_fwd_chunked_states + gla_bwd_chunked_states (dq, dk, dv,
+    dlambda) on the mixer-train workload (B=8, H=16, T=2048, do ~ N(0,1)), at
+    chunk 128 (part of the step) and chunk 64 (timed alongside);
   * decode: one decode step of the 1,280-sequence x 24-layer serving workload
     (24 gla_decode_step launches over a 36 GB fp32 state pool).
+Timed alongside (not part of the step): the 64k-token prefill (B=1, T=65,536,
+S0 given), the Laplace-layer forward from a cold cache, the decode variants,
+the mixer epilogue and the depth-wise conv.
 Each leg is timed over K steps after W warm-up steps, bracketed by device
 synchronisation; per-launch durations come from HIP events recorded on the
 stream the library launches on.  The headline value is forward tokens/s; the
 decode leg reports state-update GB/s and output tokens/s in the same line.
+MFMA fractions use the algorithmic (causal) FLOP count of each call: the work
+of the method's chunked form, not counting the blocks above the causal
+diagonal; the FLOPs the kernels issue are reported beside it.
 
 The CPU baseline leg times the fp64 oracle on a bounded sample of the same
 workloads (rank 0, one GPU only).  Usage: python bench.py [--gpus 1] [--steps K]
@@ -41,20 +47,35 @@ FWD_BYTES_PER_TOKEN_HEAD = {"bf16": 2 * 96 + 2 * 96 + 2 * 192 + 2 * 192, "f32": 
 
 
 def fwd_flops_per_token_head(C, dk=96, dv=192):
-    """Tile-issued MFMA work: 2C(dk+dv) for QK^T and AV over a full CxC tile, plus 4 dk dv for QS and K^T V."""
-    return 2 * C * (dk + dv) + 4 * dk * dv
+    """Algorithmic (causal) work of the chunked forward: QK^T and AV over the C(C+1)/2
+    (query, key) pairs at or below the diagonal, (C+1)(dk+dv) per token, plus 4 dk dv for
+    the inter-chunk readout Q S and the state update K^T V."""
+    return (C + 1) * (dk + dv) + 4 * dk * dv
+
+
+def fwd_issued_flops_per_token_head(C, dk=96, dv=192):
+    """MFMA work the forward's kernels issue: the 16x16 score blocks at or below the
+    diagonal (NIB(NIB+1)/2 of them, NIB = C/16) times dk, the 32-key pairs of the output
+    strips (C/32 strips, strip K spanning K+1 pairs) times dv, and Q S, K^T V in full."""
+    nib = C // 16
+    score = nib * (nib + 1) // 2 * 256 * dk * 2
+    out = sum(32 * 32 * (K + 1) * dv * 2 for K in range(C // 32))
+    return (score + out) // C + 4 * dk * dv
 
 
 def train_bytes_per_token_head(C, dk=96, dv=192):
-    """Forward I/O + backward I/O (q,k,v,do in; dq,dk,dv out, bf16) + one fp32
-    state write+read per chunk: 1152 + 1920 + 2*4*dk*dv/C."""
+    """Forward I/O + backward I/O (q,k,v,do in; dq,dk,dv out, bf16) + the per-chunk
+    state snapshots (bf16 start state written by the forward and read back, state
+    gradient written and read by the backward): 1152 + 1920 + 8 dk dv / C."""
     return 1152 + 1920 + 2 * 4 * dk * dv // C
 
 
 def train_flops_per_token_head(C, dk=96, dv=192):
-    """Tile-issued MFMA work of forward + backward: 2C(dk+dv) + 4dk dv for the
-    forward, 2C(2dv + 3dk) + 10 dk dv for the backward (state recompute included)."""
-    return fwd_flops_per_token_head(C, dk, dv) + 2 * C * (2 * dv + 3 * dk) + 10 * dk * dv
+    """Algorithmic work of the saved-state training pair: the forward's, plus the
+    backward's causal intra-chunk terms (dP, the recomputed scores, dQ, dK, dV:
+    (C+1)(3dk + 2dv)) and 8 dk dv for the inter-chunk terms of dQ, dK, dV and the
+    reverse state-gradient chain."""
+    return fwd_flops_per_token_head(C, dk, dv) + (C + 1) * (3 * dk + 2 * dv) + 8 * dk * dv
 
 
 DEC_BYTES_PER_SEQ_HEAD = 2 * 96 * 192 * 4 + 2 * (96 + 96 + 192 + 192)   # state R+W + q,k,v,o bf16
@@ -144,7 +165,7 @@ class FwdLeg:
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         self.fn = gla.load().gla_fwd_chunked
         self.head = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]),
-                     p(x["S0"]), ctypes.c_float(x["scale"]), p(self.o), p(self.S), p(self.ws),
+                     p(x["S0"]), ctypes.c_float(x["scale"]), p(self.o), p(self.S), None, p(self.ws),
                      ctypes.c_size_t(need))
         self.gla = gla
 
@@ -173,7 +194,7 @@ class TrainLeg:
         self.dq, self.dk, self.dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
         self.dl = torch.empty(H, dtype=torch.float32, device=dev)
         nf = gla.fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
-        nb = gla.bwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+        nb = gla.bwd_workspace_bytes(dt, B, T, H, dk, dv, chunk, saved_states=saved)
         self.wsf = torch.empty(max(nf, 16), dtype=torch.uint8, device=dev)
         self.wsb = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream()
@@ -186,16 +207,16 @@ class TrainLeg:
                                       device=dev)
             self.f, self.b = lib.gla_fwd_chunked_states, lib.gla_bwd_chunked_states
             self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
-                          p(self.o), None, p(self.states), p(self.wsf), ctypes.c_size_t(nf), st)
+                          p(self.o), None, p(self.states), None, p(self.wsf), ctypes.c_size_t(nf), st)
             self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
                           p(x["do"]), None, p(self.states), p(self.dq), p(self.dk), p(self.dv), p(self.dl), None,
-                          p(self.wsb), ctypes.c_size_t(nb), st)
+                          None, p(self.wsb), ctypes.c_size_t(nb), st)
         else:
             self.f, self.b = lib.gla_fwd_chunked, lib.gla_bwd_chunked
             self.fargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
-                          p(self.o), None, p(self.wsf), ctypes.c_size_t(nf), st)
+                          p(self.o), None, None, p(self.wsf), ctypes.c_size_t(nf), st)
             self.bargs = (dt, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None, sc,
-                          p(x["do"]), None, p(self.dq), p(self.dk), p(self.dv), p(self.dl), None, p(self.wsb),
+                          p(x["do"]), None, p(self.dq), p(self.dk), p(self.dv), p(self.dl), None, None, p(self.wsb),
                           ctypes.c_size_t(nb), st)
         self.gla = gla
 
@@ -258,7 +279,7 @@ class FwdEpilogueLeg:
         self.stream = torch.cuda.current_stream()
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         self.args = (gla.GLA_BF16, B, T, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), None,
-                     ctypes.c_float(x["scale"]), p(e["g"]), ctypes.byref(self.params), p(self.y), p(self.S),
+                     ctypes.c_float(x["scale"]), p(e["g"]), ctypes.byref(self.params), p(self.y), p(self.S), None,
                      p(self.ws), ctypes.c_size_t(need), ctypes.c_void_p(self.stream.cuda_stream))
         self.fn = gla.load().gla_fwd_chunked_epilogue
         self.gla = gla
@@ -376,6 +397,26 @@ def time_region(torch, stream, fn, K, W):
     return time.perf_counter() - t0, a.elapsed_time(b) * 1e-3
 
 
+def time_cold(torch, stream, fn, reps, W, flush_bytes=2 << 30):
+    """Each call alone, from a cold cache: before every call a fill kernel writes
+    flush_bytes (far beyond the 256 MB last-level cache) outside the timed region;
+    HIP events on the launch stream bracket the call only.  Returns the per-call
+    seconds (sorted)."""
+    for _ in range(W):
+        fn()
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        scratch.fill_(1.0)   # on torch's current stream, the launch stream here
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    return sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
+
+
 def time_decode(torch, leg, K, W):
     """K decode steps (each: one launch per layer) -> (wall, GPU region seconds)."""
     step = [0]
@@ -388,33 +429,73 @@ def time_decode(torch, leg, K, W):
     return time_region(torch, leg.stream, one_step, K, W)
 
 
-def cpu_baseline_fwd(gi, w, seed, budget_s=12.0):
-    """fp64 oracle on the same workload's inputs (drawn on the CPU), repeated until ~budget_s."""
-    import numpy as np
-    import torch
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _repeat(fn, budget_s, max_reps):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= max_reps:
+            return reps, el
+
+
+def cpu_baseline_fwd(gi, w, seed, budget_s=6.0):
+    """fp64 oracle on the Laplace layer's inputs (drawn on the CPU), repeated for ~budget_s."""
     import oracle
 
     x = gi.fwd_inputs(w, "cpu", seed)
     f = lambda t: t.double().numpy()
     q, k, v, lam = f(x["q"]), f(x["k"]), f(x["v"]), f(x["lam"])
-    threads = oracle.max_threads()
-    reps, t0 = 0, time.perf_counter()
-    while True:
+    reps, el = _repeat(lambda: oracle.fwd(q, k, v, lam, scale=x["scale"]), budget_s, 200)
+    return {"value": reps * w.B * w.T / el, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"fp64 per-token recurrence, the whole Laplace-layer forward (B=1, H=16, T=2048) x {reps} "
+                      f"repetitions in {el:.1f} s, OpenMP over the 16 (batch, head) units"}
+
+
+def cpu_baseline_train(gi, w, seed, budget_s=6.0):
+    """fp64 oracle forward + reverse mode on one of the training step's 8 sequences."""
+    import oracle
+
+    x = gi.fwd_inputs(w, "cpu", seed, B=1, with_do=True)
+    f = lambda t: t.double().numpy()
+    q, k, v, lam, do = f(x["q"]), f(x["k"]), f(x["v"]), f(x["lam"]), f(x["do"])
+
+    def step():
         oracle.fwd(q, k, v, lam, scale=x["scale"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 200:
-            break
-    tokens = reps * w.B * w.T
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 per-token recurrence, full Laplace-layer forward (B=1,H=16,T=2048) x {reps} "
-                      f"repetitions, {el:.1f} s, OpenMP over the 16 (batch, head) units"}
+        oracle.bwd(q, k, v, lam, do, scale=x["scale"])
+
+    reps, el = _repeat(step, budget_s, 50)
+    return {"value": reps * w.T / el, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"fp64 forward + reverse mode (dq, dk, dv, dlambda) of 1 of the 8 sequences "
+                      f"(H=16, T=2048) x {reps} in {el:.1f} s; tokens/s of that sample"}
 
 
-def cpu_baseline_decode(gi, w, seed, budget_s=8.0):
-    import numpy as np
+def cpu_baseline_long(gi, w, seed, tokens=8192, budget_s=5.0):
+    """fp64 oracle forward over the first `tokens` tokens of the 64k-token prefill."""
+    import oracle
 
+    x = gi.fwd_inputs(w, "cpu", seed, T=tokens)
+    f = lambda t: t.double().numpy()
+    q, k, v, lam, S0 = f(x["q"]), f(x["k"]), f(x["v"]), f(x["lam"]), f(x["S0"])
+    reps, el = _repeat(lambda: oracle.fwd(q, k, v, lam, S0=S0, scale=x["scale"]), budget_s, 100)
+    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"fp64 forward over the first {tokens} of the 65,536 tokens (B=1, H=16, S0 given) x {reps} "
+                      f"in {el:.1f} s (the recurrence's cost is linear in T)"}
+
+
+def cpu_baseline_decode(gi, w, seed, budget_s=5.0):
     import oracle
 
     n = 64
@@ -422,14 +503,14 @@ def cpu_baseline_decode(gi, w, seed, budget_s=8.0):
     S = gi.decode_state(w, "cpu", seed, 0, N=n).double().numpy()
     f = lambda t: t.double().numpy()
     q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
-    lam = np.array(w.lambdas)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        _, S = oracle.decode(q, k, v, lam, S, scale=w.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10000:
-            break
+    import torch
+    lam = torch.tensor(w.lambdas, dtype=torch.float32).double().numpy()   # the fp32 values the kernel reads
+    box = [S]
+
+    def step():
+        _, box[0] = oracle.decode(q, k, v, lam, box[0], scale=w.scale)
+
+    reps, el = _repeat(step, budget_s, 10000)
     seq_heads = reps * n * w.H
     return {"value": seq_heads * DEC_BYTES_PER_SEQ_HEAD / el / 1e9, "unit": "GB/s",
             "tokens_per_s": reps * n / el / w.decode_layers, "cores": oracle.max_threads(), "kind": "oracle",
@@ -538,8 +619,12 @@ def main():
     f_ms = f_wall / K * 1e3
     f_bytes = FWD_BYTES_PER_TOKEN_HEAD[w1.dtype] * fleg.token_heads
     f_flops = fwd_flops_per_token_head(args.chunk) * fleg.token_heads
+    f_issued = fwd_issued_flops_per_token_head(args.chunk) * fleg.token_heads
     f_ach = f_bytes / f_avg / 1e9
     fwd_tokens_per_s = K * fleg.tokens / f_wall
+    # the same call from a cold cache (each call alone after a 2 GiB write)
+    cold = time_cold(torch, fleg.stream, fleg, max(K // 2, 10), 2)
+    c_med, c_min = cold[len(cold) // 2], cold[0]
 
     result = {
         "metric": METRIC, "value": fwd_tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -555,9 +640,34 @@ def main():
                              "frac": f_ach / HBM_PEAK_GBS, "traffic": stored_traffic("fwd", f_bytes),
                              "kernel": "gla_fwd_chunked (tiled state chain + per-chunk output kernel)",
                              "alg_bytes_per_launch": f_bytes, "avg_launch_us": f_avg * 1e6,
+                             "alg_flops_per_launch": f_flops, "issued_flops_per_launch": f_issued,
                              "mfma_tflops": f_flops / f_avg / 1e12,
-                             "mfma_frac": f_flops / f_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}},
+                             "mfma_frac": f_flops / f_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+                "cold": {"timing": "each call alone after a 2 GiB write that evicts the caches; HIP events "
+                                   "around the call", "calls": len(cold), "median_us": c_med * 1e6,
+                         "min_us": c_min * 1e6, "tokens_per_s_median": fleg.tokens / c_med,
+                         "hbm_frac_median": f_bytes / c_med / 1e9 / HBM_PEAK_GBS}},
     }
+    del fleg
+    torch.cuda.empty_cache()
+
+    # ---- 64k-token prefill (B=1, T=65,536, S0 ~ N(0, 0.01)): one call per step
+    w3 = ws[3]
+    lleg = FwdLeg(gla, gi, torch, w3, 3, args.chunk)
+    l_wall, l_gpu = time_region(torch, lleg.stream, lleg, max(K // 4, 8), W)
+    l_avg = l_gpu / max(K // 4, 8)
+    l_bytes = FWD_BYTES_PER_TOKEN_HEAD[w3.dtype] * lleg.token_heads
+    l_flops = fwd_flops_per_token_head(args.chunk) * lleg.token_heads
+    result["long_prefill"] = {
+        "workload": "long-prefill-64k B=1 H=16 T=65536 dk=96 dv=192 C=%d bf16, S0 given" % args.chunk,
+        "calls": max(K // 4, 8), "avg_call_us": l_avg * 1e6, "tokens_per_s": lleg.tokens / l_avg,
+        "plan": gla.plan_resolve(gla.GLA_BF16, 1, w3.T, 16, 96, 192, args.chunk),
+        "roofline": {"bound": "hbm", "achieved": l_bytes / l_avg / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": l_bytes / l_avg / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": l_bytes,
+                     "alg_flops_per_launch": l_flops, "mfma_tflops": l_flops / l_avg / 1e12,
+                     "mfma_frac": l_flops / l_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}}
+    del lleg
+    torch.cuda.empty_cache()
 
     # ---- training-step legs (mixer-train workload, chunk 128 and 64)
     w2 = ws[2]
@@ -573,6 +683,7 @@ def main():
                "workload": f"mixer-train B=8 H=16 T=2048 dk=96 dv=192 C={C} bf16, fwd + bwd (dq,dk,dv,dlambda)",
                "calls": "gla_fwd_chunked_states + gla_bwd_chunked_states (chunk states saved by the forward)",
                "avg_step_us": t_avg * 1e6, "alg_bytes_per_step": tb, "alg_flops_per_step": tf,
+               "plan": gla.plan_resolve(gla.GLA_BF16, w2.B, w2.T, 16, 96, 192, C),
                "hbm_gbs": tb / t_avg / 1e9, "hbm_frac": tb / t_avg / 1e9 / HBM_PEAK_GBS,
                "mfma_tflops": tf / t_avg / 1e12, "mfma_frac": tf / t_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}
         if C == args.chunk:
@@ -701,8 +812,10 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        cb = cpu_baseline_fwd(gi, w1, 1)
-        result["cpu_baseline"] = cb
+        result["cpu_baseline"] = cpu_baseline_fwd(gi, w1, 1)
+        result["long_prefill"]["cpu_baseline"] = cpu_baseline_long(gi, ws[3], 3)
+        if result["train"]:
+            result["train"]["cpu_baseline"] = cpu_baseline_train(gi, w2, 2)
         if not args.no_decode:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(gi, ws[4], 4)
     print(json.dumps(result), flush=True)

@@ -1,9 +1,13 @@
-// gla_api.hip -- the extern "C" boundary of libgla (declared in include/gla.h).
+// gla_api.hip -- the extern "C" boundary of libgla (declared in include/gla.h
+// and, for the launch-plan controls, include/gla_plan.h).
 //
 // Host-side validation runs to completion before any HIP call, so an error
 // return enqueues nothing.  The library allocates nothing and keeps no state.
+// Every chunked forward and backward entry point goes through fwd_entry /
+// bwd_entry below with the optional features it exposes.
 #include "gla.h"
 #include "gla_internal.hpp"
+#include "gla_plan.h"
 
 #include <stdint.h>
 
@@ -20,6 +24,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 bool ok_dtype(int dt) { return dt == GLA_F32 || dt == GLA_BF16; }
+int esize(gla_dtype dt) { return dt == GLA_BF16 ? 2 : 4; }
 
 // Element counts must stay addressable; 2^40 elements is far above any HBM size.
 bool sane_count(long a, long b, long c, long d) {
@@ -27,7 +32,7 @@ bool sane_count(long a, long b, long c, long d) {
     return n < 1.0e12;
 }
 
-int fwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+gla_status fwd_check_shape(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
     if (!ok_dtype(dtype) || B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return GLA_ERR_INVALID_ARG;
     if (!sane_count(B, T, H, dk > dv ? dk : dv)) return GLA_ERR_INVALID_ARG;
     if (!gla::fwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
@@ -35,7 +40,7 @@ int fwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     return GLA_OK;
 }
 
-int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+gla_status bwd_check_shape(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
     if (!ok_dtype(dtype) || B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1 || chunk < 1) return GLA_ERR_INVALID_ARG;
     if (!sane_count(B, T, H, dk > dv ? dk : dv)) return GLA_ERR_INVALID_ARG;
     if (!gla::bwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
@@ -43,9 +48,38 @@ int bwd_check_shape(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
     return GLA_OK;
 }
 
+// Plan hint from the caller's gla_plan (NULL: all library choices).
+bool hint_of(const gla_plan* p, gla::PlanHint* h) {
+    *h = gla::PlanHint{0, -1, 0};
+    if (p == nullptr) return true;
+    if (p->segments < 0 || p->segments > gla::kMaxSegments || p->chain < -1 || p->chain > 1 || p->psub < 0 ||
+        p->psub > 1)
+        return false;
+    *h = gla::PlanHint{p->segments, p->chain, p->psub};
+    return true;
+}
+
+// One tensor's element strides; a zero field takes its packed value (token:
+// H * d, batch: T * token).  Token strides are multiples of 16 bytes, at least
+// a token's H * d elements and below 2^22; batch strides are multiples of 16
+// bytes.  An output's sequences must not overlap each other.
+bool resolve_stride(const gla_stride* s, int B, int T, int H, int D, int esz, bool output, gla::Tok* r) {
+    const long long row = (long long)H * D;
+    long long t = s ? s->token : 0, b = s ? s->batch : 0;
+    if (t < 0 || b < 0) return false;
+    if (t == 0) t = row;
+    if (b == 0) b = (long long)T * t;
+    const long long align = 16 / esz;
+    if (t < row || t % align != 0 || t >= gla::kMaxTokStride || b % align != 0) return false;
+    if (output && B > 1 && T > 0 && b < (long long)(T - 1) * t + row) return false;
+    r->t = (int)t;
+    r->b = b;
+    return true;
+}
+
 // Checks the epilogue parameters and fills the device-side argument block
 // (tier map by value).  Tensor pointers are checked by the callers.
-int epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::EpilogueArgs* a) {
+gla_status epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::EpilogueArgs* a) {
     if (ep == nullptr || !ok_ptr(ep->norm_w) || !ok_opt(ep->aug_a) || ep->head_tier == nullptr ||
         ep->n_tiers < 1 || ep->n_tiers > GLA_EPI_MAX_HEADS || !(ep->eps >= 0.f) || !std::isfinite(ep->eps))
         return GLA_ERR_INVALID_ARG;
@@ -61,21 +95,141 @@ int epi_fill(const gla_epilogue_params* ep, int H, int dk, int dv, gla::Epilogue
     a->norm_w = ep->norm_w;
     a->n_tiers = ep->n_tiers;
     a->eps = ep->eps;
+    a->rq = a->rk = H * dk;
+    a->rv = a->ro = a->rg = a->ry = H * dv;
     return GLA_OK;
 }
 
 static_assert(GLA_EPI_MAX_HEADS == gla::kEpiMaxHeads, "tier map capacity");
 
+gla_status device_status(hipError_t err) { return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
+
+// The chunked forward with its options: every chunk's start state saved to
+// `states` for the backward (with_states), and the fused epilogue (ep != NULL:
+// o receives y).
+gla_status fwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                     const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                     bool with_states, void* states, const void* g, const gla_epilogue_params* ep,
+                     const gla_strides* st, const gla_plan* plan_in, void* ws, size_t ws_bytes, hipStream_t stream) {
+    gla_status s = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (s != GLA_OK) return s;
+    const bool bf = dtype == GLA_BF16;
+    if (with_states && !gla::bwd_supported(bf, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+    if (with_states && ep) return GLA_ERR_UNSUPPORTED;
+    gla::PlanHint hint;
+    if (!hint_of(plan_in, &hint)) return GLA_ERR_INVALID_ARG;
+    gla::EpilogueArgs ea{};
+    if (ep && (s = epi_fill(ep, H, dk, dv, &ea)) != GLA_OK) return s;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda))) return GLA_ERR_INVALID_ARG;
+    if (T > 0 && with_states && !ok_ptr(states)) return GLA_ERR_INVALID_ARG;
+    if (T > 0 && ep && !ok_ptr(g)) return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
+    const int es = esize(dtype);
+    gla::FwdIO io{q, k, v, o, {}, {}, {}, {}};
+    gla::Tok sg{};
+    if (!resolve_stride(st ? &st->q : nullptr, B, T, H, dk, es, false, &io.sq) ||
+        !resolve_stride(st ? &st->k : nullptr, B, T, H, dk, es, false, &io.sk) ||
+        !resolve_stride(st ? &st->v : nullptr, B, T, H, dv, es, false, &io.sv) ||
+        !resolve_stride(st ? &st->o : nullptr, B, T, H, dv, es, true, &io.so) ||
+        (ep && !resolve_stride(st ? &st->g : nullptr, B, T, H, dv, es, false, &sg)))
+        return GLA_ERR_INVALID_ARG;
+    const gla::FwdPlan plan = gla::fwd_plan(bf, B, T, H, dk, dv, chunk, kPlanCUs, &hint);
+    if (plan.ws_bytes > 0 && T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    if (!ep)
+        return device_status(gla::launch_fwd(bf, plan, B, T, H, dk, dv, chunk, io, lambda, S0, scale, S_final,
+                                             T > 0 && with_states ? states : nullptr, ws, stream));
+    ea.sg = sg;
+    ea.g = g;
+    if (bf && T > 0) {
+        const hipError_t err = gla::launch_fwd_bf16_epilogue(plan, B, T, H, chunk, io, lambda, S0, scale, S_final, ws,
+                                                             ea, stream);
+        if (err == hipSuccess) return GLA_OK;
+        if (err != hipErrorNotSupported) return GLA_ERR_DEVICE;
+    }
+    // other plans: the readout into y, then the epilogue pass over y in place
+    hipError_t err = gla::launch_fwd(bf, plan, B, T, H, dk, dv, chunk, io, lambda, S0, scale, S_final, nullptr, ws,
+                                     stream);
+    if (err != hipSuccess || T == 0) return device_status(err);
+    ea.rq = io.sq.t;
+    ea.rk = io.sk.t;
+    ea.rv = io.sv.t;
+    ea.ro = ea.ry = io.so.t;
+    ea.rg = sg.t;
+    // rows equally spaced across the batch as well: one pass over all B * T rows
+    const bool uniform = io.sq.b == (long long)T * io.sq.t && io.sk.b == (long long)T * io.sk.t &&
+                         io.sv.b == (long long)T * io.sv.t && io.so.b == (long long)T * io.so.t &&
+                         sg.b == (long long)T * sg.t;
+    const int passes = uniform ? 1 : B;
+    ea.units = (long)(uniform ? B : 1) * T * H;
+    for (int b = 0; b < passes && err == hipSuccess; ++b) {
+        gla::EpilogueArgs eb = ea;
+        eb.q = static_cast<const char*>(q) + b * io.sq.b * es;
+        eb.k = static_cast<const char*>(k) + b * io.sk.b * es;
+        eb.v = static_cast<const char*>(v) + b * io.sv.b * es;
+        eb.o = static_cast<const char*>(o) + b * io.so.b * es;
+        eb.y = static_cast<char*>(o) + b * io.so.b * es;
+        eb.g = static_cast<const char*>(g) + b * sg.b * es;
+        err = gla::launch_epilogue(bf, dk, dv, eb, stream);
+    }
+    return device_status(err);
+}
+
+size_t fwd_ws_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const gla_plan* plan_in) {
+    gla::PlanHint hint;
+    if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK || !hint_of(plan_in, &hint)) return 0;
+    return gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs, &hint).ws_bytes;
+}
+
+// The chunked backward; `states` (nullable) are the chunk start states saved
+// by the forward.
+gla_status bwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                     const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
+                     const float* dS_final, const void* states, void* dq, void* dk_out, void* dv_out, float* dlambda,
+                     float* dS0, const gla_strides* st, const gla_plan* plan_in, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+    gla_status s = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (s != GLA_OK) return s;
+    gla::PlanHint hint;
+    if (!hint_of(plan_in, &hint)) return GLA_ERR_INVALID_ARG;
+    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(d_o) || !ok_ptr(dq) ||
+                  !ok_ptr(dk_out) || !ok_ptr(dv_out)))
+        return GLA_ERR_INVALID_ARG;
+    if (!ok_opt(S0) || !ok_opt(dS_final) || !ok_opt(dlambda) || !ok_opt(dS0) || !ok_opt(states))
+        return GLA_ERR_INVALID_ARG;
+    const int es = esize(dtype);
+    gla::BwdIO io{q, k, v, d_o, dq, dk_out, dv_out, {}, {}, {}, {}, {}, {}, {}};
+    if (!resolve_stride(st ? &st->q : nullptr, B, T, H, dk, es, false, &io.sq) ||
+        !resolve_stride(st ? &st->k : nullptr, B, T, H, dk, es, false, &io.sk) ||
+        !resolve_stride(st ? &st->v : nullptr, B, T, H, dv, es, false, &io.sv) ||
+        !resolve_stride(st ? &st->d_o : nullptr, B, T, H, dv, es, false, &io.sdo) ||
+        !resolve_stride(st ? &st->dq : nullptr, B, T, H, dk, es, true, &io.sdq) ||
+        !resolve_stride(st ? &st->dk : nullptr, B, T, H, dk, es, true, &io.sdk) ||
+        !resolve_stride(st ? &st->dv : nullptr, B, T, H, dv, es, true, &io.sdv))
+        return GLA_ERR_INVALID_ARG;
+    const bool saved = states != nullptr && T > 0;
+    const gla::BwdPlan plan = gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs, saved, &hint);
+    if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    return device_status(gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, io, lambda, S0, scale,
+                                         dS_final, dlambda, dS0, saved ? states : nullptr, ws, stream));
+}
+
+size_t bwd_ws_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, bool saved,
+                    const gla_plan* plan_in) {
+    gla::PlanHint hint;
+    if (bwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK || !hint_of(plan_in, &hint)) return 0;
+    return gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs, saved && T > 0, &hint).ws_bytes;
+}
+
 }  // namespace
 
 extern "C" {
 
-int gla_abi_version(void) { return 3; }
+int gla_abi_version(void) { return 4; }
 
-const char* gla_status_str(int status) {
+const char* gla_status_str(gla_status status) {
     switch (status) {
         case GLA_OK: return "GLA_OK";
-        case GLA_ERR_INVALID_ARG: return "GLA_ERR_INVALID_ARG: null/misaligned pointer or invalid size";
+        case GLA_ERR_INVALID_ARG: return "GLA_ERR_INVALID_ARG: null/misaligned pointer, invalid size or stride";
         case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: no kernel for this dtype/dk/dv/chunk";
         case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
         case GLA_ERR_DEVICE: return "GLA_ERR_DEVICE: HIP launch failed";
@@ -83,93 +237,120 @@ const char* gla_status_str(int status) {
     }
 }
 
-size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
-    if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
-    return gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
+size_t gla_fwd_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    return fwd_ws_bytes(dtype, B, T, H, dk, dv, chunk, nullptr);
 }
 
-int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                    const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                    void* ws, size_t ws_bytes, void* stream) {
-    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
-    if (st != GLA_OK) return st;
-    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda)))
-        return GLA_ERR_INVALID_ARG;
-    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
-    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
-    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
-                                           scale, o, S_final, nullptr, ws, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+gla_status gla_fwd_chunked(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                           const void* k, const void* v, const float* lambda, const float* S0, float scale, void* o,
+                           float* S_final, const gla_strides* st, void* ws, size_t ws_bytes, void* stream) {
+    return fwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, o, S_final, false, nullptr, nullptr,
+                     nullptr, st, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-size_t gla_bwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
-    if (bwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
-    return gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs).ws_bytes;
+size_t gla_bwd_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    return bwd_ws_bytes(dtype, B, T, H, dk, dv, chunk, false, nullptr);
 }
 
-int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                    const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
-                    const float* dS_final, void* dq, void* dk_out, void* dv_out, float* dlambda, float* dS0,
-                    void* ws, size_t ws_bytes, void* stream) {
-    int st = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
-    if (st != GLA_OK) return st;
-    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(d_o) || !ok_ptr(dq) ||
-                  !ok_ptr(dk_out) || !ok_ptr(dv_out)))
-        return GLA_ERR_INVALID_ARG;
-    if (!ok_opt(S0) || !ok_opt(dS_final) || !ok_opt(dlambda) || !ok_opt(dS0)) return GLA_ERR_INVALID_ARG;
-    const gla::BwdPlan plan = gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
-    if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    const hipError_t err =
-        gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final,
-                        dq, dk_out, dv_out, dlambda, dS0, nullptr, ws, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+gla_status gla_bwd_chunked(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                           const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                           const void* d_o, const float* dS_final, void* dq, void* dk_out, void* dv_out,
+                           float* dlambda, float* dS0, const gla_strides* st, void* ws, size_t ws_bytes,
+                           void* stream) {
+    return bwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final, nullptr, dq, dk_out,
+                     dv_out, dlambda, dS0, st, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-size_t gla_fwd_states_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk) {
+size_t gla_fwd_states_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
     if (fwd_check_shape(dtype, B, T, H, dk, dv, chunk) != GLA_OK) return 0;
     const size_t nc = ((size_t)T + chunk - 1) / chunk;
-    return (size_t)B * H * nc * dk * dv * (dtype == GLA_BF16 ? 2 : 4);
+    return (size_t)B * H * nc * dk * dv * esize(dtype);
 }
 
-int gla_fwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                           void* states, void* ws, size_t ws_bytes, void* stream) {
-    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
-    if (st != GLA_OK) return st;
-    if (!gla::bwd_supported(dtype == GLA_BF16, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
-    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda) || !ok_ptr(states)))
-        return GLA_ERR_INVALID_ARG;
-    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
-    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
-    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    const hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0,
-                                           scale, o, S_final, T > 0 ? states : nullptr, ws,
-                                           static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+gla_status gla_fwd_chunked_states(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                  const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                  void* o, float* S_final, void* states, const gla_strides* st, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    return fwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, o, S_final, true, states, nullptr,
+                     nullptr, st, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-int gla_bwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                           const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
-                           const float* dS_final, const void* states, void* dq, void* dk_out, void* dv_out,
-                           float* dlambda, float* dS0, void* ws, size_t ws_bytes, void* stream) {
-    int st = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
-    if (st != GLA_OK) return st;
-    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(d_o) || !ok_ptr(dq) ||
-                  !ok_ptr(dk_out) || !ok_ptr(dv_out) || !ok_ptr(states)))
-        return GLA_ERR_INVALID_ARG;
-    if (!ok_opt(S0) || !ok_opt(dS_final) || !ok_opt(dlambda) || !ok_opt(dS0)) return GLA_ERR_INVALID_ARG;
-    const gla::BwdPlan plan = gla::bwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
-    if (T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    const hipError_t err =
-        gla::launch_bwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final,
-                        dq, dk_out, dv_out, dlambda, dS0, T > 0 ? states : nullptr, ws,
-                        static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+size_t gla_bwd_states_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
+    return bwd_ws_bytes(dtype, B, T, H, dk, dv, chunk, true, nullptr);
 }
 
-int gla_decode_step(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                    const float* lambda, float* S, float scale, void* o, void* stream) {
+gla_status gla_bwd_chunked_states(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                  const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                  const void* d_o, const float* dS_final, const void* states, void* dq, void* dk_out,
+                                  void* dv_out, float* dlambda, float* dS0, const gla_strides* st, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    if (T > 0 && !ok_ptr(states)) {
+        const gla_status s = bwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+        return s != GLA_OK ? s : GLA_ERR_INVALID_ARG;
+    }
+    return bwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final, states, dq, dk_out,
+                     dv_out, dlambda, dS0, st, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+gla_status gla_fwd_chunked_epilogue(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                    const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                    const void* g, const gla_epilogue_params* ep, void* y, float* S_final,
+                                    const gla_strides* st, void* ws, size_t ws_bytes, void* stream) {
+    if (ep == nullptr) {
+        const gla_status s = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+        return s != GLA_OK ? s : GLA_ERR_INVALID_ARG;
+    }
+    return fwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, y, S_final, false, nullptr, g, ep, st,
+                     nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- launch-plan controls (gla_plan.h)
+
+gla_status gla_plan_resolve(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const gla_plan* hint_in,
+                            gla_plan* out) {
+    const gla_status s = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
+    if (s != GLA_OK) return s;
+    gla::PlanHint hint;
+    if (!hint_of(hint_in, &hint) || out == nullptr) return GLA_ERR_INVALID_ARG;
+    const gla::FwdPlan p = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs, &hint);
+    out->segments = p.nseg;
+    out->chain = p.chain;
+    out->psub = p.psub;
+    return GLA_OK;
+}
+
+size_t gla_fwd_workspace_bytes_planned(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                       const gla_plan* plan) {
+    return fwd_ws_bytes(dtype, B, T, H, dk, dv, chunk, plan);
+}
+
+size_t gla_bwd_workspace_bytes_planned(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                       int saved_states, const gla_plan* plan) {
+    return bwd_ws_bytes(dtype, B, T, H, dk, dv, chunk, saved_states != 0, plan);
+}
+
+gla_status gla_fwd_chunked_planned(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                   const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                   void* o, float* S_final, void* states, const void* g,
+                                   const gla_epilogue_params* ep, const gla_strides* st, const gla_plan* plan,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    return fwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, o, S_final, states != nullptr, states,
+                     g, ep, st, plan, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+gla_status gla_bwd_chunked_planned(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                   const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                   const void* d_o, const float* dS_final, const void* states, void* dq, void* dk_out,
+                                   void* dv_out, float* dlambda, float* dS0, const gla_strides* st,
+                                   const gla_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+    return bwd_entry(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, d_o, dS_final, states, dq, dk_out,
+                     dv_out, dlambda, dS0, st, plan, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- decode, epilogue, conv
+
+gla_status gla_decode_step(gla_dtype dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                           const float* lambda, float* S, float scale, void* o, void* stream) {
     if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
     if (!sane_count(N, H, dk, dv)) return GLA_ERR_INVALID_ARG;
     if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
@@ -177,14 +358,13 @@ int gla_decode_step(int dtype, int N, int H, int dk, int dv, const void* q, cons
     if (N == 0) return GLA_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(S) || !ok_ptr(o))
         return GLA_ERR_INVALID_ARG;
-    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, nullptr, 0,
-                                              scale, o, nullptr, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, nullptr, 0, scale, o,
+                                            nullptr, static_cast<hipStream_t>(stream)));
 }
 
-int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                         const float* lambda, float* pool, int P, const int* slots, float scale, void* o,
-                         void* stream) {
+gla_status gla_decode_step_pool(gla_dtype dtype, int N, int H, int dk, int dv, const void* q, const void* k,
+                                const void* v, const float* lambda, float* pool, int P, const int* slots, float scale,
+                                void* o, void* stream) {
     if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1 || P < 0) return GLA_ERR_INVALID_ARG;
     if (!sane_count(N, H, dk, dv) || !sane_count(P, H, dk, dv)) return GLA_ERR_INVALID_ARG;
     if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
@@ -193,17 +373,17 @@ int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv, const void* q,
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(lambda) || !ok_ptr(o) || !ok_ptr(slots))
         return GLA_ERR_INVALID_ARG;
     if (P > 0 && !ok_ptr(pool)) return GLA_ERR_INVALID_ARG;
-    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, pool, slots, P,
-                                              scale, o, nullptr, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, pool, slots, P, scale, o,
+                                            nullptr, static_cast<hipStream_t>(stream)));
 }
 
-int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                       const void* o, const void* g, const gla_epilogue_params* ep, void* y, void* stream) {
+gla_status gla_mixer_epilogue(gla_dtype dtype, int M, int H, int dk, int dv, const void* q, const void* k,
+                              const void* v, const void* o, const void* g, const gla_epilogue_params* ep, void* y,
+                              void* stream) {
     if (!ok_dtype(dtype) || M < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
     if (!sane_count(M, H, dk, dv)) return GLA_ERR_INVALID_ARG;
     gla::EpilogueArgs a;
-    const int st = epi_fill(ep, H, dk, dv, &a);
+    const gla_status st = epi_fill(ep, H, dk, dv, &a);
     if (st != GLA_OK) return st;
     if (M == 0) return GLA_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(g) || !ok_ptr(y))
@@ -215,55 +395,20 @@ int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv, const void* q, c
     a.o = o;
     a.g = g;
     a.y = y;
-    const hipError_t err = gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, static_cast<hipStream_t>(stream)));
 }
 
-int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                             const void* v, const float* lambda, const float* S0, float scale, const void* g,
-                             const gla_epilogue_params* ep, void* y, float* S_final, void* ws, size_t ws_bytes,
-                             void* stream) {
-    int st = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
-    if (st != GLA_OK) return st;
-    gla::EpilogueArgs a;
-    st = epi_fill(ep, H, dk, dv, &a);
-    if (st != GLA_OK) return st;
-    if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(y) || !ok_ptr(g) || !ok_ptr(lambda)))
-        return GLA_ERR_INVALID_ARG;
-    if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
-    const gla::FwdPlan plan = gla::fwd_plan(dtype == GLA_BF16, B, T, H, dk, dv, chunk, kPlanCUs);
-    if (plan.ws_bytes > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    a.units = (long)B * T * H;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = y;
-    a.g = g;
-    a.y = y;
-    if (dtype == GLA_BF16 && T > 0) {
-        const hipError_t err = gla::launch_fwd_bf16_epilogue(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, y,
-                                                             S_final, ws, a, s);
-        if (err == hipSuccess) return GLA_OK;
-        if (err != hipErrorNotSupported) return GLA_ERR_DEVICE;
-    }
-    // other plans: the readout into y, then the epilogue pass over y in place
-    hipError_t err = gla::launch_fwd(dtype == GLA_BF16, plan, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, y,
-                                     S_final, nullptr, ws, s);
-    if (err == hipSuccess && a.units > 0) err = gla::launch_epilogue(dtype == GLA_BF16, dk, dv, a, s);
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
-}
-
-int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                             const void* g, const float* lambda, float* S, int P, const int* slots, float scale,
-                             const gla_epilogue_params* ep, void* y, void* stream) {
+gla_status gla_decode_step_epilogue(gla_dtype dtype, int N, int H, int dk, int dv, const void* q, const void* k,
+                                    const void* v, const void* g, const float* lambda, float* S, int P,
+                                    const int* slots, float scale, const gla_epilogue_params* ep, void* y,
+                                    void* stream) {
     if (!ok_dtype(dtype) || N < 0 || H < 1 || dk < 1 || dv < 1) return GLA_ERR_INVALID_ARG;
     if (slots != nullptr && P < 0) return GLA_ERR_INVALID_ARG;
     if (!sane_count(N, H, dk, dv) || (slots != nullptr && !sane_count(P, H, dk, dv))) return GLA_ERR_INVALID_ARG;
     if (!gla::decode_supported(dk, dv)) return GLA_ERR_UNSUPPORTED;
     if ((long)N * H > 2147483647L) return GLA_ERR_UNSUPPORTED;
     gla::EpilogueArgs a;
-    const int st = epi_fill(ep, H, dk, dv, &a);
+    const gla_status st = epi_fill(ep, H, dk, dv, &a);
     if (st != GLA_OK) return st;
     if (N == 0) return GLA_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(lambda) || !ok_ptr(y) || !ok_opt(slots))
@@ -271,13 +416,12 @@ int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv, const void
     if ((slots == nullptr || P > 0) && !ok_ptr(S)) return GLA_ERR_INVALID_ARG;
     a.units = (long)N * H;
     a.g = g;
-    const hipError_t err = gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, slots,
-                                              slots ? P : 0, scale, y, &a, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_decode(dtype == GLA_BF16, N, H, dk, dv, q, k, v, lambda, S, slots,
+                                            slots ? P : 0, scale, y, &a, static_cast<hipStream_t>(stream)));
 }
 
-int gla_conv1d_silu(int dtype, int B, int T, int D, int K, const void* x, const float* w, const float* bias,
-                    const float* win_in, void* y, float* win_out, void* stream) {
+gla_status gla_conv1d_silu(gla_dtype dtype, int B, int T, int D, int K, const void* x, const float* w,
+                           const float* bias, const float* win_in, void* y, float* win_out, void* stream) {
     if (!ok_dtype(dtype) || B < 0 || T < 0 || D < 1 || K < 1) return GLA_ERR_INVALID_ARG;
     if (!sane_count(B, T, D, 1) || !sane_count(B, K, D, 1)) return GLA_ERR_INVALID_ARG;
     if (!gla::conv_supported(D, K)) return GLA_ERR_UNSUPPORTED;
@@ -295,12 +439,11 @@ int gla_conv1d_silu(int dtype, int B, int T, int D, int K, const void* x, const 
     a.win_in = win_in;
     a.y = y;
     a.win_out = win_out;
-    const hipError_t err = gla::launch_conv_prefill(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_conv_prefill(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream)));
 }
 
-int gla_conv1d_silu_decode(int dtype, int N, int D, int K, const void* x, const float* w, const float* bias,
-                           float* win, int P, const int* slots, void* y, void* stream) {
+gla_status gla_conv1d_silu_decode(gla_dtype dtype, int N, int D, int K, const void* x, const float* w,
+                                  const float* bias, float* win, int P, const int* slots, void* y, void* stream) {
     if (!ok_dtype(dtype) || N < 0 || D < 1 || K < 1) return GLA_ERR_INVALID_ARG;
     if (slots != nullptr && P < 0) return GLA_ERR_INVALID_ARG;
     if (!sane_count(N, K, D, 1) || (slots != nullptr && !sane_count(P, K, D, 1))) return GLA_ERR_INVALID_ARG;
@@ -320,8 +463,7 @@ int gla_conv1d_silu_decode(int dtype, int N, int D, int K, const void* x, const 
     a.win_out = win;
     a.slots = slots;
     a.P = slots ? P : 0;
-    const hipError_t err = gla::launch_conv_decode(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE;
+    return device_status(gla::launch_conv_decode(dtype == GLA_BF16, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

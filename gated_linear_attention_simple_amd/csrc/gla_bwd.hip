@@ -71,10 +71,9 @@ __global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
     const float lam = a.lambda[h];
     for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
 
-    const size_t tokX = (size_t)H * DK, tokY = (size_t)H * DV;
-    const size_t tok0 = (size_t)b * T * H + h;
-    const E* xb = static_cast<const E*>(a.x) + tok0 * DK;
-    const E* yb = static_cast<const E*>(a.y) + tok0 * DV;
+    const int tokX = a.sx.t, tokY = a.sy.t;
+    const E* xb = static_cast<const E*>(a.x) + b * a.sx.b + h * DK;
+    const E* yb = static_cast<const E*>(a.y) + b * a.sy.b + h * DV;
 
     f32x4 Sacc[NDB][NCB];  // Sacc[db][cb][r] = S[db*16 + 4g + r][colbase + cb*16 + n]
     auto sidx = [&](int db, int cb, int r) -> size_t {
@@ -282,12 +281,11 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dkdv_kerne
     const float lam = a.lambda[h];
     for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
 
-    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
-    const size_t tok0 = (size_t)b * T * H + h;
-    const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
-    const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
-    const E* vb = static_cast<const E*>(a.v) + tok0 * DV;
-    const E* db_ = static_cast<const E*>(a.d_o) + tok0 * DV;
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokD = a.sdo.t;
+    const E* qb = static_cast<const E*>(a.q) + b * a.sq.b + h * DK;
+    const E* kb = static_cast<const E*>(a.k) + b * a.sk.b + h * DK;
+    const E* vb = static_cast<const E*>(a.v) + b * a.sv.b + h * DV;
+    const E* db_ = static_cast<const E*>(a.d_o) + b * a.sdo.b + h * DV;
     {
         TileStage<E, ST, DK, NT> tk;
         TileStage<E, ST, DV, NT> tv;
@@ -355,8 +353,8 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dkdv_kerne
         {
             TileStage<E, ST, DK, NT> tq;
             TileStage<E, ST, DV, NT> td;
-            tq.load(qb + (size_t)(t0 + qt0) * tokK, tokK, ceff - qt0, tid);
-            td.load(db_ + (size_t)(t0 + qt0) * tokV, tokV, ceff - qt0, tid);
+            tq.load(qb + (size_t)(t0 + qt0) * tokQ, tokQ, ceff - qt0, tid);
+            td.load(db_ + (size_t)(t0 + qt0) * tokD, tokD, ceff - qt0, tid);
             __syncthreads();  // previous tile's reads of Qs / Ds are done
             tq.template store<LDK>(Qs, tid);
             td.template store<LDV>(Ds, tid);
@@ -423,8 +421,8 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dkdv_kerne
     }
 
     if (jl < ceff) {
-        E* dkr = static_cast<E*>(a.dk) + tok0 * DK + (size_t)(t0 + jl) * tokK;
-        E* dvr = static_cast<E*>(a.dv) + tok0 * DV + (size_t)(t0 + jl) * tokV;
+        E* dkr = static_cast<E*>(a.dk) + b * a.sdk.b + (size_t)(t0 + jl) * a.sdk.t + h * DK;
+        E* dvr = static_cast<E*>(a.dv) + b * a.sdv.b + (size_t)(t0 + jl) * a.sdv.t + h * DV;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) store4<E>(dkr + d * 16 + 4 * g, dKT[d]);
 #pragma unroll
@@ -464,18 +462,17 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(
     const float lam = a.lambda[h];
     for (int i = tid; i <= C; i += NT) pw[i] = pow_int(lam, i);
 
-    const size_t tokK = (size_t)H * DK, tokV = (size_t)H * DV;
-    const size_t tok0 = (size_t)b * T * H + h;
-    const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
-    const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
-    const E* vb = static_cast<const E*>(a.v) + tok0 * DV;
-    const E* db_ = static_cast<const E*>(a.d_o) + tok0 * DV;
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokD = a.sdo.t;
+    const E* qb = static_cast<const E*>(a.q) + b * a.sq.b + h * DK;
+    const E* kb = static_cast<const E*>(a.k) + b * a.sk.b + h * DK;
+    const E* vb = static_cast<const E*>(a.v) + b * a.sv.b + h * DV;
+    const E* db_ = static_cast<const E*>(a.d_o) + b * a.sdo.b + h * DV;
     {
         TileStage<E, ST, DK, NT> tq;
         TileStage<E, ST, DV, NT> td;
         TileStage<E, DK, DV, NT> ts;
-        tq.load(qb + (size_t)(t0 + qt0) * tokK, tokK, ceff - qt0, tid);
-        td.load(db_ + (size_t)(t0 + qt0) * tokV, tokV, ceff - qt0, tid);
+        tq.load(qb + (size_t)(t0 + qt0) * tokQ, tokQ, ceff - qt0, tid);
+        td.load(db_ + (size_t)(t0 + qt0) * tokD, tokD, ceff - qt0, tid);
         ts.load(static_cast<const E*>(a.sbar) + ((size_t)bh * a.nc + cid) * DK * DV, DV, DK, tid);
         tq.template store<LDK>(Qs, tid);
         td.template store<LDV>(Ds, tid);
@@ -568,7 +565,7 @@ __global__ __launch_bounds__((GradShape<E, DK, DV, C>::NT)) void grad_dq_kernel(
     }
 
     if (il < ceff) {
-        E* dqr = static_cast<E*>(a.dq) + tok0 * DK + (size_t)(t0 + il) * tokK;
+        E* dqr = static_cast<E*>(a.dq) + b * a.sdq.b + (size_t)(t0 + il) * a.sdq.t + h * DK;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) store4<E>(dqr + d * 16 + 4 * g, dQT[d]);
     }
@@ -617,33 +614,42 @@ bool bwd_supported(bool bf16_io, int dk, int dv, int chunk) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
+BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu, bool saved,
+                 const PlanHint* hint) {
     BwdPlan p{};
-    const FwdPlan f = fwd_plan(bf16_io, B, T, H, dk, dv, chunk, num_cu);
+    const FwdPlan f = fwd_plan(bf16_io, B, T, H, dk, dv, chunk, num_cu, hint);
     p.nc = f.nc;
     p.nseg = f.nseg;
     p.seg_chunks = f.seg_chunks;
+    p.saved = saved;
     const size_t units = (size_t)B * H;
     const size_t esz = bf16_io ? 2 : 4;
     p.snap_bytes = align256(units * p.nc * dk * dv * esz);
     p.u_bytes = align256(units * (p.nseg - 1) * dk * dv * sizeof(float));
     p.part_bytes = align256(units * (p.nc > 0 ? p.nc : 1) * kNPart * sizeof(float));
-    p.ws_bytes = 2 * p.snap_bytes + p.u_bytes + p.part_bytes;
+    // state gradients, (unless the forward saved them) states, segment states, partials
+    p.ws_bytes = (saved ? 1 : 2) * p.snap_bytes + p.u_bytes + p.part_bytes;
     return p;
 }
 
 template <typename E, int DK, int DV, int C>
-static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const void* q, const void* k,
-                               const void* v, const float* lambda, const float* S0, float scale, const void* d_o,
-                               const float* dST, void* dq, void* dk, void* dv, float* dlambda, float* dS0,
+static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const BwdIO& io, const float* lambda,
+                               const float* S0, float scale, const float* dST, float* dlambda, float* dS0,
                                const void* sbar_in, void* ws, hipStream_t stream) {
     constexpr int NW = DV / 16 >= 4 ? 4 : DV / 16;
     constexpr int dkdv = DK * DV;
+    // workspace: Gbar snapshots, Sbar snapshots (unless saved by the forward),
+    // segment states, dlambda partials
     char* w = static_cast<char*>(ws);
-    void* sbar = sbar_in ? const_cast<void*>(sbar_in) : w;
-    void* gbar = w + plan.snap_bytes;
-    float* U = reinterpret_cast<float*>(w + 2 * plan.snap_bytes);
-    float* part = reinterpret_cast<float*>(w + 2 * plan.snap_bytes + plan.u_bytes);
+    void* gbar = w;
+    char* rest = w + plan.snap_bytes;
+    void* sbar = const_cast<void*>(sbar_in);
+    if (!plan.saved) {
+        sbar = rest;
+        rest += plan.snap_bytes;
+    }
+    float* U = reinterpret_cast<float*>(rest);
+    float* part = reinterpret_cast<float*>(rest + plan.u_bytes);
     const unsigned units = (unsigned)B * H;
     const int nseg = plan.nseg;
     hipError_t err;
@@ -657,8 +663,10 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     s.seg_chunks = plan.seg_chunks;
     s.nc = plan.nc;
     // forward chain: snapshots Sbar
-    s.x = k;
-    s.y = v;
+    s.x = io.k;
+    s.y = io.v;
+    s.sx = io.sk;
+    s.sy = io.sv;
     s.xscale = 1.f;
     s.S_edge = S0;
     s.snap = sbar;
@@ -682,7 +690,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
             return hipGetLastError();
         }
     };
-    if (!sbar_in) {   // the forward's chunk start states were not saved: recompute them
+    if (!plan.saved) {   // the forward's chunk start states were not saved: recompute them
         if (nseg > 1) {
             if ((err = chain(false, false, nseg - 1)) != hipSuccess) return err;
             if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) !=
@@ -692,8 +700,10 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
         if ((err = chain(false, true, nseg)) != hipSuccess) return err;
     }
     // reverse chain: snapshots Gbar, dS0 (and, fp32 path, the <Gbar, Sbar> partials)
-    s.x = q;
-    s.y = d_o;
+    s.x = io.q;
+    s.y = io.d_o;
+    s.sx = io.sq;
+    s.sy = io.sdo;
     s.xscale = scale;
     s.S_edge = dST;
     s.snap = gbar;
@@ -711,17 +721,24 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
     GradArgs ga{};
     ga.T = T;
     ga.H = H;
-    ga.q = q;
-    ga.k = k;
-    ga.v = v;
-    ga.d_o = d_o;
+    ga.q = io.q;
+    ga.k = io.k;
+    ga.v = io.v;
+    ga.d_o = io.d_o;
+    ga.sq = io.sq;
+    ga.sk = io.sk;
+    ga.sv = io.sv;
+    ga.sdo = io.sdo;
+    ga.sdq = io.sdq;
+    ga.sdk = io.sdk;
+    ga.sdv = io.sdv;
     ga.lambda = lambda;
     ga.scale = scale;
     ga.sbar = sbar;
     ga.gbar = gbar;
-    ga.dq = dq;
-    ga.dk = dk;
-    ga.dv = dv;
+    ga.dq = io.dq;
+    ga.dk = io.dk;
+    ga.dv = io.dv;
     ga.part = part;
     ga.nc = plan.nc;
     using GS = GradShape<E, DK, DV, C>;
@@ -743,24 +760,24 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const v
 }
 
 hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
-                      const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
-                      const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
-                      float* dS0, const void* sbar_in, void* ws, hipStream_t stream) {
+                      const BwdIO& io, const float* lambda, const float* S0, float scale, const float* dST,
+                      float* dlambda, float* dS0, const void* sbar_in, void* ws, hipStream_t stream) {
     if (T == 0) {
         const size_t n = (size_t)B * H * dk * dv;
         hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
                            dim3(256), 0, stream, dST, dS0, n, dlambda, H);
         return hipGetLastError();
     }
+    if (plan.saved != (sbar_in != nullptr)) return hipErrorInvalidValue;
     if (bf16_io && dk == 96 && dv == 192 && chunk == 128)
-        return launch_bwd_t<bf16, 96, 192, 128>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                                dv_out, dlambda, dS0, sbar_in, ws, stream);
+        return launch_bwd_t<bf16, 96, 192, 128>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
+                                                stream);
     if (bf16_io && dk == 96 && dv == 192 && chunk == 64)
-        return launch_bwd_t<bf16, 96, 192, 64>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                               dv_out, dlambda, dS0, sbar_in, ws, stream);
+        return launch_bwd_t<bf16, 96, 192, 64>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
+                                               stream);
     if (!bf16_io && dk == 16 && dv == 32 && chunk == 32)
-        return launch_bwd_t<float, 16, 32, 32>(plan, B, T, H, q, k, v, lambda, S0, scale, d_o, dST, dq, dk_out,
-                                               dv_out, dlambda, dS0, sbar_in, ws, stream);
+        return launch_bwd_t<float, 16, 32, 32>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
+                                               stream);
     return hipErrorInvalidValue;
 }
 

@@ -65,10 +65,9 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     const float lamC = uniform_f32(pow_int(lam, C));
     const float lamTail = uniform_f32(pow_int(lam, ctail));
 
-    const int tokX = H * kDK, tokY = H * kDV;
-    const size_t tok0 = (size_t)b * T * H + hd;
-    const bf16* xb = static_cast<const bf16*>(a.x) + tok0 * kDK;
-    const bf16* yb = static_cast<const bf16*>(a.y) + tok0 * kDV;
+    const int tokX = a.sx.t, tokY = a.sy.t;
+    const bf16* xb = static_cast<const bf16*>(a.x) + b * a.sx.b + hd * kDK;
+    const bf16* yb = static_cast<const bf16*>(a.y) + b * a.sy.b + hd * kDV;
 
     // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n]
     f32x4 Sacc[3][kNCB];

@@ -9,11 +9,12 @@
 // gate; concatenating the heads is the [M][H][dv] layout itself.
 //
 // A group of LPU lanes per (row, head) (a power of two, 4..64): lane l holds the
-// 16-byte pieces l of the row's q, k (dk) and v, o, g, y (dv).  Every tensor
-// moves in 16-byte buffer loads and stores whose range is the workgroup's own
-// rows, so lanes past a row's end and rows past the last read zeros without a
-// branch, and all loads of a lane (the two parameter rows included) are issued
-// back to back before any arithmetic.  The two sums (gate logit, sum of
+// 16-byte pieces l of the row's q, k (dk) and v, o, g, y (dv).  Rows of each
+// tensor lie a row stride apart (H * d when packed), heads packed inside a row.
+// Every tensor moves in 16-byte buffer loads and stores whose range ends after
+// the batch's last (row, head), so lanes past a row's end and units past the
+// last read zeros without a branch, and all loads of a lane (the two parameter
+// rows included) are issued back to back before any arithmetic.  The two sums (gate logit, sum of
 // squares) are butterfly reductions inside the group, in a fixed order.
 // 2 dk + 4 dv elements move per (row, head) for ~10 dv flops: bound by HBM.
 #include "gla_common.hpp"
@@ -144,18 +145,43 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
         const long left = a.units - b * UPB;
         return left <= 0 ? 0 : left < UPB ? (int)left : UPB;
     };
+    // Where the units of batch b lie: the batch's first row r0; this lane's unit
+    // at row r0 + dr, head hu; the last unit at row r0 + drl, head hl.  A tensor
+    // of row stride R and width D is read from ptr + r0 R with the range
+    // (drl R + (hl + 1) D) elements, which ends after the batch's last unit (0
+    // for a batch past the end), and this lane's piece at (dr R + hu D) + lane VEC.
+    struct Pos {
+        long r0;
+        int dr, hu, drl, hl, nu;
+    };
+    auto where = [&](long b) {
+        Pos p;
+        const long u0 = b * UPB;
+        p.nu = batch_units(b);
+        p.r0 = u0 / a.H;
+        const long u = u0 + lu, ul = u0 + (p.nu > 0 ? p.nu - 1 : 0);
+        p.dr = (int)(u / a.H - p.r0);
+        p.hu = (int)(u % a.H);
+        p.drl = (int)(ul / a.H - p.r0);
+        p.hl = (int)(ul % a.H);
+        return p;
+    };
+    auto range_of = [&](const Pos& p, int R, int D) { return p.nu > 0 ? (p.drl * R + (p.hl + 1) * D) * ES : 0; };
+    auto off_of = [&](const Pos& p, int R, int D, int nl, int range) {
+        return lane < nl ? (p.dr * R + p.hu * D + lane * VEC) * ES : range;
+    };
+    auto row_load = [&](const Pos& p, const void* base, int R, int D, int nl) {
+        const int rg = range_of(p, R, D);
+        return ld16(rsrc(static_cast<const E*>(base) + p.r0 * R, rg), off_of(p, R, D, nl, rg));
+    };
     // row loads of batch b: q, k, v, o, g pieces (zeros past the rows' ends)
     auto load = [&](long b, uint4* r) {
-        const int nu = batch_units(b);
-        const int rk = nu * DK * ES, rv = nu * DV * ES;
-        const int ok = lane < NKL ? (lu * DK + lane * VEC) * ES : rk;
-        const int ov = lane < NVL ? (lu * DV + lane * VEC) * ES : rv;
-        const long u0 = b * UPB;
-        r[0] = ld16(rsrc(static_cast<const E*>(a.q) + u0 * DK, rk), ok);
-        r[1] = ld16(rsrc(static_cast<const E*>(a.k) + u0 * DK, rk), ok);
-        r[2] = ld16(rsrc(static_cast<const E*>(a.v) + u0 * DV, rv), ov);
-        r[3] = ld16(rsrc(static_cast<const E*>(a.o) + u0 * DV, rv), ov);
-        r[4] = ld16(rsrc(static_cast<const E*>(a.g) + u0 * DV, rv), ov);
+        const Pos p = where(b);
+        r[0] = row_load(p, a.q, a.rq, DK, NKL);
+        r[1] = row_load(p, a.k, a.rk, DK, NKL);
+        r[2] = row_load(p, a.v, a.rv, DV, NVL);
+        r[3] = row_load(p, a.o, a.ro, DV, NVL);
+        r[4] = row_load(p, a.g, a.rg, DV, NVL);
     };
     // one batch: issue the loads of batch b + G into `nxt`, then finish batch b from `cur`
     auto step = [&](long b, const uint4* cur, uint4* nxt) {
@@ -184,10 +210,11 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
         float y[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) y[e] = g[e] * fast_sigmoid(g[e]) * x[e] * inv * w[e];
-        const int rv = batch_units(b) * DV * ES;              // 0 past the end: the store is dropped
-        const int ov = lane < NVL ? (lu * DV + lane * VEC) * ES : rv;
+        const Pos p = where(b);                               // (past the end: range 0, store dropped)
+        const int ry = range_of(p, a.ry, DV);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Piece<E>::pack(y)),
-                                               rsrc(static_cast<E*>(a.y) + b * UPB * DV, rv), ov, 0, 0);
+                                               rsrc(static_cast<E*>(a.y) + p.r0 * a.ry, ry),
+                                               off_of(p, a.ry, DV, NVL, ry), 0, 0);
     };
 
     // two register sets in turn (no copies between them); the loop body is two

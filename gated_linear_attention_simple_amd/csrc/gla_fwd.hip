@@ -27,7 +27,6 @@
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
 
-#include <stdlib.h>
 
 namespace gla {
 
@@ -96,12 +95,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_f32_kernel(FwdArgs a) {
         hlane = pow_int(lam, n + 1);
     }
 
-    const int tokK = H * DK, tokV = H * DV;
-    const size_t tok0 = (size_t)b * T * H + h;
-    const E* qb = static_cast<const E*>(a.q) + tok0 * DK;
-    const E* kb = static_cast<const E*>(a.k) + tok0 * DK;
-    const E* vb = static_cast<const E*>(a.v) + tok0 * DV;
-    E* ob = static_cast<E*>(a.o) + tok0 * DV;
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokO = a.so.t;
+    const E* qb = static_cast<const E*>(a.q) + b * a.sq.b + h * DK;
+    const E* kb = static_cast<const E*>(a.k) + b * a.sk.b + h * DK;
+    const E* vb = static_cast<const E*>(a.v) + b * a.sv.b + h * DV;
+    E* ob = static_cast<E*>(a.o) + b * a.so.b + h * DV;
 
     // State registers: Sacc[db][cb][r] = S[db*16 + 4g + r][colbase + cb*16 + n].
     f32x4 Sacc[NDB][NCB];
@@ -136,7 +134,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_f32_kernel(FwdArgs a) {
                         for (int r = 0; r < 4; ++r) sb[sidx(db, cb, r)] = Sacc[db][cb][r];
             }
         }
-        if (!STATE_ONLY) tq.load(qb + (size_t)t0 * tokK, tokK, T - t0, tid);
+        if (!STATE_ONLY) tq.load(qb + (size_t)t0 * tokQ, tokQ, T - t0, tid);
         tk.load(kb + (size_t)t0 * tokK, tokK, T - t0, tid);
         tv.load(vb + (size_t)t0 * tokV, tokV, T - t0, tid);
         __syncthreads();  // previous chunk's LDS reads are done (and pw is visible)
@@ -222,7 +220,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_f32_kernel(FwdArgs a) {
                     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) OT[cb][r] *= a.scale;
-                        store4<E>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT[cb]);
+                        store4<E>(ob + (size_t)(t0 + irow) * tokO + colbase + cb * 16 + 4 * g, OT[cb]);
                     }
                 }
             }
@@ -308,7 +306,7 @@ bool fwd_supported(bool bf16_io, int dk, int dv, int chunk) {
            (dk == 16 && dv == 32 && chunk == 32 && !bf16_io);
 }
 
-FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu) {
+FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu, const PlanHint* hint) {
     FwdPlan p{};
     p.nc = T > 0 ? (T + chunk - 1) / chunk : 0;
     const long units = (long)B * H;
@@ -316,10 +314,7 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     // Split the sequence until the grid covers every compute unit (segments of
     // at least one chunk, at most kMaxSegments of them).
     while (units * nseg < num_cu && nseg * 2 <= p.nc && nseg < kMaxSegments) nseg *= 2;
-    if (const char* e = getenv("GLA_FWD_SEGMENTS")) {  // tuning override (sweeps, tests)
-        const int forced = atoi(e);
-        if (forced >= 1) nseg = forced < kMaxSegments ? forced : kMaxSegments;
-    }
+    if (hint && hint->nseg >= 1) nseg = hint->nseg < kMaxSegments ? hint->nseg : kMaxSegments;
     if (p.nc == 0) nseg = 1;
     nseg = nseg > p.nc && p.nc > 0 ? p.nc : nseg;
     p.seg_chunks = p.nc > 0 ? (p.nc + nseg - 1) / nseg : 0;
@@ -333,9 +328,7 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     if (bf16_io && p.nseg > 1 && p.seg_chunks % 2 == 0 && units * (p.nseg - 1) * 2 <= num_cu &&
         (p.nseg - 1) * 2 <= kMaxSegments - 1)
         p.psub = 2;
-    if (const char* e = getenv("GLA_FWD_PSUB")) {  // tuning override (sweeps, tests)
-        if (atoi(e) == 1) p.psub = 1;
-    }
+    if (hint && hint->psub == 1) p.psub = 1;
     // fp32 segment states (psub per segment boundary); the bf16 path adds a bf16
     // copy of each start state
     p.ws_bytes = (size_t)units * (p.nseg - 1) * p.psub * dk * dv * (sizeof(float) + (bf16_io ? 2 : 0));
@@ -347,29 +340,30 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     // 32.2, its 32 passes being sequential at ~0.7 us each, bound by LDS
     // transposed reads).
     p.chain = bf16_io && chunk == 128 && units <= 16 && p.nseg > 1 && p.nc <= 16;
-    if (const char* e = getenv("GLA_FWD_CHAIN")) {  // tuning override (sweeps, tests)
-        const int forced = atoi(e);
-        if (forced == 0) p.chain = 0;
-        if (forced == 1 && bf16_io && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
-    }
+    if (hint && hint->chain == 0) p.chain = 0;
+    if (hint && hint->chain == 1 && bf16_io && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
     if (p.chain) p.ws_bytes = (size_t)units * p.nc * dk * dv * 2;  // every chunk's start state, bf16
     return p;
 }
 
 template <int DK, int DV, int C, int NW>
-static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k,
-                                 const void* v, const float* lambda, const float* S0, float scale, void* o,
-                                 float* S_final, void* sbar, void* ws, hipStream_t stream) {
+static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, const float* lambda,
+                                 const float* S0, float scale, float* S_final, void* sbar, void* ws,
+                                 hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
     a.H = H;
-    a.q = q;
-    a.k = k;
-    a.v = v;
+    a.q = io.q;
+    a.k = io.k;
+    a.v = io.v;
+    a.sq = io.sq;
+    a.sk = io.sk;
+    a.sv = io.sv;
+    a.so = io.so;
     a.lambda = lambda;
     a.S0 = S0;
     a.scale = scale;
-    a.o = o;
+    a.o = io.o;
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
     a.sbar = sbar;
@@ -390,8 +384,8 @@ static hipError_t launch_fwd_f32(const FwdPlan& plan, int B, int T, int H, const
 }
 
 hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
-                      const void* q, const void* k, const void* v, const float* lambda, const float* S0,
-                      float scale, void* o, float* S_final, void* sbar, void* ws, hipStream_t stream) {
+                      const FwdIO& io, const float* lambda, const float* S0, float scale, float* S_final, void* sbar,
+                      void* ws, hipStream_t stream) {
     if (B == 0 || H == 0) return hipSuccess;
     if (T == 0) {
         if (!S_final) return hipSuccess;
@@ -402,13 +396,12 @@ hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, in
     }
     if (bf16_io) {
         if (dk == 96 && dv == 192)
-            return launch_fwd_bf16(plan, B, T, H, chunk, q, k, v, lambda, S0, scale, o, S_final, sbar, ws, stream);
+            return launch_fwd_bf16(plan, B, T, H, chunk, io, lambda, S0, scale, S_final, sbar, ws, stream);
         return hipErrorInvalidValue;
     }
-#define GLA_FWD_CASE(DK_, DV_, C_, NW_)                                                                   \
-    if (dk == DK_ && dv == DV_ && chunk == C_)                                                             \
-        return launch_fwd_f32<DK_, DV_, C_, NW_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, sbar, \
-                                                 ws, stream);
+#define GLA_FWD_CASE(DK_, DV_, C_, NW_)                                                                    \
+    if (dk == DK_ && dv == DV_ && chunk == C_)                                                              \
+        return launch_fwd_f32<DK_, DV_, C_, NW_>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, stream);
     GLA_FWD_CASE(96, 192, 64, 4)
     GLA_FWD_CASE(16, 32, 32, 2)
 #undef GLA_FWD_CASE

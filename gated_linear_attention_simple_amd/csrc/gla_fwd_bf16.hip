@@ -9,9 +9,10 @@
 // -- the per-token recurrence S_t = lam S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t
 // regrouped exactly.  A partial last chunk uses its own length in place of C.
 //
-// One workgroup per (batch, head, segment) of NW = 2 * NCG waves, NCG column
-// groups of 16 * NCB state/output columns (NCB = 3: 8 waves, two per SIMD;
-// NCB = 2: 12 waves, three per SIMD).  Waves w and w + NCG form a pair owning
+// One workgroup per (batch, head, segment) of NW = 2 * NCG = 12 waves (three per
+// SIMD), NCG = 6 column groups of 16 * NCB = 32 state/output columns.  (NCB, the
+// 16-column blocks per wave, is a template parameter; an 8-wave layout with
+// NCB = 3 measured slower and is not built.)  Waves w and w + NCG form a pair owning
 // columns [16 NCB (w % NCG), +16 NCB); inside a pair, wave h = w / NCG keeps the
 // 16-row state blocks db = 2i + h (i = 0..2) in fp32 accumulator registers for
 // the whole chunk loop.  Per chunk:
@@ -39,7 +40,6 @@
 #include "gla_internal.hpp"
 #include "gla_tile.hpp"
 
-#include <stdlib.h>
 #include <type_traits>
 #include <utility>
 
@@ -74,17 +74,7 @@ struct F8 {
 // score_lead<C, NW>() slots of every wave lie in its first strip.
 template <int C, int NW>
 __host__ __device__ constexpr int score_block(int w, int k) {
-    if constexpr (C == 128 && NW == 8) {
-        constexpr signed char t[8][5] = {{0x70, 0x71, 0x72, 0x73, -1}, {0x74, 0x75, 0x76, 0x77, -1},
-                                         {0x60, 0x61, 0x62, 0x63, -1}, {0x64, 0x65, 0x66, 0x00, -1},
-                                         {0x50, 0x51, 0x52, 0x53, 0x54}, {0x40, 0x41, 0x42, 0x43, 0x55},
-                                         {0x30, 0x31, 0x32, 0x33, 0x44}, {0x20, 0x21, 0x22, 0x10, 0x11}};
-        return t[w][k];
-    } else if constexpr (C == 64 && NW == 8) {
-        constexpr signed char t[8][2] = {{0x30, 0x31}, {0x32, 0x33}, {0x20, 0x21}, {0x22, 0x10},
-                                         {0x11, 0x00}, {-1, -1},     {-1, -1},     {-1, -1}};
-        return t[w][k];
-    } else if constexpr (C == 128 && NW == 12) {
+    if constexpr (C == 128 && NW == 12) {
         constexpr signed char t[12][3] = {{0x70, 0x71, 0x72}, {0x73, 0x74, 0x75}, {0x76, 0x77, 0x00},
                                           {0x60, 0x61, 0x62}, {0x63, 0x64, 0x65}, {0x10, 0x11, 0x66},
                                           {0x50, 0x51, 0x52}, {0x53, 0x54, 0x55}, {0x40, 0x41, 0x42},
@@ -126,7 +116,7 @@ __device__ __forceinline__ void score_blocks_uniform(int w, int* blk, std::integ
 
 template <int C, int NW>
 constexpr int score_lead() {
-    return C == 128 ? (NW == 12 ? 2 : 3) : 1;
+    return C == 128 ? 2 : 1;
 }
 
 // Element offset of row `row`, 16-byte unit `u` (0 or 1) of a 16x16 bf16 score
@@ -215,13 +205,13 @@ __device__ __forceinline__ void out_strip(const bf16* Qs, const bf16* As, SopF s
 // Output strip K stored as bf16: row irow, columns colbase + 16 cb + 4 g + r.
 template <int C, int LDK, int NCB, int K, typename SopF>
 __device__ __forceinline__ void out_pair(const bf16* Qs, const bf16* As, SopF sop, const bf16x8 (&vf)[NCB][C / 32],
-                                         const float* pws, bf16* ob, size_t tokV, int t0, int ceff, int colbase,
+                                         const float* pws, bf16* ob, size_t tokO, int t0, int ceff, int colbase,
                                          int n, int g) {
     out_strip<C, LDK, NCB, K>(Qs, As, sop, vf, pws, n, g, [&](int, int irow, const f32x4(&OT)[NCB]) {
         if (irow < ceff) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                store4<bf16>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, OT[cb]);
+                store4<bf16>(ob + (size_t)(t0 + irow) * tokO + colbase + cb * 16 + 4 * g, OT[cb]);
         }
     });
 }
@@ -252,12 +242,11 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nc, c_begin + a.seg_chunks);
 
-    const int tokK = H * kDK, tokV = H * kDV;
-    const size_t tok0 = (size_t)b * T * H + hd;
-    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
-    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
-    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
-    bf16* ob = static_cast<bf16*>(a.o) + tok0 * kDV;
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokO = a.so.t;
+    const bf16* qb = static_cast<const bf16*>(a.q) + b * a.sq.b + hd * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + b * a.sk.b + hd * kDK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + b * a.sv.b + hd * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + b * a.so.b + hd * kDV;
 
     // This wave's score blocks (scalar): query strips sa (slot 0) and sb (last slot).
     constexpr int NS = L::NSLOT;
@@ -340,7 +329,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
     StageV tv;
     // Tiles of the chunk at token t, rows [0, valid) read.
     auto load_chunk = [&](int t, int valid, int tid) {
-        if constexpr (!SO) tq.load(qb + (size_t)t * tokK, tokK, valid, tid);
+        if constexpr (!SO) tq.load(qb + (size_t)t * tokQ, tokQ, valid, tid);
         tk.load(kb + (size_t)t * tokK, tokK, valid, tid);
         tv.load(vb + (size_t)t * tokV, tokV, valid, tid);
     };
@@ -451,15 +440,15 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
             };
             if constexpr (C == 128) {
                 if (h == 0) {
-                    out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                    out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
                 } else {
-                    out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                    out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                    out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
                 }
             } else {
-                if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
             }
         }
 
@@ -578,12 +567,11 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     const int H = a.H, T = a.T;
     const int hd = bh % H, b = bh / H;
     const int t0 = c * C, ceff = min(C, T - t0);
-    const int tokK = H * kDK, tokV = H * kDV;
-    const size_t tok0 = ((size_t)b * T + t0) * H + hd;
-    const bf16* qb = static_cast<const bf16*>(a.q) + tok0 * kDK;
-    const bf16* kb = static_cast<const bf16*>(a.k) + tok0 * kDK;
-    const bf16* vb = static_cast<const bf16*>(a.v) + tok0 * kDV;
-    bf16* ob = static_cast<bf16*>(a.o) + ((size_t)b * T * H + hd) * kDV;
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokO = a.so.t;
+    const bf16* qb = static_cast<const bf16*>(a.q) + b * a.sq.b + (size_t)t0 * tokQ + hd * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + b * a.sk.b + (size_t)t0 * tokK + hd * kDK;
+    const bf16* vb = static_cast<const bf16*>(a.v) + b * a.sv.b + (size_t)t0 * tokV + hd * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + b * a.so.b + hd * kDV;
 
     constexpr int NS = L::NSLOT;
     int blk[NS];
@@ -607,7 +595,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
         if (ep.aug_a && tid < kDK) augv = ep.aug_a[(size_t)hd * kDK + tid];
     StageK tq, tk;
     StageV tv;
-    tq.load(qb, tokK, ceff, tid);
+    tq.load(qb, tokQ, ceff, tid);
     tk.load(kb, tokK, ceff, tid);
     tv.load(vb, tokV, ceff, tid);
     // start state: this wave's half and the partner's, 4 bf16 per block and lane
@@ -626,9 +614,10 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     uint2 gq[NSTRIP][2][NCB];
     f32x4 wn[NCB];
     if constexpr (EPI) {
-        const bf16* gb = static_cast<const bf16*>(ep.g) + tok0 * kDV;   // row t0 of this (b, h)
+        const int tokG = ep.sg.t;
+        const bf16* gb = static_cast<const bf16*>(ep.g) + b * ep.sg.b + (size_t)t0 * tokG + hd * kDV;  // row t0
         const auto rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(gb), 0,
-                                                          __builtin_amdgcn_readfirstlane(ceff * tokV * 2), kBufWord3);
+                                                          __builtin_amdgcn_readfirstlane(ceff * tokG * 2), kBufWord3);
 #pragma unroll
         for (int j = 0; j < NSTRIP; ++j)
 #pragma unroll
@@ -638,7 +627,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
                     const int K = C == 128 ? (h == 0 ? 3 * j : 1 + j) : h;
                     const int irow = 32 * K + 16 * u + n;
                     gq[j][u][cb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                                 rg, (irow * tokV + colbase + 16 * cb + 4 * g) * 2, 0, 0));
+                                                                 rg, (irow * tokG + colbase + 16 * cb + 4 * g) * 2, 0, 0));
                 }
         const float* wt = ep.norm_w + (size_t)ep.tier[hd] * kDV + colbase + 4 * g;
 #pragma unroll
@@ -685,15 +674,15 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     if constexpr (!EPI) {
         if constexpr (C == 128) {
             if (h == 0) {
-                out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
             } else {
-                out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-                out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
             }
         } else {
-            if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
-            else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokV, t0, ceff, colbase, n, g);
+            if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+            else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
         }
         if (a.sbar) {
             // the chunk's start state for the backward, row-major: this wave's
@@ -766,7 +755,7 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
                             const float gc = to_f32(g4[r]);
                             y[r] = gc * fast_sigmoid(gc) * X[j][u][cb][r] * inv * wn[cb][r];
                         }
-                        store4<bf16>(ob + (size_t)(t0 + irow) * tokV + colbase + cb * 16 + 4 * g, y);
+                        store4<bf16>(ob + (size_t)(t0 + irow) * tokO + colbase + cb * 16 + 4 * g, y);
                     }
                 }
             }
@@ -795,6 +784,7 @@ struct ChainArgs {
     int T, H, nc, units, ncbo;
     const bf16* k;
     const bf16* v;
+    Tok sk, sv;
     const float* lambda;
     const float* S0;
     bf16* snap;
@@ -836,10 +826,9 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
     const int vb = wave % NVB, jlo = NJ == 2 ? 0 : wave / NVB;  // this wave's blocks: rows 16 (jlo + j), columns 16 vb
     const int H = a.H, T = a.T, nc = a.nc;
     const int hd = bh % H, b = bh / H;
-    const int tokK = H * kDK, tokV = H * kDV;
-    const size_t tok0 = (size_t)b * T * H + hd;
-    const bf16* kb = a.k + tok0 * kDK + dk0;
-    const bf16* vb_ = a.v + tok0 * kDV + dv0;
+    const int tokK = a.sk.t, tokV = a.sv.t;
+    const bf16* kb = a.k + b * a.sk.b + hd * kDK + dk0;
+    const bf16* vb_ = a.v + b * a.sv.b + hd * kDV + dv0;
 
     // Start state of the tile (fp32 [dk][dv] -> this wave's blocks), requested
     // before the tiles so that waiting for it waits for no tile.
@@ -1002,8 +991,8 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
 }
 
 template <int C>
-hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, const void* k, const void* v,
-                        const float* lambda, const float* S0, float* S_final, void* ws, hipStream_t stream) {
+hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, const FwdIO& io, const float* lambda,
+                        const float* S0, float* S_final, void* ws, hipStream_t stream) {
     // 4 waves, two 16x16 blocks each, over a 32 x 64 tile (the fastest of the
     // shapes tried; a pass costs ~0.7 us, about half of it LDS time for the
     // transposed operand reads).  Chunks in flight: as deep as the wave's
@@ -1020,8 +1009,10 @@ hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, cons
     c.nc = plan.nc;
     c.units = B * H;
     c.ncbo = ncbo;
-    c.k = static_cast<const bf16*>(k);
-    c.v = static_cast<const bf16*>(v);
+    c.k = static_cast<const bf16*>(io.k);
+    c.v = static_cast<const bf16*>(io.v);
+    c.sk = io.sk;
+    c.sv = io.sv;
     c.lambda = lambda;
     c.S0 = S0;
     c.snap = static_cast<bf16*>(ws);
@@ -1032,19 +1023,22 @@ hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, cons
 }
 
 template <int C, int LDK, int NCB>
-hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, const void* k, const void* v,
-                    const float* lambda, const float* S0, float scale, void* o, float* S_final, void* sbar, void* ws,
-                    const EpilogueArgs* ep, hipStream_t stream) {
+hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, const float* lambda, const float* S0,
+                    float scale, float* S_final, void* sbar, void* ws, const EpilogueArgs* ep, hipStream_t stream) {
     FwdArgs a{};
     a.T = T;
     a.H = H;
-    a.q = q;
-    a.k = k;
-    a.v = v;
+    a.q = io.q;
+    a.k = io.k;
+    a.v = io.v;
+    a.sq = io.sq;
+    a.sk = io.sk;
+    a.sv = io.sv;
+    a.so = io.so;
     a.lambda = lambda;
     a.S0 = S0;
     a.scale = scale;
-    a.o = o;
+    a.o = io.o;
     a.S_final = S_final;
     a.U = static_cast<float*>(ws);
     a.Ub = static_cast<char*>(ws) +
@@ -1058,7 +1052,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
     if (plan.chain) {
         // every chunk's start state from the tiled chain, then one output
         // workgroup per chunk
-        hipError_t err = launch_chain<C>(plan, B, T, H, NCB, k, v, lambda, S0, S_final, ws, stream);
+        hipError_t err = launch_chain<C>(plan, B, T, H, NCB, io, lambda, S0, S_final, ws, stream);
         if (err != hipSuccess) return err;
         a.U = nullptr;
         a.Ub = ws;
@@ -1096,32 +1090,24 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const void* q, con
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
-                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                           void* sbar, void* ws, hipStream_t stream) {
-    // Waves per workgroup: 12 (two 16-column blocks each) or 8 (three each).
-    int ncb = 2;
-    if (const char* e = getenv("GLA_FWD_NCB")) ncb = atoi(e) == 3 ? 3 : 2;  // tuning override (sweeps)
-#define GLA_CASE(C_, NCB_)                                                                                          \
-    if (chunk == C_ && ncb == NCB_)                                                                                  \
-        return launch_c<C_, 104, NCB_>(plan, B, T, H, q, k, v, lambda, S0, scale, o, S_final, sbar, ws, nullptr, \
-                                       stream);
-    GLA_CASE(128, 2)
-    GLA_CASE(128, 3)
-    GLA_CASE(64, 2)
-    GLA_CASE(64, 3)
-#undef GLA_CASE
+hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const FwdIO& io, const float* lambda,
+                           const float* S0, float scale, float* S_final, void* sbar, void* ws, hipStream_t stream) {
+    // 12 waves per workgroup, two 16-column blocks each
+    if (chunk == 128)
+        return launch_c<128, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
+    if (chunk == 64)
+        return launch_c<64, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
     return hipErrorInvalidValue;
 }
 
 // The forward with the mixer epilogue applied in the output kernel's store
 // (the tiled-chain form only; hipErrorNotSupported otherwise, the caller then
 // runs the forward and the epilogue pass).
-hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
-                                    const void* v, const float* lambda, const float* S0, float scale, void* y,
-                                    float* S_final, void* ws, const EpilogueArgs& ep, hipStream_t stream) {
+hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const FwdIO& io,
+                                    const float* lambda, const float* S0, float scale, float* S_final, void* ws,
+                                    const EpilogueArgs& ep, hipStream_t stream) {
     if (!plan.chain || chunk != 128) return hipErrorNotSupported;
-    return launch_c<128, 104, 2>(plan, B, T, H, q, k, v, lambda, S0, scale, y, S_final, nullptr, ws, &ep, stream);
+    return launch_c<128, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, nullptr, ws, &ep, stream);
 }
 
 }  // namespace gla

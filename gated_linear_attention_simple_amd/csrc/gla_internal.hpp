@@ -6,11 +6,25 @@
 
 namespace gla {
 
+// Element strides of a token-major tensor [B][T][H][D] whose head and feature
+// dimensions are packed: element (b, t, h, d) sits at b * b_ + t * t_ + h * D + d.
+// Token strides stay below 2^22 elements, so a tile's offsets fit 32 bits.
+struct Tok {
+    long long b;
+    int t;
+};
+constexpr long long kMaxTokStride = 1LL << 22;
+
+__host__ __device__ inline Tok packed_tok(int T, int H, int D) {
+    return Tok{(long long)T * H * D, H * D};
+}
+
 struct FwdArgs {
     int T, H;
     const void* q;
     const void* k;
     const void* v;
+    Tok sq, sk, sv, so;   // element strides of q, k, v and o
     const float* lambda;
     const float* S0;
     float scale;
@@ -37,19 +51,35 @@ struct FwdPlan {
 // it replaces the segment split only up to this many chunks.
 constexpr int kChainMaxChunks = 64;
 
+// Launch-plan choices a caller may fix (tests, sweeps); zero fields (chain: -1)
+// leave the choice to fwd_plan.
+struct PlanHint {
+    int nseg;   // sequence segments, 1 .. kMaxSegments (0: default)
+    int chain;  // 0: segment split, 1: tiled chain where it can run (-1: default)
+    int psub;   // 1: one prologue workgroup per segment (0: default)
+};
+
+// Token-major operands of one forward call (pointers and their strides).
+struct FwdIO {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    Tok sq, sk, sv, so;
+};
+
 bool fwd_supported(bool bf16_io, int dk, int dv, int chunk);
-FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
+FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu,
+                 const PlanHint* hint = nullptr);
 // sbar (nullable): also store every chunk's start state, [B*H][nc][dk][dv] in
 // the input dtype (the snapshots the backward consumes).
-hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv,
-                      int chunk, const void* q, const void* k, const void* v, const float* lambda,
-                      const float* S0, float scale, void* o, float* S_final, void* sbar, void* ws,
-                      hipStream_t stream);
+hipError_t launch_fwd(bool bf16_io, const FwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
+                      const FwdIO& io, const float* lambda, const float* S0, float scale, float* S_final, void* sbar,
+                      void* ws, hipStream_t stream);
 
 // bf16 forward (dk = 96, dv = 192, chunk 64 or 128): prologue, scan and main launches.
-hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
-                           const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                           void* sbar, void* ws, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const FwdIO& io, const float* lambda,
+                           const float* S0, float scale, float* S_final, void* sbar, void* ws, hipStream_t stream);
 
 // Sequence segments run in parallel (at most this many per sequence).
 constexpr int kMaxSegments = 16;
@@ -71,6 +101,7 @@ struct StateArgs {
     int T, H;
     const void* x;        // [B][T][H][DK]: keys (forward pass) or queries (reverse pass)
     const void* y;        // [B][T][H][DV]: values (forward pass) or output gradients (reverse pass)
+    Tok sx, sy;           // their element strides
     const float* lambda;
     float xscale;         // extra row factor on x: 1 (forward) or the readout scale (reverse)
     const float* S_edge;  // state entering the pass: S0 (forward) or dS_T (reverse); nullable
@@ -92,6 +123,7 @@ struct GradArgs {
     const void* k;
     const void* v;
     const void* d_o;
+    Tok sq, sk, sv, sdo, sdq, sdk, sdv;   // element strides of the token-major tensors
     const float* lambda;
     float scale;
     const void* sbar;  // [BH][NC][DK][DV] (E): chunk start states
@@ -103,24 +135,39 @@ struct GradArgs {
     int nc;
 };
 
-// bf16 gradient kernels (dk = 96, dv = 192, chunk 64 or 128): dK/dV then dQ.
+// bf16 gradient kernel (dk = 96, dv = 192, chunk 64 or 128): dQ, dK and dV of a chunk.
 hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipStream_t stream);
 
 struct BwdPlan {
     int nc, nseg, seg_chunks;
-    size_t snap_bytes;  // per-chunk snapshots (one array for states, one for state gradients)
+    bool saved;         // chunk start states come from the forward (no state snapshot array here)
+    size_t snap_bytes;  // per-chunk snapshots: state gradients (and, unless saved, states)
     size_t u_bytes;     // segment states (fp32)
     size_t part_bytes;  // dlambda partials
     size_t ws_bytes;    // total
 };
+
+// Token-major operands of one backward call.
+struct BwdIO {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* d_o;
+    void* dq;
+    void* dk;
+    void* dv;
+    Tok sq, sk, sv, sdo, sdq, sdk, sdv;
+};
+
 bool bwd_supported(bool bf16_io, int dk, int dv, int chunk);
-BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu);
-// sbar_in (nullable): the chunk start states saved by the forward; the
-// backward then skips its own forward state pass.
+// saved: the backward reads the chunk start states the forward saved.
+BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, int num_cu, bool saved,
+                 const PlanHint* hint = nullptr);
+// sbar_in (non-null exactly when plan.saved): the chunk start states saved by
+// the forward; the backward then skips its own forward state pass.
 hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, int dk, int dv, int chunk,
-                      const void* q, const void* k, const void* v, const float* lambda, const float* S0, float scale,
-                      const void* d_o, const float* dST, void* dq, void* dk_out, void* dv_out, float* dlambda,
-                      float* dS0, const void* sbar_in, void* ws, hipStream_t stream);
+                      const BwdIO& io, const float* lambda, const float* S0, float scale, const float* dST,
+                      float* dlambda, float* dS0, const void* sbar_in, void* ws, hipStream_t stream);
 
 bool decode_supported(int dk, int dv);
 // Mixer epilogue: device pointers, the tier map travels by value.
@@ -135,6 +182,10 @@ struct EpilogueArgs {
     const void* o;
     const void* g;
     void* y;
+    // element strides between consecutive rows (a packed [M][H][D] tensor: H * D);
+    // the forward's output kernel reads the gate through sg instead
+    int rq, rk, rv, ro, rg, ry;
+    Tok sg;
     const float* aug_a;
     const float* norm_w;  // [n_tiers][dv]
     int n_tiers;
@@ -145,10 +196,10 @@ struct EpilogueArgs {
 bool epilogue_supported(int dk, int dv);
 hipError_t launch_epilogue(bool bf16_io, int dk, int dv, const EpilogueArgs& a, hipStream_t stream);
 // bf16 forward with the epilogue in the output kernel (tiled-chain plans only;
-// hipErrorNotSupported for other plans)
-hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const void* q, const void* k,
-                                    const void* v, const float* lambda, const float* S0, float scale, void* y,
-                                    float* S_final, void* ws, const EpilogueArgs& ep, hipStream_t stream);
+// hipErrorNotSupported for other plans); io.o is y
+hipError_t launch_fwd_bf16_epilogue(const FwdPlan& plan, int B, int T, int H, int chunk, const FwdIO& io,
+                                    const float* lambda, const float* S0, float scale, float* S_final, void* ws,
+                                    const EpilogueArgs& ep, hipStream_t stream);
 
 // Depth-wise causal conv + SiLU (width 4).  Prefill: x, y [B][T][D], windows
 // [B][4][D] fp32 (win_in nullable).  Decode: x, y [N = B][D], win_out is the

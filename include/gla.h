@@ -16,11 +16,15 @@
  *   device); `stream` is a hipStream_t passed as void* (NULL = default stream).
  *   Sizes are host ints.  The library never allocates or frees device memory:
  *   the caller owns every buffer, including the workspace.
- * - Layouts are dense row-major, last index fastest:
+ * - Layouts are row-major, last index fastest:
  *     q, k  [B][T][H][dk]     v, o  [B][T][H][dv]      (token-major, as the fused
  *                                                        QKVG projection emits them)
- *     S0, S_final, dS_T, dS0   [B][H][dk][dv] fp32
+ *     S0, S_final, dS_T, dS0   [B][H][dk][dv] fp32, dense
  *     lambda, dlambda          [H] fp32
+ *   The token-major tensors of the chunked forward and backward may be strided
+ *   views (gla_strides below): the paragraph "QKVG projection" of the same
+ *   section has q, k, v and the output gate g come out of one fused projection
+ *   of width H (2 dk + 2 dv) = 9,216, so they can be read in place from it.
  * - dtype selects the element type of q, k, v, o, do, dq, dk, dv: GLA_F32 (fp32)
  *   or GLA_BF16 (bfloat16).  States, lambda and every accumulation are fp32.
  *   bf16 outputs are rounded to nearest even.
@@ -31,8 +35,9 @@
  *   chunk (the last chunk is partial).
  * - Validation is host-only and finishes before any HIP call: on any error
  *   nothing is enqueued and no output is touched.  Pointers must be 16-byte
- *   aligned.  lambda in [0, 1] is a precondition (device data is not read on
- *   the host).  Outputs must not alias inputs (decode's S is in/out by design).
+ *   aligned.  Every computing entry point returns a gla_status.  lambda in
+ *   [0, 1] is a precondition (device data is not read on the host).  Outputs
+ *   must not alias inputs (decode's S is in/out by design).
  * - Calls are asynchronous: GLA_OK means "validated and enqueued on `stream`".
  *   GLA_ERR_DEVICE reports a launch failure; device faults surface at the
  *   caller's next synchronisation.  Results are deterministic (no float
@@ -61,11 +66,34 @@ typedef enum {
 
 typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
 
+/*
+ * Element strides of one token-major tensor [B][T][H][d] whose head and
+ * feature dimensions are packed (head h of token t of sequence b starts at
+ * b * batch + t * token + h * d).  A zero field takes the packed value:
+ * token = H * d, batch = T * token.  Rules (else GLA_ERR_INVALID_ARG):
+ * strides >= 0 and multiples of 16 bytes; H * d <= token < 2^22; for an
+ * output with B > 1, batch >= (T - 1) * token + H * d (its sequences do not
+ * overlap).  Example, the fused projection output X [B][T][H (2dk + 2dv)]:
+ * q = X, k = X + H dk, v = X + 2 H dk, g = X + 2 H dk + H dv, each with
+ * token = H (2dk + 2dv) and batch = T * token.
+ */
+typedef struct {
+    long long batch;
+    long long token;
+} gla_stride;
+
+/* Strides of every token-major tensor of the chunked calls; a call reads only
+ * the entries of the tensors it takes (o holds y for the epilogue forward).
+ * A NULL gla_strides pointer means every tensor is packed. */
+typedef struct {
+    gla_stride q, k, v, o, d_o, dq, dk, dv, g;
+} gla_strides;
+
 /* Version of this ABI (bumped on any signature or semantic change). */
 int gla_abi_version(void);
 
 /* Static, human-readable name of a status code (never NULL). */
-const char* gla_status_str(int status);
+const char* gla_status_str(gla_status status);
 
 /*
  * Workspace needed by gla_fwd_chunked for these sizes, in bytes (0 if none).
@@ -73,7 +101,7 @@ const char* gla_status_str(int status);
  * depends only on the arguments (no device query).
  * Returns 0 as well for unsupported or invalid sizes; the call then reports it.
  */
-size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+size_t gla_fwd_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk);
 
 /*
  * Chunked-parallel forward (Laplace 3B post, section "Challenge 1": per chunk
@@ -88,21 +116,22 @@ size_t gla_fwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, i
  *   o           output [B][T][H][dv] (dtype)
  *   S_final     optional output: state after token T-1 (NULL = not written);
  *               with T == 0 it receives S0 (or zeros)
+ *   st          optional strides of q, k, v, o (NULL = packed)
  *   ws, ws_bytes  caller-owned device workspace, at least
  *               gla_fwd_workspace_bytes(...) bytes (may be NULL when that is 0)
  */
-int gla_fwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
-                    const void* q, const void* k, const void* v,
-                    const float* lambda, const float* S0, float scale,
-                    void* o, float* S_final,
-                    void* ws, size_t ws_bytes, void* stream);
+gla_status gla_fwd_chunked(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                           const void* q, const void* k, const void* v,
+                           const float* lambda, const float* S0, float scale,
+                           void* o, float* S_final, const gla_strides* st,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Workspace needed by gla_bwd_chunked (bytes; 0 for unsupported/invalid sizes).
  * Holds the per-chunk state snapshots (2 * B*H*ceil(T/chunk)*dk*dv elements of
  * the input dtype), segment states and the dlambda partials.
  */
-size_t gla_bwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+size_t gla_bwd_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk);
 
 /*
  * Chunked backward: gradients of a scalar loss L given do = dL/do and the
@@ -116,16 +145,17 @@ size_t gla_bwd_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv, i
  *   dq, dk_out [B][T][H][dk] (dtype) outputs;  dv_out [B][T][H][dv] (dtype) output
  *   dlambda    [H] fp32 output, summed over the batch (NULL = not computed)
  *   dS0        [B][H][dk][dv] fp32 output, gradient of the initial state (NULL = skip)
+ *   st         optional strides of q, k, v, d_o, dq, dk, dv (NULL = packed)
  *   ws, ws_bytes  caller-owned workspace of at least gla_bwd_workspace_bytes(...)
  * With T == 0: dS0 = dS_final (or 0) and dlambda = 0.
  */
-int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
-                    const void* q, const void* k, const void* v,
-                    const float* lambda, const float* S0, float scale,
-                    const void* d_o, const float* dS_final,
-                    void* dq, void* dk_out, void* dv_out,
-                    float* dlambda, float* dS0,
-                    void* ws, size_t ws_bytes, void* stream);
+gla_status gla_bwd_chunked(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                           const void* q, const void* k, const void* v,
+                           const float* lambda, const float* S0, float scale,
+                           const void* d_o, const float* dS_final,
+                           void* dq, void* dk_out, void* dv_out,
+                           float* dlambda, float* dS0, const gla_strides* st,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Training pair: a forward that also saves the state entering every chunk, and
@@ -136,28 +166,32 @@ int gla_bwd_chunked(int dtype, int B, int T, int H, int dk, int dv, int chunk,
  *           states[b][h][c] = the state before chunk c (S0 or 0 for c = 0),
  *           rounded to the dtype; gla_fwd_states_bytes gives its size.
  * gla_fwd_chunked_states: as gla_fwd_chunked, plus `states` (written).  Only for
- * shapes gla_bwd_chunked supports (else GLA_ERR_UNSUPPORTED); same workspace.
+ * shapes gla_bwd_chunked supports (else GLA_ERR_UNSUPPORTED); same workspace
+ * (gla_fwd_workspace_bytes).
  * gla_bwd_chunked_states: as gla_bwd_chunked, plus `states` (read), which must
- * come from gla_fwd_chunked_states over the same q, k, v, lambda, S0 and sizes;
- * same workspace size (gla_bwd_workspace_bytes).  The gradients agree with
+ * come from gla_fwd_chunked_states over the same q, k, v, lambda, S0 and sizes.
+ * Its workspace, gla_bwd_states_workspace_bytes, holds no state snapshots
+ * (about half of gla_bwd_workspace_bytes).  The gradients agree with
  * gla_bwd_chunked's within rounding (the saved states are rounded as the
  * backward's own are, from a differently ordered but equal fp32 recurrence).
  */
-size_t gla_fwd_states_bytes(int dtype, int B, int T, int H, int dk, int dv, int chunk);
+size_t gla_fwd_states_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk);
 
-int gla_fwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk,
-                           const void* q, const void* k, const void* v,
-                           const float* lambda, const float* S0, float scale,
-                           void* o, float* S_final, void* states,
-                           void* ws, size_t ws_bytes, void* stream);
+gla_status gla_fwd_chunked_states(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                  const void* q, const void* k, const void* v,
+                                  const float* lambda, const float* S0, float scale,
+                                  void* o, float* S_final, void* states, const gla_strides* st,
+                                  void* ws, size_t ws_bytes, void* stream);
 
-int gla_bwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int chunk,
-                           const void* q, const void* k, const void* v,
-                           const float* lambda, const float* S0, float scale,
-                           const void* d_o, const float* dS_final, const void* states,
-                           void* dq, void* dk_out, void* dv_out,
-                           float* dlambda, float* dS0,
-                           void* ws, size_t ws_bytes, void* stream);
+size_t gla_bwd_states_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk);
+
+gla_status gla_bwd_chunked_states(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                  const void* q, const void* k, const void* v,
+                                  const float* lambda, const float* S0, float scale,
+                                  const void* d_o, const float* dS_final, const void* states,
+                                  void* dq, void* dk_out, void* dv_out,
+                                  float* dlambda, float* dS0, const gla_strides* st,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Batched single-token decode step (Laplace 3B post, section "Optimizing
@@ -168,10 +202,10 @@ int gla_bwd_chunked_states(int dtype, int B, int T, int H, int dk, int dv, int c
  *   S      [N][H][dk][dv] fp32, updated in place (the sequence's state page)
  * No workspace.  One kernel launch per call.
  */
-int gla_decode_step(int dtype, int N, int H, int dk, int dv,
-                    const void* q, const void* k, const void* v,
-                    const float* lambda, float* S, float scale, void* o,
-                    void* stream);
+gla_status gla_decode_step(gla_dtype dtype, int N, int H, int dk, int dv,
+                           const void* q, const void* k, const void* v,
+                           const float* lambda, float* S, float scale, void* o,
+                           void* stream);
 
 /*
  * The same decode step on a pool of state pages (Laplace 3B post, section
@@ -190,10 +224,10 @@ int gla_decode_step(int dtype, int N, int H, int dk, int dv,
  * Errors: as gla_decode_step; P < 0 or a NULL slots pointer -> GLA_ERR_INVALID_ARG.
  * No workspace.  One kernel launch per call.
  */
-int gla_decode_step_pool(int dtype, int N, int H, int dk, int dv,
-                         const void* q, const void* k, const void* v,
-                         const float* lambda, float* pool, int P, const int* slots,
-                         float scale, void* o, void* stream);
+gla_status gla_decode_step_pool(gla_dtype dtype, int N, int H, int dk, int dv,
+                                const void* q, const void* k, const void* v,
+                                const float* lambda, float* pool, int P, const int* slots,
+                                float scale, void* o, void* stream);
 
 /*
  * Mixer epilogue (Laplace 3B post, section "i14 and the Laplace 3B
@@ -229,10 +263,10 @@ typedef struct {
  * out of range, a negative or non-finite eps, M < 0 -> GLA_ERR_INVALID_ARG;
  * H > 64 or another (dk, dv) -> GLA_ERR_UNSUPPORTED.  M == 0 enqueues nothing.
  */
-int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv,
-                       const void* q, const void* k, const void* v,
-                       const void* o, const void* g,
-                       const gla_epilogue_params* ep, void* y, void* stream);
+gla_status gla_mixer_epilogue(gla_dtype dtype, int M, int H, int dk, int dv,
+                              const void* q, const void* k, const void* v,
+                              const void* o, const void* g,
+                              const gla_epilogue_params* ep, void* y, void* stream);
 
 /*
  * The forward (gla_fwd_chunked) followed by the epilogue above, with y in place
@@ -243,14 +277,16 @@ int gla_mixer_epilogue(int dtype, int M, int H, int dk, int dv,
  * applied in the output kernel's store, on the fp32 readout; other plans run the
  * forward into y and the epilogue pass over y in place.
  *   g      [B][T][H][dv] (dtype) output-gate logits;   y  [B][T][H][dv] (dtype) output
+ *   st     optional strides of q, k, v, g and of y (the `o` entry); NULL = packed
  *   ws     as gla_fwd_chunked (gla_fwd_workspace_bytes of the same sizes)
  *   others as gla_fwd_chunked and gla_mixer_epilogue; the errors of both.
  */
-int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int chunk,
-                             const void* q, const void* k, const void* v,
-                             const float* lambda, const float* S0, float scale,
-                             const void* g, const gla_epilogue_params* ep, void* y,
-                             float* S_final, void* ws, size_t ws_bytes, void* stream);
+gla_status gla_fwd_chunked_epilogue(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                    const void* q, const void* k, const void* v,
+                                    const float* lambda, const float* S0, float scale,
+                                    const void* g, const gla_epilogue_params* ep, void* y,
+                                    float* S_final, const gla_strides* st,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Decode step with the epilogue fused into it: the state update and readout of
@@ -262,11 +298,11 @@ int gla_fwd_chunked_epilogue(int dtype, int B, int T, int H, int dk, int dv, int
  * Other arguments and errors: as gla_decode_step(_pool) and gla_mixer_epilogue
  * (P is ignored when slots == NULL).  One kernel launch, no workspace.
  */
-int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv,
-                             const void* q, const void* k, const void* v, const void* g,
-                             const float* lambda, float* S, int P, const int* slots,
-                             float scale, const gla_epilogue_params* ep, void* y,
-                             void* stream);
+gla_status gla_decode_step_epilogue(gla_dtype dtype, int N, int H, int dk, int dv,
+                                    const void* q, const void* k, const void* v, const void* g,
+                                    const float* lambda, float* S, int P, const int* slots,
+                                    float scale, const gla_epilogue_params* ep, void* y,
+                                    void* stream);
 
 /*
  * Depth-wise causal convolution of width K = 4 with SiLU, the step before the
@@ -286,9 +322,9 @@ int gla_decode_step_epilogue(int dtype, int N, int H, int dk, int dv,
  * Errors: a NULL/misaligned required pointer, negative sizes -> GLA_ERR_INVALID_ARG;
  * another K or D -> GLA_ERR_UNSUPPORTED.
  */
-int gla_conv1d_silu(int dtype, int B, int T, int D, int K,
-                    const void* x, const float* w, const float* bias,
-                    const float* win_in, void* y, float* win_out, void* stream);
+gla_status gla_conv1d_silu(gla_dtype dtype, int B, int T, int D, int K,
+                           const void* x, const float* w, const float* bias,
+                           const float* win_in, void* y, float* win_out, void* stream);
 
 /*
  * One decode token per sequence through the same convolution: the window of
@@ -300,9 +336,9 @@ int gla_conv1d_silu(int dtype, int B, int T, int D, int K,
  * Each row is computed on its own (bit-identical whatever batch it is in).
  * Errors and support: as gla_conv1d_silu; P < 0 with slots -> GLA_ERR_INVALID_ARG.
  */
-int gla_conv1d_silu_decode(int dtype, int N, int D, int K,
-                           const void* x, const float* w, const float* bias,
-                           float* win, int P, const int* slots, void* y, void* stream);
+gla_status gla_conv1d_silu_decode(gla_dtype dtype, int N, int D, int K,
+                                  const void* x, const float* w, const float* bias,
+                                  float* win, int P, const int* slots, void* y, void* stream);
 
 #ifdef __cplusplus
 }

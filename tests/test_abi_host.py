@@ -28,8 +28,8 @@ def test_library_loads_and_exports_header_symbols():
     assert "gla_fwd_chunked" in decl and "gla_decode_step" in decl
     for name in decl:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
-    assert set(gla.SYMBOLS) <= set(decl)
-    assert lib.gla_abi_version() == 3
+    assert set(gla.SYMBOLS) == set(decl)
+    assert lib.gla_abi_version() == 4
 
 
 def test_status_strings():
@@ -43,8 +43,9 @@ MIS = ctypes.c_void_p(18)
 
 
 def fwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, o=P, Sf=None,
-        ws=None, wsb=0):
-    return gla.load().gla_fwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, o, Sf, ws, wsb, None)
+        ws=None, wsb=0, st=None):
+    return gla.load().gla_fwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, o, Sf,
+                                      None if st is None else ctypes.byref(st), ws, wsb, None)
 
 
 def test_fwd_rejects_bad_arguments_before_touching_the_device():
@@ -195,8 +196,8 @@ def test_saved_state_entry_points_validate():
     assert lib.gla_fwd_states_bytes(1, 1, 100, 16, 80, 192, 128) == 0
 
     def f(dtype=1, B=1, T=256, dk=96, dv=192, C=128, states=P, ws=P, wsb=1 << 30):
-        return lib.gla_fwd_chunked_states(dtype, B, T, 16, dk, dv, C, P, P, P, P, None, 1.0, P, None, states, ws,
-                                          wsb, None)
+        return lib.gla_fwd_chunked_states(dtype, B, T, 16, dk, dv, C, P, P, P, P, None, 1.0, P, None, states, None,
+                                          ws, wsb, None)
 
     assert f(dtype=0) == gla.GLA_ERR_UNSUPPORTED           # fp32 96/192: no backward, so no saved states
     assert f(states=None) == gla.GLA_ERR_INVALID_ARG
@@ -205,16 +206,22 @@ def test_saved_state_entry_points_validate():
 
     def b(states=P, ws=None, wsb=0, T=256):
         return lib.gla_bwd_chunked_states(1, 1, T, 16, 96, 192, 128, P, P, P, P, None, 1.0, P, None, states, P, P, P,
-                                          None, None, ws, wsb, None)
+                                          None, None, None, ws, wsb, None)
 
     assert b(states=None) == gla.GLA_ERR_INVALID_ARG
     assert b() == gla.GLA_ERR_WORKSPACE
+    # the saved-state backward's workspace holds no state snapshots of its own
+    full = lib.gla_bwd_workspace_bytes(1, 8, 2048, 16, 96, 192, 128)
+    saved = lib.gla_bwd_states_workspace_bytes(1, 8, 2048, 16, 96, 192, 128)
+    assert full - saved == 8 * 16 * 16 * 96 * 192 * 2
+    # (one byte short of the call's own size: rejected before any launch)
+    assert b(ws=P, wsb=lib.gla_bwd_states_workspace_bytes(1, 1, 256, 16, 96, 192, 128) - 1) == gla.GLA_ERR_WORKSPACE
 
 
 def bwd(dtype=1, B=1, T=256, H=16, dk=96, dv=192, C=128, q=P, k=P, v=P, lam=P, S0=None, do=P, dST=None,
-        dq=P, dk_=P, dv_=P, dl=None, dS0=None, ws=None, wsb=0):
+        dq=P, dk_=P, dv_=P, dl=None, dS0=None, ws=None, wsb=0, st=None):
     return gla.load().gla_bwd_chunked(dtype, B, T, H, dk, dv, C, q, k, v, lam, S0, 1.0, do, dST, dq, dk_, dv_,
-                                      dl, dS0, ws, wsb, None)
+                                      dl, dS0, None if st is None else ctypes.byref(st), ws, wsb, None)
 
 
 def test_bwd_rejects_bad_arguments_before_touching_the_device():
@@ -232,6 +239,73 @@ def test_bwd_rejects_bad_arguments_before_touching_the_device():
     assert need > 0
     assert bwd() == E.GLA_ERR_WORKSPACE
     assert bwd(ws=P, wsb=need - 1) == E.GLA_ERR_WORKSPACE
+
+
+def test_strides_validated_on_the_host():
+    """gla_strides: zero fields mean packed; token strides below H*d, not a multiple of
+    16 bytes or at 2^22 and above are rejected, as are misaligned batch strides and
+    output batch strides that make sequences overlap -- all before any HIP call."""
+    E = gla
+
+    def st(**kw):
+        s = gla.Strides()
+        for name, (b, t) in kw.items():
+            getattr(s, name).batch, getattr(s, name).token = b, t
+        return s
+
+    fused = 16 * (2 * 96 + 2 * 192)                 # the fused QKVG projection's width
+    ok = st(q=(256 * fused, fused), k=(256 * fused, fused), v=(256 * fused, fused), o=(0, 0))
+    # with no workspace the call gets past the stride checks to the workspace check
+    assert fwd(B=2, T=256, st=ok) == E.GLA_ERR_WORKSPACE
+    assert fwd(st=st(q=(0, 16 * 96 - 8))) == E.GLA_ERR_INVALID_ARG          # token < H dk
+    assert fwd(st=st(k=(0, 16 * 96 + 4))) == E.GLA_ERR_INVALID_ARG          # not 16 bytes
+    assert fwd(st=st(v=(0, 1 << 22))) == E.GLA_ERR_INVALID_ARG              # too large
+    assert fwd(st=st(v=(-8, 0))) == E.GLA_ERR_INVALID_ARG
+    assert fwd(st=st(q=(12, 0))) == E.GLA_ERR_INVALID_ARG                   # batch not 16 bytes
+    assert fwd(B=2, st=st(o=(255 * 16 * 192, 0))) == E.GLA_ERR_INVALID_ARG  # output sequences overlap
+    assert fwd(B=2, st=st(q=(8, 0))) == E.GLA_ERR_WORKSPACE                 # overlapping inputs are fine
+    assert bwd(st=st(dq=(0, 16 * 96 - 8))) == E.GLA_ERR_INVALID_ARG
+    assert bwd(B=2, st=st(dv=(16 * 192, 0))) == E.GLA_ERR_INVALID_ARG
+    assert bwd(st=st(d_o=(0, 3))) == E.GLA_ERR_INVALID_ARG
+
+
+def test_plan_controls_validate_and_resolve():
+    lib = gla.load()
+    r = lambda **kw: gla.plan_resolve(1, *kw.pop("shape", (8, 2048, 16, 96, 192, 128)), kw or None)
+    assert r() == {"segments": 2, "chain": 0, "psub": 2}                 # the training step's plan
+    assert r(shape=(1, 2048, 16, 96, 192, 128)) == {"segments": 16, "chain": 1, "psub": 1}   # the layer
+    assert r(shape=(1, 65536, 16, 96, 192, 128)) == {"segments": 16, "chain": 0, "psub": 1}  # the 64k prefill
+    assert r(chain=0, shape=(1, 2048, 16, 96, 192, 128))["chain"] == 0
+    assert r(psub=1) == {"segments": 2, "chain": 0, "psub": 1}
+    assert r(segments=8)["segments"] == 8
+    assert r(segments=5)["segments"] == 4          # 16 chunks in segments of 4
+    for bad in ({"segments": 17}, {"chain": 2}, {"psub": 2}, {"segments": -1}):
+        with pytest.raises(gla.GlaError):
+            r(**bad)
+        assert lib.gla_fwd_workspace_bytes_planned(1, 8, 2048, 16, 96, 192, 128,
+                                                   ctypes.byref(gla._plan(bad))) == 0
+    # planned workspace sizes match the plain ones when nothing is fixed
+    assert gla.fwd_workspace_bytes(1, 1, 2048, 16, 96, 192, 128, plan={}) == \
+        lib.gla_fwd_workspace_bytes(1, 1, 2048, 16, 96, 192, 128)
+    assert gla.bwd_workspace_bytes(1, 8, 2048, 16, 96, 192, 64, saved_states=True, plan={}) == \
+        lib.gla_bwd_states_workspace_bytes(1, 8, 2048, 16, 96, 192, 64)
+
+
+def test_binding_rejects_cpu_tensors_before_the_library():
+    """A host tensor handed to a GPU kernel would fault the device: the binding raises
+    before any library call."""
+    import torch
+    q = torch.zeros(1, 4, 16, 96, dtype=torch.bfloat16)
+    v = torch.zeros(1, 4, 16, 192, dtype=torch.bfloat16)
+    lam = torch.full((16,), 0.9)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.fwd_chunked(q, q, v, lam)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.bwd_chunked(q, q, v, lam, v)
+    with pytest.raises(ValueError, match="GPU"):
+        gla.decode_step(q[:, 0], q[:, 0], v[:, 0], lam, torch.zeros(1, 16, 96, 192))
+    with pytest.raises(ValueError, match="GPU"):
+        gla.conv1d_silu(torch.zeros(1, 4, 3072, dtype=torch.bfloat16), torch.zeros(3072, 4))
 
 
 def test_bwd_workspace_holds_both_snapshot_sets():

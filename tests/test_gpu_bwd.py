@@ -24,13 +24,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(w, seed, B=None, T=None, chunk=None, s0_var=None, with_dS=True):
+def _run(w, seed, B=None, T=None, chunk=None, s0_var=None, with_dS=True, plan=None):
     chunk = chunk or w.chunk
     x = gi.fwd_inputs(w, DEV, seed, B=B, T=T, with_do=True, with_dS=with_dS, s0_var=s0_var)
     _say(f"bwd {w.name} dtype={w.dtype} B={x['q'].shape[0]} T={x['q'].shape[1]} C={chunk} "
          f"S0={'yes' if x['S0'] is not None else 'no'} dS_T={'yes' if with_dS else 'no'} seed={seed}")
     dq, dk, dv, dl, dS0 = gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"],
-                                          dS_final=x.get("dS"), scale=x["scale"], chunk=chunk)
+                                          dS_final=x.get("dS"), scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.synchronize()
     r = oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), f64(x["do"]),
                    S0=None if x["S0"] is None else f64(x["S0"]),
@@ -57,38 +57,16 @@ def test_bf16_ragged_with_states(chunk, T):
 
 
 @pytest.mark.parametrize("chunk", [128, 64])
-@pytest.mark.parametrize("T", [40, 100, 1000, 2048])
-def test_one_kernel_gradients_match_two_kernel_form(chunk, T, monkeypatch):
-    """The one-kernel gradients (dQ, dK, dV of a chunk from one set of operand
-    tiles) and the two-kernel form (dK/dV, then dQ, per 64-token tile) add the
-    same terms in a different order, so they agree to bf16 rounding; the
-    one-kernel result also meets the oracle.  At C = 128, T = 40 and 100 are a
-    single partial chunk (no second query half, then one)."""
-    w = gi.workloads()[1]
-    x = gi.fwd_inputs(w, DEV, 1500 + T + chunk, B=2, T=T, with_do=True, with_dS=True, s0_var=0.01)
-    _say(f"one-kernel vs two-kernel gradients B=2 T={T} C={chunk}")
-    outs = []
-    for split in ("1", "0"):
-        monkeypatch.setenv("GLA_GRAD_SPLIT", split)
-        outs.append(gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"], dS_final=x["dS"],
-                                    scale=x["scale"], chunk=chunk))
-    torch.cuda.synchronize()
-    for a_, b_, name in zip(outs[0], outs[1], ("dq", "dk", "dv", "dlambda", "dS0")):
-        a64, b64 = f64(a_), f64(b_)
-        rel = np.linalg.norm(a64 - b64) / max(np.linalg.norm(a64), 1e-30)
-        assert rel <= (1e-5 if name in ("dlambda", "dS0") else 4e-3), f"{name}: forms differ, rel L2 {rel:.3e}"
-    r = oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), f64(x["do"]), S0=f64(x["S0"]),
-                   dS_T=f64(x["dS"]), scale=x["scale"])
-    dq, dk, dv, dl, dS0 = outs[1]
-    for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
-        assert_close(f64(got), ref, w.dtype, name)
-    assert_close(f64(dl), r[3], w.dtype, "dlambda", batch_axis=None)
+@pytest.mark.parametrize("T", [40, 2048])
+def test_single_partial_chunk_and_full_length(chunk, T):
+    """One partial chunk (T = 40: no second query half at either chunk size) and the
+    full 2,048-token sequence, with S0 and dS_T."""
+    _run(gi.workloads()[1], seed=1500 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
 
 
 @pytest.mark.parametrize("nseg", [1, 3, 5])
-def test_bf16_segment_split(nseg, monkeypatch):
-    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(nseg))
-    _run(gi.workloads()[1], seed=90 + nseg, B=1, T=1000, chunk=64, s0_var=0.01)
+def test_bf16_segment_split(nseg):
+    _run(gi.workloads()[1], seed=90 + nseg, B=1, T=1000, chunk=64, s0_var=0.01, plan={"segments": nseg})
 
 
 @pytest.mark.parametrize("chunk", [128, 64])
@@ -127,13 +105,12 @@ def test_page_decay_schedule(chunk):
     _run(w, seed=90 + chunk, B=2, T=600, chunk=chunk, s0_var=0.01)
 
 
-def _states_case(w, seed, B, T, chunk, s0_var, chain=None, monkeypatch=None):
-    if chain is not None:
-        monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+def _states_case(w, seed, B, T, chunk, s0_var, chain=None):
+    plan = None if chain is None else {"chain": chain}
     x = gi.fwd_inputs(w, DEV, seed, B=B, T=T, with_do=True, with_dS=True, s0_var=s0_var)
     _say(f"fwd/bwd with saved states {w.name} B={B} T={T} C={chunk} chain={chain}")
     o, S, states = gla.fwd_chunked_states(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"],
-                                          chunk=chunk)
+                                          chunk=chunk, plan=plan)
     g = gla.bwd_chunked_states(x["q"], x["k"], x["v"], x["lam"], x["do"], states, S0=x["S0"], dS_final=x["dS"],
                                scale=x["scale"], chunk=chunk)
     torch.cuda.synchronize()
@@ -141,14 +118,14 @@ def _states_case(w, seed, B, T, chunk, s0_var, chain=None, monkeypatch=None):
 
 
 @pytest.mark.parametrize("wi,B,T,chunk,chain", [(1, 2, 700, 128, None), (1, 2, 700, 64, None),
-                                                (1, 1, 2048, 128, "1"), (1, 1, 2048, 128, "0"),
-                                                (1, 1, 300, 128, "1"), (0, 2, 200, 32, None)])
-def test_saved_states_and_backward_match_oracle(wi, B, T, chunk, chain, monkeypatch):
+                                                (1, 1, 2048, 128, 1), (1, 1, 2048, 128, 0),
+                                                (1, 1, 300, 128, 1), (0, 2, 200, 32, None)])
+def test_saved_states_and_backward_match_oracle(wi, B, T, chunk, chain):
     """gla_fwd_chunked_states writes the state before every chunk (checked against the
     oracle's state after each prefix of whole chunks), and gla_bwd_chunked_states'
     gradients from them match the oracle's reverse mode."""
     w = gi.workloads()[wi]
-    x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 90 + T + chunk, B, T, chunk, 0.01, chain, monkeypatch)
+    x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 90 + T + chunk, B, T, chunk, 0.01, chain)
     nc = (T + chunk - 1) // chunk
     c64 = lambda name: f64(x[name])
     for c in range(nc):
@@ -176,6 +153,8 @@ def test_saved_states_training_width(chunk):
     dq, dk, dv and dS0, and dlambda (a sum over the batch), against the oracle; the
     gradients also agree with the recomputing backward's within the bf16 bar."""
     w = gi.workloads()[2]
+    plan = gla.plan_resolve(gla.GLA_BF16, 8, 2048, 16, 96, 192, chunk)
+    assert plan == {"segments": 2, "chain": 0, "psub": 2}, plan   # the plan the bench times
     x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 7 + chunk, 8, 2048, chunk, 0.0)
     g2 = gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"], dS_final=x["dS"], scale=x["scale"],
                          chunk=chunk)

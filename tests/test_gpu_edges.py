@@ -43,13 +43,7 @@ def _wl(wi, lams, chunk=None, dtype=None):
                        w.scale, w.s0_var)
 
 
-def _set_plan(monkeypatch, plan):
-    for key in ("GLA_FWD_CHAIN", "GLA_FWD_SEGMENTS"):
-        monkeypatch.delenv(key, raising=False)
-    if plan == "chain":
-        monkeypatch.setenv("GLA_FWD_CHAIN", "1")
-    elif plan == "segments":
-        monkeypatch.setenv("GLA_FWD_CHAIN", "0")
+PLANS = {None: None, "chain": {"chain": 1}, "segments": {"chain": 0}}
 
 
 # (workload, B, T, chunk, dtype, S0 variance, plan): the Laplace layer through the tiled
@@ -67,14 +61,14 @@ FWD_CASES = {
 
 @pytest.mark.parametrize("lset", sorted(LAMBDA_SETS))
 @pytest.mark.parametrize("case", sorted(FWD_CASES))
-def test_forward_edges(case, lset, monkeypatch):
+def test_forward_edges(case, lset):
     wi, B, T, chunk, dtype, s0, plan = FWD_CASES[case]
     lams = (TINY_SETS if wi == 0 else LAMBDA_SETS)[lset]
     w = _wl(wi, lams, chunk, dtype)
-    _set_plan(monkeypatch, plan)
     x = gi.fwd_inputs(w, DEV, 4000 + len(case) + T, B=B, T=T, s0_var=s0)
     _say(f"fwd edges {case} lambda={lset} B={B} T={T} C={chunk} {w.dtype} plan={plan}")
-    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk,
+                           plan=PLANS[plan])
     torch.cuda.synchronize()
     S0r = None if x["S0"] is None else f64(x["S0"])
     ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), S0=S0r, scale=x["scale"])
@@ -157,16 +151,15 @@ def test_decode_edges(lset, dtype):
 
 @pytest.mark.parametrize("lset", sorted(LAMBDA_SETS))
 @pytest.mark.parametrize("plan", ["chain", "segments"])
-def test_forward_epilogue_edges(lset, plan, monkeypatch):
+def test_forward_epilogue_edges(lset, plan):
     """The forward with the epilogue fused into its output kernel (tiled chain) and
     the forward followed by the epilogue pass (segments), Laplace-layer shape."""
     w = _wl(1, LAMBDA_SETS[lset])
-    _set_plan(monkeypatch, plan)
     x = gi.fwd_inputs(w, DEV, seed=71, s0_var=0.01)
     e = gi.epilogue_inputs(w, DEV, 71, (w.B, w.T))
     _say(f"fwd+epilogue edges lambda={lset} plan={plan}")
     y, S = gla.fwd_chunked_epilogue(x["q"], x["k"], x["v"], x["lam"], e["g"], e["norm_w"], e["tier"],
-                                    aug_a=e["aug_a"], S0=x["S0"], scale=x["scale"], chunk=128)
+                                    aug_a=e["aug_a"], S0=x["S0"], scale=x["scale"], chunk=128, plan=PLANS[plan])
     torch.cuda.synchronize()
     ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), S0=f64(x["S0"]), scale=x["scale"])
     ry = oracle.epilogue(f64(x["q"]), f64(x["k"]), f64(x["v"]), ro, f64(e["g"]), f64(e["aug_a"]), f64(e["norm_w"]),

@@ -236,22 +236,21 @@ def test_decode_epilogue_full_width_sampled():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("B,T,chunk,chain", [(1, 2048, 128, "1"), (1, 2048, 128, "0"), (1, 300, 128, "1"),
-                                             (1, 300, 128, "0"), (2, 700, 128, None), (1, 2048, 64, None)])
+@pytest.mark.parametrize("B,T,chunk,chain", [(1, 2048, 128, 1), (1, 2048, 128, 0), (1, 300, 128, 1),
+                                             (1, 300, 128, 0), (2, 700, 128, None), (1, 2048, 64, None)])
 @pytest.mark.parametrize("aug", [True, False])
-def test_forward_epilogue_matches_oracle(B, T, chunk, chain, aug, monkeypatch):
+def test_forward_epilogue_matches_oracle(B, T, chunk, chain, aug):
     """gla_fwd_chunked_epilogue: fused into the output kernel on tiled-chain plans
     (chain = "1"), forward then the epilogue pass otherwise; y and S_final against the
     oracle's forward followed by its epilogue."""
-    if chain is not None:
-        monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+    plan = None if chain is None else {"chain": chain}
     w = gi.workloads()[1]
     x = gi.fwd_inputs(w, DEV, seed=51 + T, B=B, T=T, s0_var=0.01)
     e = gi.epilogue_inputs(w, DEV, 51 + T, (B, T))
     a = e["aug_a"] if aug else None
     _say(f"fwd+epilogue B={B} T={T} C={chunk} chain={chain} aug={aug}")
     y, S = gla.fwd_chunked_epilogue(x["q"], x["k"], x["v"], x["lam"], e["g"], e["norm_w"], e["tier"], aug_a=a,
-                                    S0=x["S0"], scale=x["scale"], chunk=chunk)
+                                    S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.synchronize()
     ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), S0=f64(x["S0"]), scale=x["scale"])
     ry = oracle.epilogue(f64(x["q"]), f64(x["k"]), f64(x["v"]), ro, f64(e["g"]), None if a is None else f64(a),

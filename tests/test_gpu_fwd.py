@@ -26,14 +26,14 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run_and_check(w, seed, B=None, T=None, chunk=None, s0_var=None, dtype=None):
+def _run_and_check(w, seed, B=None, T=None, chunk=None, s0_var=None, dtype=None, plan=None):
     chunk = chunk or w.chunk
     if dtype is not None:
         w = gi.Workload(w.name, w.B, w.T, w.H, w.dk, w.dv, chunk, dtype, w.lambdas, w.scale, w.s0_var)
     x = gi.fwd_inputs(w, DEV, seed, B=B, T=T, s0_var=s0_var)
     _say(f"{w.name} dtype={w.dtype} B={x['q'].shape[0]} T={x['q'].shape[1]} C={chunk} "
-         f"S0={'yes' if x['S0'] is not None else 'no'} seed={seed}")
-    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+         f"S0={'yes' if x['S0'] is not None else 'no'} plan={plan} seed={seed}")
+    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.synchronize()
     ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]),
                         S0=None if x["S0"] is None else f64(x["S0"]), scale=x["scale"])
@@ -68,47 +68,40 @@ def test_fp32_laplace_shape_chunk64():
 
 
 @pytest.mark.parametrize("nseg", [1, 2, 3, 5, 16])
-def test_segment_split_equivalence(nseg, monkeypatch):
+def test_segment_split_equivalence(nseg):
     """Forcing different sequence-segment counts gives the oracle's result."""
-    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(nseg))
-    monkeypatch.setenv("GLA_FWD_CHAIN", "0")
-    _run_and_check(gi.workloads()[1], seed=200 + nseg, B=1, T=2000, chunk=64, s0_var=0.01)
+    _run_and_check(gi.workloads()[1], seed=200 + nseg, B=1, T=2000, chunk=64, s0_var=0.01,
+                   plan={"segments": nseg, "chain": 0})
 
 
-@pytest.mark.parametrize("ncb", ["2", "3"])
+PLANS = {"seg1": {"segments": 1, "chain": 0}, "seg3": {"segments": 3, "chain": 0}, "chain": {"chain": 1}}
+
+
 @pytest.mark.parametrize("chunk", [128, 64])
-@pytest.mark.parametrize("mode", ["seg1", "seg3", "chain"])
-def test_bf16_wave_layouts(ncb, chunk, mode, monkeypatch):
-    """Both bf16 workgroup layouts (12 waves with 32-column pairs, 8 waves with
-    48-column pairs): unsplit, with sequence segments, and with the tiled state
+@pytest.mark.parametrize("mode", sorted(PLANS))
+def test_bf16_plans(chunk, mode):
+    """The bf16 launch plans: unsplit, with sequence segments, and the tiled state
     chain feeding one output workgroup per chunk; ragged tail, S0."""
-    monkeypatch.setenv("GLA_FWD_NCB", ncb)
-    monkeypatch.setenv("GLA_FWD_SEGMENTS", "3" if mode == "seg3" else "1")
-    monkeypatch.setenv("GLA_FWD_CHAIN", "1" if mode == "chain" else "0")
-    _run_and_check(gi.workloads()[1], seed=300 + 7 * int(ncb) + chunk + len(mode), B=2, T=1000, chunk=chunk,
-                   s0_var=0.01)
+    _run_and_check(gi.workloads()[1], seed=314 + chunk + len(mode), B=2, T=1000, chunk=chunk, s0_var=0.01,
+                   plan=PLANS[mode])
 
 
-@pytest.mark.parametrize("ncb", ["2", "3"])
 @pytest.mark.parametrize("chunk,T,s0", [(128, 2048, None), (64, 1000, None), (128, 700, 0.01), (64, 700, 0.01)])
 @pytest.mark.parametrize("want_final", [True, False])
-def test_chain_matches_one_chunk_segments_bitwise(ncb, chunk, T, s0, want_final, monkeypatch):
+def test_chain_matches_one_chunk_segments_bitwise(chunk, T, s0, want_final):
     """The tiled state chain forms each chunk's contribution on its own and folds
     it in with the segment scan's fma, i.e. the arithmetic of the segment split
     with one chunk per segment: the outputs agree bit for bit, the final states
     (rounded in a different order by the segment path's last workgroup) to fp32
     accuracy.  Both also meet the oracle."""
     w = gi.workloads()[1]
-    monkeypatch.setenv("GLA_FWD_NCB", ncb)
     x = gi.fwd_inputs(w, DEV, 900 + chunk + T, B=1, T=T, s0_var=s0)
     nc = (T + chunk - 1) // chunk
-    _say(f"chain vs {nc} one-chunk segments ncb={ncb} C={chunk} T={T} S0={s0 is not None} S_final={want_final}")
+    _say(f"chain vs {nc} one-chunk segments C={chunk} T={T} S0={s0 is not None} S_final={want_final}")
     outs = []
-    for segs, chain in ((str(nc), "0"), ("1", "1")):
-        monkeypatch.setenv("GLA_FWD_SEGMENTS", segs)
-        monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+    for plan in ({"segments": nc, "chain": 0}, {"segments": 1, "chain": 1}):
         o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk,
-                               S_final=want_final)
+                               S_final=want_final, plan=plan)
         outs.append((o, S))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]), "o differs between the segment and chain paths"
@@ -122,24 +115,21 @@ def test_chain_matches_one_chunk_segments_bitwise(ncb, chunk, T, s0, want_final,
 
 
 @pytest.mark.parametrize("chunk,T,segs,s0", [(64, 1500, 2, 0.01), (128, 2048, 3, None), (128, 1000, 2, 0.01)])
-def test_prologue_sub_segments(chunk, T, segs, s0, monkeypatch):
+def test_prologue_sub_segments(chunk, T, segs, s0):
     """When the state-only prologue would fill at most half the compute units it runs
     over half-length sub-segments and the scan combines their states: the start states
     differ from one prologue workgroup per segment only by fp32 rounding, which can
     flip the bf16 rounding of a state operand, so the outputs agree to rel L2 1e-3
     (a tenth of the oracle tolerance); both meet the oracle."""
     w = gi.workloads()[1]
-    monkeypatch.setenv("GLA_FWD_CHAIN", "0")
-    monkeypatch.setenv("GLA_FWD_SEGMENTS", str(segs))
     x = gi.fwd_inputs(w, DEV, 1700 + T + chunk, B=2, T=T, s0_var=s0)
     _say(f"prologue sub-segments B=2 T={T} C={chunk} segments={segs}")
+    base = {"chain": 0, "segments": segs}
+    assert gla.plan_resolve(gla.GLA_BF16, 2, T, 16, 96, 192, chunk, base)["psub"] == 2
     outs = []
-    for psub in ("1", "2"):
-        if psub == "1":
-            monkeypatch.setenv("GLA_FWD_PSUB", "1")
-        else:
-            monkeypatch.delenv("GLA_FWD_PSUB", raising=False)
-        outs.append(gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk))
+    for plan in (dict(base, psub=1), base):
+        outs.append(gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk,
+                                    plan=plan))
     torch.cuda.synchronize()
     a, b = f64(outs[0][0]), f64(outs[1][0])
     rel = np.linalg.norm(a - b) / np.linalg.norm(a)
@@ -259,13 +249,12 @@ def test_causality():
     assert torch.equal(o[:, :cut], o2[:, :cut])
 
 
-@pytest.mark.parametrize("chunk,chain", [(128, "0"), (128, "1"), (64, "0")])
-def test_page_decay_schedule(chunk, chain, monkeypatch):
+@pytest.mark.parametrize("chunk,chain", [(128, 0), (128, 1), (64, 0)])
+def test_page_decay_schedule(chunk, chain):
     """The pages' geometric half-life schedule (head 0: lambda = 0.5, so lambda^C
     underflows fp32's normal range at C = 128) on the Laplace-layer shape, through
     the segment split and the tiled chain."""
-    monkeypatch.setenv("GLA_FWD_CHAIN", chain)
     w = gi.workloads()[1]
     w = gi.Workload(w.name + "-page-decay", w.B, w.T, w.H, w.dk, w.dv, chunk, w.dtype,
                     tuple(gi.page_lambdas(w.H)), w.scale)
-    _run_and_check(w, seed=95 + chunk, chunk=chunk, s0_var=0.01)
+    _run_and_check(w, seed=95 + chunk, chunk=chunk, s0_var=0.01, plan={"chain": chain})

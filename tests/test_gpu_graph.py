@@ -1,4 +1,5 @@
-"""HIP-graph capture of the library calls (the bench times the forward as graph replays).
+"""HIP-graph capture of the library calls (for callers that replay a captured step;
+the bench itself times eager calls).
 
 The forward and backward record only kernel launches on the caller's stream (no
 allocation, no memset), so they can be captured.  Each replay, with unrelated
@@ -22,38 +23,39 @@ def _say(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("chunk,chain", [(128, "0"), (64, "0"), (128, "1")])
-def test_graph_replays_match_eager(chunk, chain, monkeypatch):
+@pytest.mark.parametrize("chunk,chain", [(128, 0), (64, 0), (128, 1)])
+def test_graph_replays_match_eager(chunk, chain):
     """Also with the forward's tiled state chain (two launches, a chunk start
     state workspace) in the captured sequence."""
-    monkeypatch.setenv("GLA_FWD_CHAIN", chain)
+    plan = {"chain": chain}
     w = gi.workloads()[1]
     x = gi.fwd_inputs(w, DEV, 41 + chunk, B=2, T=700, with_do=True, s0_var=0.01)
     y = gi.fwd_inputs(w, DEV, 43 + chunk, B=2, T=700, with_do=True, s0_var=0.01)
     _say(f"graph capture fwd+bwd B=2 T=700 C={chunk} chain={chain}")
     args = (x["q"], x["k"], x["v"], x["lam"])
-    o_ref, S_ref = gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk)
-    g_ref = gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+    o_ref, S_ref = gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
+    g_ref = gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.synchronize()
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk)
-        gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+        gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
+        gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        o, S = gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk)
-        grads = gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk)
+        o, S = gla.fwd_chunked(*args, S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
+        grads = gla.bwd_chunked(*args, x["do"], S0=x["S0"], scale=x["scale"], chunk=chunk, plan=plan)
     torch.cuda.synchronize()
 
     for rep in range(3):
         # unrelated eager work on the same buffers' neighbours between replays
-        gla.fwd_chunked(y["q"], y["k"], y["v"], y["lam"], S0=y["S0"], scale=y["scale"], chunk=chunk)
-        gla.bwd_chunked(y["q"], y["k"], y["v"], y["lam"], y["do"], S0=y["S0"], scale=y["scale"], chunk=chunk)
+        gla.fwd_chunked(y["q"], y["k"], y["v"], y["lam"], S0=y["S0"], scale=y["scale"], chunk=chunk, plan=plan)
+        gla.bwd_chunked(y["q"], y["k"], y["v"], y["lam"], y["do"], S0=y["S0"], scale=y["scale"], chunk=chunk,
+                        plan=plan)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
