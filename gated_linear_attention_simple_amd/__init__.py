@@ -52,7 +52,11 @@ SYMBOLS = (
     "gla_bwd_workspace_bytes_planned",
     "gla_fwd_chunked_planned",
     "gla_bwd_chunked_planned",
+    "gla_fwd_chunked_noalloc",
 )
+
+# the allocation-free forward's workspace limit (GLA_NOALLOC_WORKSPACE_MAX in gla.h)
+NOALLOC_WORKSPACE_MAX = 32 << 20
 
 _lib = None
 
@@ -119,6 +123,7 @@ def load():
         lib.gla_bwd_workspace_bytes_planned.argtypes = [i] * 8 + [pp]
         lib.gla_fwd_chunked_planned.argtypes = [i] * 7 + [vp] * 5 + [f, vp, vp, vp, vp, ep, stp, pp, vp, sz, vp]
         lib.gla_bwd_chunked_planned.argtypes = [i] * 7 + [vp] * 5 + [f] + [vp] * 8 + [stp, pp, vp, sz, vp]
+        lib.gla_fwd_chunked_noalloc.argtypes = [i] * 7 + [vp] * 5 + [f, vp, vp, stp, vp]
         for name in SYMBOLS:   # every call that computes returns a gla_status
             if name not in ("gla_status_str", "gla_abi_version") and not name.endswith("bytes"):
                 getattr(lib, name).restype = i
@@ -302,6 +307,22 @@ def fwd_chunked(q, k, v, lam, S0=None, scale=1.0, chunk=128, o=None, S_final=Tru
     gla_fwd_chunked_planned with that launch plan."""
     o, S_final, _ = _fwd_call(q, k, v, lam, S0, scale, chunk, o, S_final, None, None, None, workspace, stream, plan,
                               "gla_fwd_chunked")
+    return o, S_final
+
+
+def fwd_chunked_noalloc(q, k, v, lam, o, S_final=None, S0=None, scale=1.0, chunk=128, stream=None):
+    """gla_fwd_chunked_noalloc: the forward with its workspace in the library's fixed
+    per-GPU scratch array (no allocation in the call; outputs are the caller's)."""
+    lib = load()
+    B, T, H, dk, dv, dev = _fwd_common(q, k, v, lam, S0, None, "gla_fwd_chunked_noalloc")
+    _check_tok(o, "o", (B, T, H, dv), q.dtype, dev)
+    if S_final is not None:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    _, sp = _stream(stream)
+    st = _strides(q=q, k=k, v=v, o=o)
+    _raise(lib.gla_fwd_chunked_noalloc(_dt(q), B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                       _ptr(S0), float(scale), _ptr(o), _ptr(S_final), ctypes.byref(st), sp),
+           "gla_fwd_chunked_noalloc")
     return o, S_final
 
 

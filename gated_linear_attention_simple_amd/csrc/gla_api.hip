@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -104,13 +105,28 @@ static_assert(GLA_EPI_MAX_HEADS == gla::kEpiMaxHeads, "tier map capacity");
 
 gla_status device_status(hipError_t err) { return err == hipSuccess ? GLA_OK : GLA_ERR_DEVICE; }
 
-// The chunked forward with its options: every chunk's start state saved to
-// `states` for the backward (with_states), and the fused epilogue (ep != NULL:
+// A validated chunked forward, ready to launch: every chunk's start state saved
+// to `states` for the backward (with_states), and the fused epilogue (ep != NULL:
 // o receives y).
-gla_status fwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
-                     const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
-                     bool with_states, void* states, const void* g, const gla_epilogue_params* ep,
-                     const gla_strides* st, const gla_plan* plan_in, void* ws, size_t ws_bytes, hipStream_t stream) {
+struct FwdCall {
+    bool bf;
+    int B, T, H, dk, dv, chunk;
+    gla::FwdIO io;
+    const float* lambda;
+    const float* S0;
+    float scale;
+    float* S_final;
+    void* states;       // null unless saved
+    bool epi;
+    gla::EpilogueArgs ea;
+    gla::FwdPlan plan;
+};
+
+// All host-side checks of a forward; fills `c` on success.  Makes no HIP call.
+gla_status fwd_prepare(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                       const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                       bool with_states, void* states, const void* g, const gla_epilogue_params* ep,
+                       const gla_strides* st, const gla_plan* plan_in, FwdCall* c) {
     gla_status s = fwd_check_shape(dtype, B, T, H, dk, dv, chunk);
     if (s != GLA_OK) return s;
     const bool bf = dtype == GLA_BF16;
@@ -118,38 +134,60 @@ gla_status fwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int c
     if (with_states && ep) return GLA_ERR_UNSUPPORTED;
     gla::PlanHint hint;
     if (!hint_of(plan_in, &hint)) return GLA_ERR_INVALID_ARG;
-    gla::EpilogueArgs ea{};
-    if (ep && (s = epi_fill(ep, H, dk, dv, &ea)) != GLA_OK) return s;
+    *c = FwdCall{};
+    if (ep && (s = epi_fill(ep, H, dk, dv, &c->ea)) != GLA_OK) return s;
     if (T > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(lambda))) return GLA_ERR_INVALID_ARG;
     if (T > 0 && with_states && !ok_ptr(states)) return GLA_ERR_INVALID_ARG;
     if (T > 0 && ep && !ok_ptr(g)) return GLA_ERR_INVALID_ARG;
     if (!ok_opt(S0) || !ok_opt(S_final)) return GLA_ERR_INVALID_ARG;
     const int es = esize(dtype);
-    gla::FwdIO io{q, k, v, o, {}, {}, {}, {}};
+    c->io = gla::FwdIO{q, k, v, o, {}, {}, {}, {}};
     gla::Tok sg{};
-    if (!resolve_stride(st ? &st->q : nullptr, B, T, H, dk, es, false, &io.sq) ||
-        !resolve_stride(st ? &st->k : nullptr, B, T, H, dk, es, false, &io.sk) ||
-        !resolve_stride(st ? &st->v : nullptr, B, T, H, dv, es, false, &io.sv) ||
-        !resolve_stride(st ? &st->o : nullptr, B, T, H, dv, es, true, &io.so) ||
+    if (!resolve_stride(st ? &st->q : nullptr, B, T, H, dk, es, false, &c->io.sq) ||
+        !resolve_stride(st ? &st->k : nullptr, B, T, H, dk, es, false, &c->io.sk) ||
+        !resolve_stride(st ? &st->v : nullptr, B, T, H, dv, es, false, &c->io.sv) ||
+        !resolve_stride(st ? &st->o : nullptr, B, T, H, dv, es, true, &c->io.so) ||
         (ep && !resolve_stride(st ? &st->g : nullptr, B, T, H, dv, es, false, &sg)))
         return GLA_ERR_INVALID_ARG;
-    const gla::FwdPlan plan = gla::fwd_plan(bf, B, T, H, dk, dv, chunk, kPlanCUs, &hint);
-    if (plan.ws_bytes > 0 && T > 0 && (!ok_ptr(ws) || ws_bytes < plan.ws_bytes)) return GLA_ERR_WORKSPACE;
-    if (!ep)
-        return device_status(gla::launch_fwd(bf, plan, B, T, H, dk, dv, chunk, io, lambda, S0, scale, S_final,
-                                             T > 0 && with_states ? states : nullptr, ws, stream));
-    ea.sg = sg;
-    ea.g = g;
-    if (bf && T > 0) {
-        const hipError_t err = gla::launch_fwd_bf16_epilogue(plan, B, T, H, chunk, io, lambda, S0, scale, S_final, ws,
-                                                             ea, stream);
+    c->bf = bf;
+    c->B = B;
+    c->T = T;
+    c->H = H;
+    c->dk = dk;
+    c->dv = dv;
+    c->chunk = chunk;
+    c->lambda = lambda;
+    c->S0 = S0;
+    c->scale = scale;
+    c->S_final = S_final;
+    c->states = T > 0 && with_states ? states : nullptr;
+    c->epi = ep != nullptr;
+    c->ea.sg = sg;
+    c->ea.g = g;
+    c->plan = gla::fwd_plan(bf, B, T, H, dk, dv, chunk, kPlanCUs, &hint);
+    return GLA_OK;
+}
+
+// Launches a prepared forward with its workspace.
+gla_status fwd_run(const FwdCall& c, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const int B = c.B, T = c.T, H = c.H, dk = c.dk, dv = c.dv, chunk = c.chunk;
+    if (c.plan.ws_bytes > 0 && T > 0 && (!ok_ptr(ws) || ws_bytes < c.plan.ws_bytes)) return GLA_ERR_WORKSPACE;
+    if (!c.epi)
+        return device_status(gla::launch_fwd(c.bf, c.plan, B, T, H, dk, dv, chunk, c.io, c.lambda, c.S0, c.scale,
+                                             c.S_final, c.states, ws, stream));
+    gla::EpilogueArgs ea = c.ea;
+    if (c.bf && T > 0) {
+        const hipError_t err = gla::launch_fwd_bf16_epilogue(c.plan, B, T, H, chunk, c.io, c.lambda, c.S0, c.scale,
+                                                             c.S_final, ws, ea, stream);
         if (err == hipSuccess) return GLA_OK;
         if (err != hipErrorNotSupported) return GLA_ERR_DEVICE;
     }
     // other plans: the readout into y, then the epilogue pass over y in place
-    hipError_t err = gla::launch_fwd(bf, plan, B, T, H, dk, dv, chunk, io, lambda, S0, scale, S_final, nullptr, ws,
-                                     stream);
+    hipError_t err = gla::launch_fwd(c.bf, c.plan, B, T, H, dk, dv, chunk, c.io, c.lambda, c.S0, c.scale, c.S_final,
+                                     nullptr, ws, stream);
     if (err != hipSuccess || T == 0) return device_status(err);
+    const gla::FwdIO& io = c.io;
+    const gla::Tok sg = ea.sg;
     ea.rq = io.sq.t;
     ea.rk = io.sk.t;
     ea.rv = io.sv.t;
@@ -160,18 +198,29 @@ gla_status fwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int c
                          io.sv.b == (long long)T * io.sv.t && io.so.b == (long long)T * io.so.t &&
                          sg.b == (long long)T * sg.t;
     const int passes = uniform ? 1 : B;
+    const int es = c.bf ? 2 : 4;
     ea.units = (long)(uniform ? B : 1) * T * H;
     for (int b = 0; b < passes && err == hipSuccess; ++b) {
         gla::EpilogueArgs eb = ea;
-        eb.q = static_cast<const char*>(q) + b * io.sq.b * es;
-        eb.k = static_cast<const char*>(k) + b * io.sk.b * es;
-        eb.v = static_cast<const char*>(v) + b * io.sv.b * es;
-        eb.o = static_cast<const char*>(o) + b * io.so.b * es;
-        eb.y = static_cast<char*>(o) + b * io.so.b * es;
-        eb.g = static_cast<const char*>(g) + b * sg.b * es;
-        err = gla::launch_epilogue(bf, dk, dv, eb, stream);
+        eb.q = static_cast<const char*>(io.q) + b * io.sq.b * es;
+        eb.k = static_cast<const char*>(io.k) + b * io.sk.b * es;
+        eb.v = static_cast<const char*>(io.v) + b * io.sv.b * es;
+        eb.o = static_cast<const char*>(io.o) + b * io.so.b * es;
+        eb.y = static_cast<char*>(io.o) + b * io.so.b * es;
+        eb.g = static_cast<const char*>(ea.g) + b * sg.b * es;
+        err = gla::launch_epilogue(c.bf, dk, dv, eb, stream);
     }
     return device_status(err);
+}
+
+gla_status fwd_entry(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q, const void* k,
+                     const void* v, const float* lambda, const float* S0, float scale, void* o, float* S_final,
+                     bool with_states, void* states, const void* g, const gla_epilogue_params* ep,
+                     const gla_strides* st, const gla_plan* plan_in, void* ws, size_t ws_bytes, hipStream_t stream) {
+    FwdCall c;
+    const gla_status s = fwd_prepare(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, o, S_final,
+                                     with_states, states, g, ep, st, plan_in, &c);
+    return s != GLA_OK ? s : fwd_run(c, ws, ws_bytes, stream);
 }
 
 size_t fwd_ws_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const gla_plan* plan_in) {
@@ -222,7 +271,54 @@ size_t bwd_ws_bytes(gla_dtype dtype, int B, int T, int H, int dk, int dv, int ch
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free forward
+//
+// gla_fwd_chunked_noalloc keeps the forward's workspace in this fixed device
+// array instead of caller memory.  Every device the library runs on holds its
+// own copy for the life of the process; host code never uses the array's name
+// as an address (it is a host-side stand-in): it asks the runtime for each
+// device's address once and passes that to the kernels.
+constexpr size_t kScratchBytes = (size_t)GLA_NOALLOC_WORKSPACE_MAX;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device: the address of `scratch` there
+
+// The scratch array's address on the current device (looked up on the first
+// call on that device, with it current).
+gla_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GLA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GLA_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+gla_status gla_fwd_chunked_noalloc(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, const void* q,
+                                   const void* k, const void* v, const float* lambda, const float* S0, float scale,
+                                   void* o, float* S_final, const gla_strides* st, void* stream) {
+    FwdCall c;
+    gla_status s = fwd_prepare(dtype, B, T, H, dk, dv, chunk, q, k, v, lambda, S0, scale, o, S_final, false, nullptr,
+                               nullptr, nullptr, st, nullptr, &c);
+    if (s != GLA_OK) return s;
+    if (c.plan.ws_bytes > kScratchBytes) return GLA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (c.plan.ws_bytes > 0 && T > 0 && (s = scratch_on_current_device(&ws)) != GLA_OK) return s;
+    // (the forward writes every workspace byte it reads before reading it: no clearing)
+    return fwd_run(c, ws, kScratchBytes, static_cast<hipStream_t>(stream));
+}
 
 int gla_abi_version(void) { return 4; }
 

@@ -127,6 +127,30 @@ gla_status gla_fwd_chunked(gla_dtype dtype, int B, int T, int H, int dk, int dv,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gla_fwd_chunked for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace argument and calls no allocating routine: the workspace
+ * is a fixed GLA_NOALLOC_WORKSPACE_MAX-byte device array inside the library,
+ * one per GPU, held until the process ends.  Sizes whose
+ * gla_fwd_workspace_bytes exceeds that limit return GLA_ERR_WORKSPACE (before
+ * any HIP call); that admits, among others, the Laplace layer (B=1, T=2,048:
+ * 9.4 MB), the training width (B=8, T=2,048: 28.3 MB) and the 64k-token
+ * prefill (B=1, T=65,536: 26.5 MB).  All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * give wrong results; calls ordered on one stream are safe.  The array keeps
+ * the last call's contents; the forward writes every workspace byte it reads
+ * before reading it, so nothing needs clearing.  Results equal
+ * gla_fwd_chunked's bit for bit.  GLA_ERR_DEVICE if the array's address cannot
+ * be found on the current device.
+ */
+#define GLA_NOALLOC_WORKSPACE_MAX (32u << 20)
+
+gla_status gla_fwd_chunked_noalloc(gla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                                   const void* q, const void* k, const void* v,
+                                   const float* lambda, const float* S0, float scale,
+                                   void* o, float* S_final, const gla_strides* st, void* stream);
+
+/*
  * Workspace needed by gla_bwd_chunked (bytes; 0 for unsupported/invalid sizes).
  * Holds the per-chunk state snapshots (2 * B*H*ceil(T/chunk)*dk*dv elements of
  * the input dtype), segment states and the dlambda partials.

@@ -291,6 +291,28 @@ def test_plan_controls_validate_and_resolve():
         lib.gla_bwd_states_workspace_bytes(1, 8, 2048, 16, 96, 192, 64)
 
 
+def test_noalloc_forward_limits_checked_on_the_host():
+    """gla_fwd_chunked_noalloc: the usual argument errors, and a size whose workspace
+    exceeds the fixed scratch array is refused with GLA_ERR_WORKSPACE, all before any
+    HIP call (no device is touched here)."""
+    lib = gla.load()
+
+    def n(dtype=1, B=1, T=256, H=16, C=128, q=P, o=P):
+        return lib.gla_fwd_chunked_noalloc(dtype, B, T, H, 96, 192, C, q, P, P, P, None, 1.0, o, None, None, None)
+
+    assert n(dtype=9) == gla.GLA_ERR_INVALID_ARG
+    assert n(C=32) == gla.GLA_ERR_UNSUPPORTED
+    assert n(q=None) == gla.GLA_ERR_INVALID_ARG
+    assert n(o=MIS) == gla.GLA_ERR_INVALID_ARG
+    # B=6, H=20, T=2048: four segments, 39.8 MB of workspace > 32 MiB
+    need = lib.gla_fwd_workspace_bytes(1, 6, 2048, 20, 96, 192, 128)
+    assert need > gla.NOALLOC_WORKSPACE_MAX
+    assert n(B=6, T=2048, H=20) == gla.GLA_ERR_WORKSPACE
+    # the workloads it is for fit: the layer, the training width, the 64k prefill
+    for B, T in ((1, 2048), (8, 2048), (1, 65536)):
+        assert 0 < lib.gla_fwd_workspace_bytes(1, B, T, 16, 96, 192, 128) <= gla.NOALLOC_WORKSPACE_MAX
+
+
 def test_binding_rejects_cpu_tensors_before_the_library():
     """A host tensor handed to a GPU kernel would fault the device: the binding raises
     before any library call."""
