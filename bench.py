@@ -95,6 +95,7 @@ CONV_D = 3072
 # the C ABI, which picks the launch plan): a change elsewhere leaves them valid.
 DIGEST_FILES = {
     "fwd": ["gla_fwd.hip", "gla_fwd_bf16.hip"],
+    "long": ["gla_fwd.hip", "gla_fwd_bf16.hip"],
     "decode": ["gla_decode.hip"],
     "grad": ["gla_grad_bf16.hip", "gla_bwd.hip"],
 }
@@ -138,9 +139,11 @@ def parse():
     ap.add_argument("--counters", action="store_true",
                     help="run a short fixed sequence (copy kernel + each hot kernel) for rocprofv3 --pmc")
     ap.add_argument("--chunk", type=int, default=128)
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter_collection.csv files of the --counters pass "
-                         "(FETCH_SIZE, WRITE_SIZE) into profiles/counters.json")
+    ap.add_argument("--ingest-ktrace", metavar="STATS_CSV",
+                    help="turn rocprofv3 --kernel-trace --stats kernel_stats.csv into profiles/kernel_time_by_kernel.md")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="CSV",
+                    help="turn the rocprofv3 --pmc counter_collection.csv files of the --counters pass "
+                         "(one per COUNTER_PASSES entry) into profiles/counters.json")
     return ap.parse_args()
 
 
@@ -518,82 +521,262 @@ def cpu_baseline_decode(gi, w, seed, budget_s=5.0):
                       f"GB/s counts the fp32 workload's algorithmic bytes"}
 
 
+# rocprofv3 --pmc passes over the --counters sequence: HBM traffic (one counter per run),
+# then SQ counters (at most 8 SQ_ and 2 GRBM_ counters per run)
+COUNTER_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "sq_mfma": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"],
+    "sq_wait": ["SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY",
+                "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_ACTIVE_INST_VALU",
+                "GRBM_GUI_ACTIVE"],
+}
+# groups of the --counters sequence, in launch order; each group is followed by a
+# device copy (a marker between groups, and the traffic calibration)
+COUNTER_GROUPS = ["train", "fwd", "long", "decode"]
+MARKER_BYTES = 1 << 28          # each marker copy reads and writes 256 MiB
+
+
 def counters_pass(torch, gla, gi, chunk):
     """Fixed launch sequence for rocprofv3 --pmc: 3 training steps (mixer-train workload,
-    forward saving chunk states + backward), then a 1 GiB device copy (calibration), then
-    3 forward calls and 3 decode launches on the bench workloads (decode at one layer)."""
+    forward saving chunk states + backward), 3 Laplace-layer forward calls, 3 calls of the
+    64k-token prefill and 3 decode launches (one layer of the serving workload), each group
+    followed by a 256 MiB device copy (the marker between groups and the calibration of
+    the traffic counters)."""
     dev = torch.device("cuda:0")
     ws = gi.workloads()
+    src = torch.empty(MARKER_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def marker():
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
     t = TrainLeg(gla, gi, torch, ws[2], 2, chunk)
     for _ in range(3):
         t()
-    torch.cuda.synchronize()
+    marker()
     del t
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
     f = FwdLeg(gla, gi, torch, ws[1], 1, chunk)
     for _ in range(3):
         f()
-    torch.cuda.synchronize()
+    marker()
+    del f
+    torch.cuda.empty_cache()
+    lg = FwdLeg(gla, gi, torch, ws[3], 3, chunk)
+    for _ in range(3):
+        lg()
+    marker()
+    del lg
+    torch.cuda.empty_cache()
     w4 = ws[4]
     w1 = gi.Workload(w4.name, w4.B, w4.T, w4.H, w4.dk, w4.dv, 0, w4.dtype, w4.lambdas, w4.scale, w4.s0_var, 1)
     d = DecodeLeg(gla, gi, torch, w1, 4, n_inputs=1)
     for s in range(3):
         d.launch(0, s)
-    torch.cuda.synchronize()
-    print(json.dumps({"counters_pass": "done", "copy_bytes_each": 2 * (1 << 30)}), flush=True)
+    marker()
+    print(json.dumps({"counters_pass": "done", "marker_bytes_each": 2 * MARKER_BYTES}), flush=True)
 
 
-def ingest_counters(fetch_csv, write_csv):
-    """Per-dispatch HBM traffic of the hot kernels from the --counters pass, scaled by
-    what the same counters read for the 1 GiB device copy (2 GiB moved) of that pass."""
+ENGINE_GHZ = 2.4    # MI355X peak engine clock: counter cycles per ns of kernel time
+N_SIMD, N_CU = 1024, 256
+
+
+def _read_counter_csv(path):
+    """{dispatch_id: {"kernel": name, "dur_ns": duration, counter: value}} (one row per
+    dispatch and counter, already reduced over the hardware instances)."""
     import csv
 
-    def per_kernel(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        by = {}
-        for r in rows:
-            by.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), 0.0)
-            by[(int(r["Dispatch_Id"]), r["Kernel_Name"])] += float(r["Counter_Value"])
-        return by
+    out = {}
+    for r in csv.DictReader(open(path)):
+        rec = out.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+        rec["dur_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
 
-    out = {"src_digest": src_digest(), "kernels": {}}
+
+def _group_dispatches(disp):
+    """Split the --counters sequence into its groups at the marker copies; returns
+    ({group: [dispatch ids]}, [marker dispatch ids])."""
+    ids = sorted(disp)
+    markers = [d for d in ids if "copy" in disp[d]["kernel"].lower() or "elementwise" in disp[d]["kernel"].lower()]
+    # the markers are the copies that follow a group: the last copy-like dispatch before
+    # each run of library kernels ends
+    lib = lambda d: any(k in disp[d]["kernel"] for k in ("gla", "fwd_", "grad_", "chain_", "seg_scan", "decode_",
+                                                          "dlambda", "rev_scan", "bwd_"))
+    groups, cur, gi_ = {}, [], 0
+    marks = []
+    for d in ids:
+        if lib(d):
+            cur.append(d)
+        elif cur and d in markers:
+            groups[COUNTER_GROUPS[gi_]] = cur
+            marks.append(d)
+            cur, gi_ = [], gi_ + 1
+            if gi_ == len(COUNTER_GROUPS):
+                break
+    return groups, marks
+
+
+def _short_kernel_name(full):
+    """'void gla::(anonymous namespace)::fwd_out_kernel<128, 104, 2, false>(gla::FwdArgs, ...)'
+    -> 'fwd_out_kernel<128, 104, 2, false>'."""
+    import re
+
+    m = re.search(r"(\w+)(<[^()]*>)?\(", full)
+    return (m.group(1) + (m.group(2) or "")) if m else full
+
+
+def ingest_counters(csvs):
+    """Per-dispatch counters of the --counters pass -> profiles/counters.json: HBM traffic
+    per call of each group (FETCH_SIZE and WRITE_SIZE scaled by what they read for the
+    256 MiB marker copies), and per-kernel SQ summaries (MFMA busy, LDS activity, bank
+    conflicts, waits) for every kernel of the sequence."""
+    data = {}
+    for path in csvs:
+        pas = os.path.basename(os.path.dirname(path))
+        for d, rec in _read_counter_csv(path).items():
+            dst = data.setdefault(d, {"kernel": rec["kernel"], "dur_ns": {}})
+            dst["dur_ns"][pas] = rec["dur_ns"]
+            dst.update({k: v for k, v in rec.items() if k not in ("kernel", "dur_ns")})
+    groups, marks = _group_dispatches(data)
+    out = {"src_digest": src_digest(), "groups": {}, "kernels": {}}
     fac = {}
-    vals = {}
-    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
-        by = per_kernel(path, counter)
-        copies = [(d, v) for (d, name), v in by.items() if "copy" in name.lower() and v > 0]
-        ref = max(v for d, v in copies)  # the 1 GiB copy: reads 1 GiB, writes 1 GiB (counters in KiB)
-        first_copy = min(d for d, v in copies if v >= 0.9 * ref)  # (other copies: torch's input casts)
-        fac[counter] = (1 << 30) / (ref * 1024.0)
-        # the training steps run before the copies, the forward and decode calls after them
-        groups = {"fwd": (["fwd_bf16_kernel", "seg_scan", "fwd_chain_kernel", "fwd_out_kernel"], False),
-                  "decode": (["decode_kernel"], False), "grad": (["grad_fused_bf16"], True)}
-        for key, (pats, before) in groups.items():
-            # per call: sum over the kernels one call launches, averaged over the 3 calls
-            sel = [(d, v) for (d, name), v in by.items() if any(pt in name for pt in pats)
-                   and (d < first_copy) == before]
-            vals.setdefault(key, {})[counter] = sum(v for d, v in sel) / 3.0 * 1024.0 * fac[counter]
-            vals[key]["dispatches"] = len(sel)
-    for key, v in vals.items():
-        out["kernels"][key] = {"src_digest": src_digest(key), "fetch_bytes_per_launch": v["FETCH_SIZE"],
-                               "write_bytes_per_launch": v["WRITE_SIZE"],
-                               "hbm_bytes_per_launch": v["FETCH_SIZE"] + v["WRITE_SIZE"],
-                               "dispatches_in_3_calls": v["dispatches"]}
-    out["copy_calibration"] = {"fetch_factor": fac["FETCH_SIZE"], "write_factor": fac["WRITE_SIZE"]}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = [data[m][counter] for m in marks if counter in data[m]]
+        if vals:   # counters in KiB; the copy reads and writes MARKER_BYTES each
+            fac[counter] = MARKER_BYTES / (sorted(vals)[len(vals) // 2] * 1024.0)
+    out["copy_calibration"] = {"fetch_factor": fac.get("FETCH_SIZE"), "write_factor": fac.get("WRITE_SIZE"),
+                               "marker_bytes_read_and_written": MARKER_BYTES}
+    digest_of = {"train": "grad", "fwd": "fwd", "long": "fwd", "decode": "decode"}
+    for g, ids in groups.items():
+        calls = 3.0
+        rec = {"src_digest": src_digest(digest_of[g]), "dispatches": len(ids)}
+        if fac:
+            fb = sum(data[d].get("FETCH_SIZE", 0.0) for d in ids) / calls * 1024.0 * fac["FETCH_SIZE"]
+            wb = sum(data[d].get("WRITE_SIZE", 0.0) for d in ids) / calls * 1024.0 * fac["WRITE_SIZE"]
+            rec.update({"fetch_bytes_per_call": fb, "write_bytes_per_call": wb, "hbm_bytes_per_call": fb + wb})
+        # per kernel inside the group
+        per = {}
+        for d in ids:
+            per.setdefault(_short_kernel_name(data[d]["kernel"]), []).append(d)
+        rec["kernels"] = {}
+        for name, ds in per.items():
+            kr = {"dispatches_per_call": len(ds) / calls}
+            if fac:
+                kr["hbm_bytes_per_dispatch"] = sum(data[d].get("FETCH_SIZE", 0.0) * fac["FETCH_SIZE"] +
+                                                   data[d].get("WRITE_SIZE", 0.0) * fac["WRITE_SIZE"]
+                                                   for d in ds) * 1024.0 / len(ds)
+            tot = lambda c: sum(data[d].get(c, 0.0) for d in ds)
+            # kernel time of the dispatches in the run that read a counter (each
+            # dispatch runs alone while counters are collected)
+            dur = lambda pas: sum(data[d]["dur_ns"].get(pas, 0.0) for d in ds)
+            kr["avg_us"] = sum(dur(p) for p in data[ds[0]]["dur_ns"]) / len(data[ds[0]]["dur_ns"]) / len(ds) / 1e3
+            if dur("sq_mfma") > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in data[ds[0]]:
+                kr["mfma_busy_pct"] = 100.0 * tot("SQ_VALU_MFMA_BUSY_CYCLES") / (dur("sq_mfma") * ENGINE_GHZ * N_SIMD)
+            if dur("sq_wait") > 0 and "SQ_LDS_IDX_ACTIVE" in data[ds[0]]:
+                kr["lds_active_pct"] = 100.0 * tot("SQ_LDS_IDX_ACTIVE") / (dur("sq_wait") * ENGINE_GHZ * N_CU)
+                kr["lds_bank_conflict_pct_of_lds_active"] = (100.0 * tot("SQ_LDS_BANK_CONFLICT") /
+                                                             max(tot("SQ_LDS_IDX_ACTIVE"), 1.0))
+            for c in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+                      "SQ_WAVES"):
+                if tot(c):
+                    kr[c.lower() + "_per_dispatch"] = tot(c) / len(ds)
+            if tot("SQ_INSTS_MFMA"):
+                kr["valu_per_mfma"] = tot("SQ_INSTS_VALU") / tot("SQ_INSTS_MFMA")
+            if tot("SQ_WAVE_CYCLES"):
+                for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                          "SQ_ACTIVE_INST_VALU"):
+                    if tot(c):
+                        kr[c.lower() + "_pct_of_wave_cycles"] = 100.0 * tot(c) / tot("SQ_WAVE_CYCLES")
+            rec["kernels"][name] = kr
+        out["groups"][g] = rec
+    # traffic per group under the keys the bench reads
+    for g, key in (("fwd", "fwd"), ("long", "long"), ("decode", "decode")):
+        if g in out["groups"] and "hbm_bytes_per_call" in out["groups"][g]:
+            r = out["groups"][g]
+            out["kernels"][key] = {"src_digest": r["src_digest"], "hbm_bytes_per_launch": r["hbm_bytes_per_call"],
+                                   "fetch_bytes_per_launch": r["fetch_bytes_per_call"],
+                                   "write_bytes_per_launch": r["write_bytes_per_call"]}
+    tr = out["groups"].get("train", {}).get("kernels", {})
+    for name, kr in tr.items():
+        if name.startswith("grad_fused") and "hbm_bytes_per_dispatch" in kr:
+            out["kernels"]["grad"] = {"src_digest": src_digest("grad"),
+                                      "hbm_bytes_per_launch": kr["hbm_bytes_per_dispatch"]}
     with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
         json.dump(out, f, indent=1)
+    write_counter_summary(out)
     print(json.dumps(out, indent=1))
+
+
+COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 170 rocprofv3 --pmc {counters} -f csv "
+               "-d gpurun_out/pmc/{name} -o pmc -- python3 bench.py --counters")
+GROUP_DESC = {"train": "training step, B=8 H=16 T=2048 C=128 (saved-state pair)",
+              "fwd": "Laplace-layer forward, B=1 H=16 T=2048 C=128",
+              "long": "64k-token prefill, B=1 H=16 T=65536 C=128, S0 given",
+              "decode": "decode, 1,280 sequences x H=16, one layer"}
+
+
+def write_counter_summary(out):
+    """profiles/counters_by_kernel.md: the per-kernel table of counters.json."""
+    lines = ["# rocprofv3 counters per kernel (bench.py --counters sequence)", "",
+             "Commands (one run per counter set, the sets of bench.COUNTER_PASSES):", ""]
+    for name, cs in COUNTER_PASSES.items():
+        lines.append("    " + COUNTER_CMD.format(counters=" ".join(cs), name=name))
+    lines += ["", "then `python bench.py --ingest-counters gpurun_out/pmc/{fetch,write,sq_mfma,sq_wait}/"
+                  "pmc_counter_collection.csv`.", "",
+              "HBM bytes: FETCH_SIZE x %.3f + WRITE_SIZE x %.3f (the factors that make the 256 MiB marker "
+              "copies read and write 256 MiB). Utilisations: counter / (dispatch time x %.1f GHz x units) with "
+              "units = %d SIMDs (MFMA busy) or %d CUs (LDS active); waits and VMEM activity as a share of wave "
+              "cycles. Source digest %s." % (out["copy_calibration"]["fetch_factor"] or 0,
+                                              out["copy_calibration"]["write_factor"] or 0, ENGINE_GHZ, N_SIMD,
+                                              N_CU, out["src_digest"]), ""]
+    for g, r in out["groups"].items():
+        lines += [f"## {GROUP_DESC.get(g, g)}", "",
+                  f"HBM per call: {r.get('hbm_bytes_per_call', 0) / 1e6:.1f} MB over {r['dispatches']} dispatches "
+                  f"(3 calls).", "",
+                  "| kernel | us | HBM MB | MFMA busy % | LDS active % | bank conflicts % of LDS | VALU/MFMA | "
+                  "wait % | MFMA insts | LDS insts |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for k, kr in r["kernels"].items():
+            lines.append("| `%s` | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f | %.1f | %.3g | %.3g |" % (
+                k, kr.get("avg_us", 0), kr.get("hbm_bytes_per_dispatch", 0) / 1e6, kr.get("mfma_busy_pct", 0),
+                kr.get("lds_active_pct", 0), kr.get("lds_bank_conflict_pct_of_lds_active", 0),
+                kr.get("valu_per_mfma", 0), kr.get("sq_wait_inst_any_pct_of_wave_cycles", 0),
+                kr.get("sq_insts_mfma_per_dispatch", 0), kr.get("sq_insts_lds_per_dispatch", 0)))
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", "counters_by_kernel.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
+def ingest_ktrace(stats_csv):
+    """profiles/kernel_time_by_kernel.md from rocprofv3 --kernel-trace --stats of a bench run."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel time per kernel (rocprofv3 --kernel-trace --stats of a bench run)", "",
+             "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 200 rocprofv3 --kernel-trace --stats -f csv "
+             "-d gpurun_out/pmc/ktrace -o kt -- python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline", "",
+             "(source digest %s; every leg of the bench, so a kernel's average mixes the workloads that "
+             "launch it: fwd_bf16_kernel<128, ...> runs in the training step's forward and in the 64k prefill)"
+             % src_digest(), "", "| kernel | calls | average us | min us | max us | share of GPU time % |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %s |" % (
+            _short_kernel_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, r["Percentage"][:5]))
+    with open(os.path.join(ROOT, "profiles", "kernel_time_by_kernel.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def main():
     args = parse()
     if args.ingest_counters:
-        ingest_counters(*args.ingest_counters)
+        ingest_counters(args.ingest_counters)
+        return
+    if args.ingest_ktrace:
+        ingest_ktrace(args.ingest_ktrace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the mixer's hot path is single-GPU here); got --gpus {args.gpus}",
@@ -663,7 +846,8 @@ def main():
         "calls": max(K // 4, 8), "avg_call_us": l_avg * 1e6, "tokens_per_s": lleg.tokens / l_avg,
         "plan": gla.plan_resolve(gla.GLA_BF16, 1, w3.T, 16, 96, 192, args.chunk),
         "roofline": {"bound": "hbm", "achieved": l_bytes / l_avg / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": l_bytes / l_avg / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": l_bytes,
+                     "frac": l_bytes / l_avg / 1e9 / HBM_PEAK_GBS, "traffic": stored_traffic("long", l_bytes),
+                     "alg_bytes_per_launch": l_bytes,
                      "alg_flops_per_launch": l_flops, "mfma_tflops": l_flops / l_avg / 1e12,
                      "mfma_frac": l_flops / l_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}}
     del lleg
