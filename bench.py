@@ -857,7 +857,7 @@ def main():
     w2 = ws[2]
     t_ms = 0.0
     result["train"] = {}
-    for C in (() if args.no_train else (128, 64)):
+    for C in (() if args.no_train else (128, 64, 32)):
         tleg = TrainLeg(gla, gi, torch, w2, 2, C)
         t_wall, t_gpu = time_region(torch, tleg.stream, tleg, K, W)
         t_avg = t_gpu / K

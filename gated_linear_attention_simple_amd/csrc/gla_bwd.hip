@@ -608,7 +608,7 @@ __global__ void bwd_empty_kernel(const float* __restrict__ dST, float* __restric
 // ---------------------------------------------------------------- host side
 
 bool bwd_supported(bool bf16_io, int dk, int dv, int chunk) {
-    return bf16_io ? (dk == 96 && dv == 192 && (chunk == 128 || chunk == 64))
+    return bf16_io ? (dk == 96 && dv == 192 && (chunk == 128 || chunk == 64 || chunk == 32))
                    : (dk == 16 && dv == 32 && chunk == 32);
 }
 
@@ -774,6 +774,9 @@ hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, in
                                                 stream);
     if (bf16_io && dk == 96 && dv == 192 && chunk == 64)
         return launch_bwd_t<bf16, 96, 192, 64>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
+                                               stream);
+    if (bf16_io && dk == 96 && dv == 192 && chunk == 32)
+        return launch_bwd_t<bf16, 96, 192, 32>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
                                                stream);
     if (!bf16_io && dk == 16 && dv == 32 && chunk == 32)
         return launch_bwd_t<float, 16, 32, 32>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,

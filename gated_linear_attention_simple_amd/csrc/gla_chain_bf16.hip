@@ -1,5 +1,5 @@
 // gla_chain_bf16.hip -- the backward's chunk-state chains for bf16 q/k/v/do
-// (dk = 96, dv = 192, chunks of 64 or 128 tokens) on gfx950.
+// (dk = 96, dv = 192, chunks of 32, 64 or 128 tokens) on gfx950.
 //
 // Laplace 3B post, sections "Challenge 1" and "Challenge 3": the chunked
 // backward needs, for every chunk c, the state entering it (Sbar_c) and the
@@ -192,6 +192,7 @@ hipError_t launch_chain_bf16(int chunk, bool rev, bool emit, const StateArgs& s,
     }
     GLA_CHAIN(128)
     GLA_CHAIN(64)
+    GLA_CHAIN(32)
 #undef GLA_CHAIN
     return hipErrorInvalidValue;
 }

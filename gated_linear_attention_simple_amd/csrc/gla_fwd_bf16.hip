@@ -1,5 +1,5 @@
 // gla_fwd_bf16.hip -- chunked-parallel GLA forward for bf16 q/k/v on gfx950
-// (dk = 96, dv = 192, chunks of 64 or 128 tokens).
+// (dk = 96, dv = 192, chunks of 32, 64 or 128 tokens).
 //
 // Method: Laplace 3B post, section "Challenge 1" (chunked GLA).  For chunk c
 // of C tokens with start state S (positions i, j in [0, C); b_i = lam^(i+1),
@@ -69,8 +69,8 @@ struct F8 {
 
 // Score blocks of wave w (slot k), packed 16 * ib + jb, or -1 for an empty slot.
 // Each wave's blocks lie in at most two query strips, so per k-step it reads
-// at most two query fragments; the sets balance the 36 (C = 128) or 10
-// (C = 64) blocks of the lower triangle over the NW waves.  The first
+// at most two query fragments; the sets balance the 36 (C = 128), 10 (C = 64)
+// or 3 (C = 32) blocks of the lower triangle over the NW waves.  The first
 // score_lead<C, NW>() slots of every wave lie in its first strip.
 template <int C, int NW>
 __host__ __device__ constexpr int score_block(int w, int k) {
@@ -80,9 +80,12 @@ __host__ __device__ constexpr int score_block(int w, int k) {
                                           {0x50, 0x51, 0x52}, {0x53, 0x54, 0x55}, {0x40, 0x41, 0x42},
                                           {0x43, 0x44, 0x20}, {0x21, 0x22, 0x30}, {0x31, 0x32, 0x33}};
         return t[w][k];
-    } else {
-        static_assert(C == 64 && NW == 12, "score block table");
+    } else if constexpr (C == 64 && NW == 12) {
         constexpr signed char t[12] = {0x30, 0x31, 0x32, 0x33, 0x20, 0x21, 0x22, 0x10, 0x11, 0x00, -1, -1};
+        return k == 0 ? t[w] : -1;
+    } else {
+        static_assert(C == 32 && NW == 12, "score block table");
+        constexpr signed char t[12] = {0x10, 0x11, 0x00, -1, -1, -1, -1, -1, -1, -1, -1, -1};
         return k == 0 ? t[w] : -1;
     }
 }
@@ -446,9 +449,12 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                     out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
                     out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
                 }
-            } else {
+            } else if constexpr (C == 64) {
                 if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
                 else out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+            } else {
+                // one 32-row strip: the h = 0 wave of each pair writes it
+                if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
             }
         }
 
@@ -1049,7 +1055,8 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
     a.seg_chunks = plan.seg_chunks;
     a.nc = plan.nc;
     const unsigned units = (unsigned)B * H;
-    if (plan.chain) {
+    if constexpr (C >= 64) {
+      if (plan.chain) {
         // every chunk's start state from the tiled chain, then one output
         // workgroup per chunk
         hipError_t err = launch_chain<C>(plan, B, T, H, NCB, io, lambda, S0, S_final, ws, stream);
@@ -1064,6 +1071,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
             hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, false>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT),
                                0, stream, a, EpilogueArgs{});
         return hipGetLastError();
+      }
     }
     if (ep) return hipErrorNotSupported;   // the epilogue is fused into the chain form only
     if (plan.nseg > 1) {
@@ -1097,6 +1105,8 @@ hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, 
         return launch_c<128, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
     if (chunk == 64)
         return launch_c<64, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
+    if (chunk == 32 && !plan.chain)
+        return launch_c<32, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
     return hipErrorInvalidValue;
 }
 

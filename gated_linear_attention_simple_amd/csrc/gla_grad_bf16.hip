@@ -86,14 +86,16 @@ __device__ __forceinline__ float snap_dot_lds(const Stage& gs, const bf16* S, in
 // their key blocks, which only see queries 64..127, after their dQ blocks).
 template <int C>
 __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
-    static_assert(C == 128 || C == 64, "one or two 64-query halves");
-    constexpr int NSUB = C / kST;
-    constexpr int NKB = C / 16;  // key blocks (waves that own one)
+    static_assert(C == 128 || C == 64 || C == 32, "one or two query halves of at most 64 rows");
+    constexpr int HALF = C < kFHalf ? C : kFHalf;  // query rows per half
+    constexpr int NSUB = C / HALF;                 // halves
+    constexpr int NKB = C / 16;                    // key blocks (waves that own one)
+    constexpr int NQB = HALF / 16;                 // query blocks per half
     __shared__ __align__(16) bf16 Ks[C * kLDK];
     __shared__ __align__(16) bf16 Vs[C * kLDV];
     __shared__ __align__(16) bf16 Xs[kDK * kLDV];            // Sbar, then Gbar
-    __shared__ __align__(16) bf16 Qs[kFHalf * kLDK];         // one half's queries
-    __shared__ __align__(16) bf16 Ds[kFHalf * kLDV];         // and output gradients
+    __shared__ __align__(16) bf16 Qs[HALF * kLDK];           // one half's queries
+    __shared__ __align__(16) bf16 Ds[HALF * kLDV];           // and output gradients
     __shared__ float pw[C + 2], dpw[C + 2];
     __shared__ float red[3][kFNW];
 
@@ -114,8 +116,8 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     const bf16* kb = static_cast<const bf16*>(a.k) + b * a.sk.b + (size_t)t0 * tokK + hd * kDK;
     const bf16* vb = static_cast<const bf16*>(a.v) + b * a.sv.b + (size_t)t0 * tokV + hd * kDV;
     const bf16* db_ = static_cast<const bf16*>(a.d_o) + b * a.sdo.b + (size_t)t0 * tokD + hd * kDV;
-    BufStage<kFHalf, kDK, kFNT> tq;
-    BufStage<kFHalf, kDV, kFNT> td;
+    BufStage<HALF, kDK, kFNT> tq;
+    BufStage<HALF, kDV, kFNT> td;
     {
         BufStage<C, kDK, kFNT> tk;
         BufStage<C, kDV, kFNT> tv;
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         td.template store<kLDV>(Ds, tid);
     }
     // the second half's queries and output gradients, in registers meanwhile
-    if (kFHalf < ceff) {
-        tq.load(qb + (size_t)kFHalf * tokQ, tokQ, ceff - kFHalf, tid);
-        td.load(db_ + (size_t)kFHalf * tokD, tokD, ceff - kFHalf, tid);
+    if (HALF < ceff) {
+        tq.load(qb + (size_t)HALF * tokQ, tokQ, ceff - HALF, tid);
+        td.load(db_ + (size_t)HALF * tokD, tokD, ceff - HALF, tid);
     }
     __syncthreads();
 
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
 #pragma unroll
         for (int p = 0; p < kDV / 32; ++p) vr[p] = op_row8(Vs, kLDV, jb * 16 + n, 32 * p + 8 * g);
 #pragma unroll
-        for (int pr = 0; pr < kFHalf / 32; ++pr) {
+        for (int pr = 0; pr < HALF / 32; ++pr) {
             if (qt0 + 32 * pr + 31 < jb * 16) continue;  // pair entirely above the diagonal (uniform)
             f32x4 Ab[2], Pb[2];
 #pragma unroll
@@ -244,19 +246,22 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         }
     };
 
-    // A: queries 0..63
-    if (wave < 4) key_terms(0);
-    else query_block(0, wave - 4);
+    // A: queries 0 .. HALF-1 (waves past the chunk's key or query blocks idle)
+    if (wave < 4) {
+        if (wave < NKB) key_terms(0);
+    } else if (wave - 4 < NQB) {
+        query_block(0, wave - 4);
+    }
     // B: queries 64..127 (Gbar requested for C meanwhile)
     BufStage<kDK, kDV, kFNT> tg;
-    if (C > kFHalf && kFHalf < ceff) {
+    if (C > HALF && HALF < ceff) {
         __syncthreads();  // half 0 reads are done
         tq.template store<kLDK>(Qs, tid);
         td.template store<kLDV>(Ds, tid);
         __syncthreads();
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
-        if (wave >= 4) query_block(kFHalf, wave - 4);
-        key_terms(kFHalf);
+        if (wave >= 4) query_block(HALF, wave - 4);
+        key_terms(HALF);
     } else {
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
     }
@@ -343,6 +348,8 @@ hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipSt
         hipLaunchKernelGGL(grad_fused_bf16<128>, dim3((unsigned)ga.nc, units), dim3(kFNT), 0, stream, ga);
     else if (chunk == 64)
         hipLaunchKernelGGL(grad_fused_bf16<64>, dim3((unsigned)ga.nc, units), dim3(kFNT), 0, stream, ga);
+    else if (chunk == 32)
+        hipLaunchKernelGGL(grad_fused_bf16<32>, dim3((unsigned)ga.nc, units), dim3(kFNT), 0, stream, ga);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

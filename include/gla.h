@@ -29,7 +29,7 @@
  *   or GLA_BF16 (bfloat16).  States, lambda and every accumulation are fp32.
  *   bf16 outputs are rounded to nearest even.
  * - Supported shapes (instantiated kernels), (dk, dv, chunk):
- *     bf16: (96, 192, 128), (96, 192, 64);   fp32: (96, 192, 64), (16, 32, 32);
+ *     bf16: (96, 192, 128), (96, 192, 64), (96, 192, 32);   fp32: (96, 192, 64), (16, 32, 32);
  *     decode, either dtype: (dk, dv) = (96, 192) or (16, 32).
  *   Anything else returns GLA_ERR_UNSUPPORTED.  T need not be a multiple of
  *   chunk (the last chunk is partial).
@@ -162,7 +162,7 @@ size_t gla_bwd_workspace_bytes(gla_dtype dtype, int B, int T, int H, int dk, int
  * optional dS_final = dL/dS_final, through the forward defined above (Laplace
  * 3B post, section "Challenge 3": the backward differentiates through the
  * sequential chunk-to-chunk state chain, run here in reverse chunk order).
- * Supported shapes: bf16 (96, 192, 128), (96, 192, 64); fp32 (16, 32, 32).
+ * Supported shapes: bf16 (96, 192, 128), (96, 192, 64), (96, 192, 32); fp32 (16, 32, 32).
  *   q, k, v, lambda, S0, scale, chunk   as in gla_fwd_chunked (S0 nullable)
  *   d_o        [B][T][H][dv] (dtype) upstream gradient of o
  *   dS_final   [B][H][dk][dv] fp32 upstream gradient of S_final (NULL = 0)

@@ -55,7 +55,8 @@ def test_fwd_rejects_bad_arguments_before_touching_the_device():
     assert fwd(T=-1) == E.GLA_ERR_INVALID_ARG
     assert fwd(H=0) == E.GLA_ERR_INVALID_ARG
     assert fwd(dk=64) == E.GLA_ERR_UNSUPPORTED
-    assert fwd(C=32) == E.GLA_ERR_UNSUPPORTED
+    assert fwd(C=256) == E.GLA_ERR_UNSUPPORTED                  # 256-row tiles exceed the LDS
+    assert fwd(C=96) == E.GLA_ERR_UNSUPPORTED
     assert fwd(dtype=0, C=128) == E.GLA_ERR_UNSUPPORTED          # fp32 stops at chunk 64
     assert fwd(dtype=1, dk=16, dv=32, C=32) == E.GLA_ERR_UNSUPPORTED
     assert fwd(q=None) == E.GLA_ERR_INVALID_ARG
@@ -301,7 +302,7 @@ def test_noalloc_forward_limits_checked_on_the_host():
         return lib.gla_fwd_chunked_noalloc(dtype, B, T, H, 96, 192, C, q, P, P, P, None, 1.0, o, None, None, None)
 
     assert n(dtype=9) == gla.GLA_ERR_INVALID_ARG
-    assert n(C=32) == gla.GLA_ERR_UNSUPPORTED
+    assert n(C=256) == gla.GLA_ERR_UNSUPPORTED
     assert n(q=None) == gla.GLA_ERR_INVALID_ARG
     assert n(o=MIS) == gla.GLA_ERR_INVALID_ARG
     # B=6, H=20, T=2048: four segments, 39.8 MB of workspace > 32 MiB

@@ -50,17 +50,17 @@ def test_tiny_fp32_ragged_with_states(T):
     _run(gi.workloads()[0], seed=60 + T, B=2, T=T, s0_var=0.5)
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 @pytest.mark.parametrize("T", [1, 100, 300, 1000])
 def test_bf16_ragged_with_states(chunk, T):
     _run(gi.workloads()[1], seed=70 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 @pytest.mark.parametrize("T", [40, 2048])
 def test_single_partial_chunk_and_full_length(chunk, T):
-    """One partial chunk (T = 40: no second query half at either chunk size) and the
-    full 2,048-token sequence, with S0 and dS_T."""
+    """T = 40: one partial chunk with no second query half (chunks 128, 64), one full
+    and one partial chunk (32); and the full 2,048-token sequence, with S0 and dS_T."""
     _run(gi.workloads()[1], seed=1500 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
 
 
@@ -69,9 +69,9 @@ def test_bf16_segment_split(nseg):
     _run(gi.workloads()[1], seed=90 + nseg, B=1, T=1000, chunk=64, s0_var=0.01, plan={"segments": nseg})
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 def test_train_step_config(chunk):
-    """B=8, H=16, T=2048, dk=96, dv=192, bf16, do ~ N(0,1); C=128 and C=64."""
+    """B=8, H=16, T=2048, dk=96, dv=192, bf16, do ~ N(0,1); C=128, 64 and 32."""
     _run(gi.workloads()[2], seed=2, chunk=chunk, with_dS=False)
 
 
@@ -145,7 +145,7 @@ def test_saved_states_and_backward_match_oracle(wi, B, T, chunk, chain):
     assert_close(f64(dl), r[3], w.dtype, "dlambda", batch_axis=None)
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 def test_saved_states_training_width(chunk):
     """The bench's training legs exactly: gla_fwd_chunked_states + gla_bwd_chunked_states
     at B=8, H=16, T=2048 (two sequence segments; the state-only prologue over half-length
@@ -171,7 +171,7 @@ def test_saved_states_training_width(chunk):
     assert_close(f64(dl), r[3], "bf16", "dlambda", batch_axis=None)
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 def test_bwd_batch_position_invariant(chunk):
     """Each (batch, head) unit's gradients are computed alone: permuting the batch
     permutes dq, dk, dv and dS0 bit for bit (saved-state pair and recomputing form);
@@ -204,7 +204,7 @@ def test_fwd_bwd_shape_sweep(case):
     rng = np.random.default_rng(9000 + case)
     H = int(rng.choice([1, 3, 5, 16]))
     B = int(rng.choice([1, 2, 3]))
-    chunk = int(rng.choice([64, 128]))
+    chunk = int(rng.choice([32, 64, 128]))
     T = int(rng.choice([1, 63, 64, 129, 255, 384, 513, 777]))
     s0 = 0.01 if rng.random() < 0.5 else None
     lam = tuple(gi.laplace_lambdas(16))[:H] if H < 16 else tuple(gi.laplace_lambdas(16))

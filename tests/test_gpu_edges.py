@@ -53,6 +53,7 @@ FWD_CASES = {
     "layer_chain": (1, 1, 2048, 128, None, 0.01, "chain"),
     "layer_segments": (1, 1, 2048, 128, None, 0.01, "segments"),
     "ragged_c64": (1, 2, 1000, 64, None, 0.01, None),
+    "ragged_c32": (1, 2, 1000, 32, None, 0.01, None),
     "train_width": (2, 8, 2048, 128, None, 0.0, None),
     "fp32_tiny": (0, 2, 250, 32, None, 0.5, None),
     "fp32_wide_c64": (1, 2, 300, 64, "f32", 0.01, None),
@@ -81,6 +82,8 @@ BWD_CASES = {
     "c64": (1, 2, 700, 64, "recompute"),
     "c128_saved": (1, 2, 1000, 128, "saved"),
     "c64_saved": (1, 2, 1500, 64, "saved"),
+    "c32": (1, 2, 700, 32, "recompute"),
+    "c32_saved": (1, 2, 1000, 32, "saved"),
     "fp32_tiny": (0, 2, 200, 32, "recompute"),
 }
 

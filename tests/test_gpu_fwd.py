@@ -57,7 +57,7 @@ def test_laplace_layer_config():
     _run_and_check(gi.workloads()[1], seed=1)
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
+@pytest.mark.parametrize("chunk", [128, 64, 32])
 @pytest.mark.parametrize("T", [1, 100, 300, 1000])
 def test_bf16_ragged_with_state(chunk, T):
     _run_and_check(gi.workloads()[1], seed=100 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
@@ -77,11 +77,12 @@ def test_segment_split_equivalence(nseg):
 PLANS = {"seg1": {"segments": 1, "chain": 0}, "seg3": {"segments": 3, "chain": 0}, "chain": {"chain": 1}}
 
 
-@pytest.mark.parametrize("chunk", [128, 64])
-@pytest.mark.parametrize("mode", sorted(PLANS))
+@pytest.mark.parametrize("chunk,mode", [(c, m) for c in (128, 64, 32) for m in sorted(PLANS)
+                                        if not (c == 32 and m == "chain")])
 def test_bf16_plans(chunk, mode):
     """The bf16 launch plans: unsplit, with sequence segments, and the tiled state
-    chain feeding one output workgroup per chunk; ragged tail, S0."""
+    chain feeding one output workgroup per chunk (built for 64- and 128-token
+    chunks); ragged tail, S0."""
     _run_and_check(gi.workloads()[1], seed=314 + chunk + len(mode), B=2, T=1000, chunk=chunk, s0_var=0.01,
                    plan=PLANS[mode])
 
@@ -143,10 +144,10 @@ def test_prologue_sub_segments(chunk, T, segs, s0):
         assert_close(f64(S), rS, w.dtype, "S_final")
 
 
-def test_train_batch_forward_chunk64_and_128():
-    w = gi.workloads()[2]
-    for chunk in (128, 64):
-        _run_and_check(w, seed=2, chunk=chunk)
+@pytest.mark.parametrize("chunk", [128, 64, 32])
+def test_train_batch_forward(chunk):
+    """The training width (B=8, H=16, T=2048) forward at each chunk size."""
+    _run_and_check(gi.workloads()[2], seed=2, chunk=chunk)
 
 
 def test_long_prefill_split_carry():
@@ -249,7 +250,7 @@ def test_causality():
     assert torch.equal(o[:, :cut], o2[:, :cut])
 
 
-@pytest.mark.parametrize("chunk,chain", [(128, 0), (128, 1), (64, 0)])
+@pytest.mark.parametrize("chunk,chain", [(128, 0), (128, 1), (64, 0), (32, 0)])
 def test_page_decay_schedule(chunk, chain):
     """The pages' geometric half-life schedule (head 0: lambda = 0.5, so lambda^C
     underflows fp32's normal range at C = 128) on the Laplace-layer shape, through

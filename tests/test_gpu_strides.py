@@ -49,6 +49,7 @@ FWD_CASES = {
     "layer_chain": (1, 1, 2048, 128, None, {"chain": 1}),
     "layer_segments": (1, 1, 2048, 128, 0.01, {"chain": 0}),
     "ragged_c64": (1, 2, 1000, 64, 0.01, None),
+    "ragged_c32": (1, 2, 1000, 32, 0.01, None),
     "train_width": (2, 8, 2048, 128, None, None),
     "fp32_wide_c64": (1, 2, 300, 64, 0.01, None),
     "fp32_tiny": (0, 3, 250, 32, 0.5, None),
@@ -83,7 +84,7 @@ def test_forward_reads_fused_projection(case):
 
 
 BWD_CASES = {"c128": (1, 2, 1000, 128, False), "c64_saved": (1, 2, 700, 64, True), "train_c128": (2, 8, 2048, 128, True),
-             "fp32_tiny": (0, 2, 200, 32, False)}
+             "c32_saved": (1, 2, 900, 32, True), "fp32_tiny": (0, 2, 200, 32, False)}
 
 
 @pytest.mark.parametrize("case", sorted(BWD_CASES))
