@@ -79,8 +79,10 @@ class Strides(ctypes.Structure):
 
 
 class Plan(ctypes.Structure):
-    """gla_plan: segments (0 = library), chain (-1 = library, 0, 1), psub (0 = library, 1)."""
-    _fields_ = [("segments", ctypes.c_int), ("chain", ctypes.c_int), ("psub", ctypes.c_int)]
+    """gla_plan: segments (0 = library), chain (-1 = library, 0, 1), psub (0 = library, 1),
+    scan (-1 = library, 0 = scan launch, 1 = folded into the segments)."""
+    _fields_ = [("segments", ctypes.c_int), ("chain", ctypes.c_int), ("psub", ctypes.c_int),
+                ("scan", ctypes.c_int)]
 
 
 class GlaError(RuntimeError):
@@ -195,10 +197,11 @@ def _strides(**tensors) -> Strides:
 
 
 def _plan(plan):
-    """A gla_plan from a dict {segments, chain, psub} (missing keys: the library's choice)."""
+    """A gla_plan from a dict {segments, chain, psub, scan} (missing keys: the library's choice)."""
     if plan is None:
         return None
-    return Plan(int(plan.get("segments", 0)), int(plan.get("chain", -1)), int(plan.get("psub", 0)))
+    return Plan(int(plan.get("segments", 0)), int(plan.get("chain", -1)), int(plan.get("psub", 0)),
+                int(plan.get("scan", -1)))
 
 
 def _ref(p):
@@ -215,7 +218,7 @@ def plan_resolve(dtype: int, B, T, H, dk, dv, chunk, plan=None) -> dict:
     out = Plan()
     _raise(load().gla_plan_resolve(dtype, B, T, H, dk, dv, chunk, _ref(_plan(plan)), ctypes.byref(out)),
            "gla_plan_resolve")
-    return {"segments": out.segments, "chain": out.chain, "psub": out.psub}
+    return {"segments": out.segments, "chain": out.chain, "psub": out.psub, "scan": out.scan}
 
 
 def fwd_workspace_bytes(dtype: int, B, T, H, dk, dv, chunk, plan=None) -> int:

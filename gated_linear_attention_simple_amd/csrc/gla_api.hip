@@ -51,12 +51,12 @@ gla_status bwd_check_shape(gla_dtype dtype, int B, int T, int H, int dk, int dv,
 
 // Plan hint from the caller's gla_plan (NULL: all library choices).
 bool hint_of(const gla_plan* p, gla::PlanHint* h) {
-    *h = gla::PlanHint{0, -1, 0};
+    *h = gla::PlanHint{0, -1, 0, -1};
     if (p == nullptr) return true;
     if (p->segments < 0 || p->segments > gla::kMaxSegments || p->chain < -1 || p->chain > 1 || p->psub < 0 ||
-        p->psub > 1)
+        p->psub > 1 || p->scan < -1 || p->scan > 1)
         return false;
-    *h = gla::PlanHint{p->segments, p->chain, p->psub};
+    *h = gla::PlanHint{p->segments, p->chain, p->psub, p->scan};
     return true;
 }
 
@@ -412,6 +412,7 @@ gla_status gla_plan_resolve(gla_dtype dtype, int B, int T, int H, int dk, int dv
     out->segments = p.nseg;
     out->chain = p.chain;
     out->psub = p.psub;
+    out->scan = p.fuse_scan;
     return GLA_OK;
 }
 

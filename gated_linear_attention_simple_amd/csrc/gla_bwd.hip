@@ -621,6 +621,10 @@ BwdPlan bwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     p.nc = f.nc;
     p.nseg = f.nseg;
     p.seg_chunks = f.seg_chunks;
+    // bf16: with at most kFuseMaxStates local states the emit passes fold them in
+    // (no scan launches)
+    p.fuse_scan = bf16_io && p.nseg > 1 && p.nseg - 1 <= kFuseMaxStates;
+    if (hint && hint->scan == 0) p.fuse_scan = 0;
     p.saved = saved;
     const size_t units = (size_t)B * H;
     const size_t esz = bf16_io ? 2 : 4;
@@ -659,6 +663,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const B
     s.H = H;
     s.lambda = lambda;
     s.U = U;
+    s.fuse_scan = sizeof(E) == 2 ? plan.fuse_scan : 0;   // (the fp32 state passes always scan)
     s.nseg = nseg;
     s.seg_chunks = plan.seg_chunks;
     s.nc = plan.nc;
@@ -693,8 +698,9 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const B
     if (!plan.saved) {   // the forward's chunk start states were not saved: recompute them
         if (nseg > 1) {
             if ((err = chain(false, false, nseg - 1)) != hipSuccess) return err;
-            if ((err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) !=
-                hipSuccess)
+            if (!s.fuse_scan &&
+                (err = launch_seg_scan(S0, U, lambda, H, nseg, plan.seg_chunks * C, dkdv, units, stream)) !=
+                    hipSuccess)
                 return err;
         }
         if ((err = chain(false, true, nseg)) != hipSuccess) return err;
@@ -712,9 +718,11 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const B
     s.part = part;
     if (nseg > 1) {
         if ((err = chain(true, false, nseg - 1)) != hipSuccess) return err;
-        hipLaunchKernelGGL(rev_scan_kernel, dim3((dkdv / 4 + 255) / 256, units), dim3(256), 0, stream, dST, U, lambda,
-                           H, nseg, plan.seg_chunks * C, T, dkdv);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if (!s.fuse_scan) {
+            hipLaunchKernelGGL(rev_scan_kernel, dim3((dkdv / 4 + 255) / 256, units), dim3(256), 0, stream, dST, U,
+                               lambda, H, nseg, plan.seg_chunks * C, T, dkdv);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
     }
     if ((err = chain(true, true, nseg)) != hipSuccess) return err;
 

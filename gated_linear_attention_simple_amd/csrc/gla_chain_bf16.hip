@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     };
     const float* Sin = nullptr;
     if constexpr (EMIT) {
-        if (!REV) Sin = seg == 0 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg - 1) * kDK * kDV;
+        if (a.fuse_scan) Sin = a.S_edge;  // the local states are folded in below
+        else if (!REV) Sin = seg == 0 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg - 1) * kDK * kDV;
         else Sin = seg == a.nseg - 1 ? a.S_edge : a.U + ((size_t)bh * (a.nseg - 1) + seg) * kDK * kDV;
         if (Sin && Sin == a.S_edge) Sin += (size_t)bh * kDK * kDV;
     }
@@ -86,6 +87,26 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
         for (int cb = 0; cb < kNCB; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sacc[i][cb][r] = Sin ? Sin[sidx(i, cb, r)] : 0.f;
+    if constexpr (EMIT) {
+        if (a.fuse_scan) {
+            // Fold the local passes' states of the segments this one continues, in the
+            // scan kernels' order (the same bits): forward from S0 over segments
+            // 0 .. seg-1, reverse from dS_T over segments nseg-1 down to seg+1.
+            const float* u = a.U + (size_t)bh * (a.nseg - 1) * kDK * kDV;
+            const int seg_tokens = a.seg_chunks * C;
+            for (int k = 0; k < (REV ? a.nseg - 1 - seg : seg); ++k) {
+                const int s = REV ? a.nseg - 1 - k : k;   // segment folded in
+                const float f = REV ? pow_int(lam, min(seg_tokens, T - s * seg_tokens)) : pow_int(lam, seg_tokens);
+                const float* x = u + (size_t)(REV ? s - 1 : s) * kDK * kDV;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < kNCB; ++cb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Sacc[i][cb][r] = fmaf(f, Sacc[i][cb][r], x[sidx(i, cb, r)]);
+            }
+        }
+    }
 
     RowStage<C, kDK, kNT> tx;
     RowStage<C, kDV, kNT> ty;

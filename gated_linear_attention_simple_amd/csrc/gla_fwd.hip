@@ -344,6 +344,11 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     // (the tiled chain and its output kernel are built for 64- and 128-token chunks)
     if (hint && hint->chain == 1 && bf16_io && chunk >= 64 && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
     if (p.chain) p.ws_bytes = (size_t)units * p.nc * dk * dv * 2;  // every chunk's start state, bf16
+    // bf16 segments with at most kFuseMaxStates local states before the last segment
+    // (e.g. two segments with the sub-segment prologue): no scan launch, each segment
+    // folds them into its start state in the scan's order (same bits)
+    p.fuse_scan = bf16_io && !p.chain && p.nseg > 1 && (p.nseg - 1) * p.psub <= kFuseMaxStates;
+    if (hint && hint->scan == 0) p.fuse_scan = 0;
     return p;
 }
 

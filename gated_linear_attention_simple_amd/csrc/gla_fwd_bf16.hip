@@ -294,6 +294,32 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_bf16_kernel(FwdA
                     for (int r = 0; r < 4; ++r)
                         Sacc[i][cb][r] = __builtin_bit_cast(
                             float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * sidx(i, cb, r), 0, 0));
+        } else if (a.fuse_scan) {
+            // Fold the prologue's local states of sub-segments 0 .. seg*psub-1 into the
+            // start state from S0 (or 0), in the scan kernel's order: the same bits.
+            const float* s0 = a.S0 ? a.S0 + (size_t)bh * kDK * kDV : a.lambda;
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s0), 0,
+                                                              a.S0 ? kDK * kDV * 4 : 0, kBufWord3);
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Sacc[i][cb][r] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * sidx(i, cb, r), 0, 0));
+            const float lamL = pow_int(a.lambda[hd], a.seg_chunks / a.psub * C);
+            const f32x4* u = reinterpret_cast<const f32x4*>(a.U + (size_t)bh * (a.nseg - 1) * a.psub * kDK * kDV);
+            for (int j = 0; j < seg * a.psub; ++j) {
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const f32x4 x = u[(size_t)j * (kDK * kDV / 4) + fidx(i, cb)];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Sacc[i][cb][e] = fmaf(lamL, Sacc[i][cb][e], x[e]);
+                    }
+            }
         } else {
             // (the scanned state at the segment's start: sub-segment boundary seg * psub)
             const size_t st = ((size_t)bh * (a.nseg - 1) * a.psub + (seg * a.psub - 1)) * kDK * kDV;
@@ -1050,6 +1076,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
     a.Ub = static_cast<char*>(ws) +
            (size_t)B * H * (plan.nseg > 1 ? plan.nseg - 1 : 0) * plan.psub * kDK * kDV * sizeof(float);
     a.psub = plan.psub;
+    a.fuse_scan = plan.fuse_scan;
     a.sbar = sbar;
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
@@ -1085,11 +1112,13 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
                            0, stream, pa);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(seg_scan_frag_kernel<NCB>, dim3((kDK * kDV / 4 + 255) / 256, units), dim3(256), 0, stream,
-                           S0, a.U, static_cast<bf16*>(a.Ub), lambda, H, pa.nseg, plan.seg_chunks,
-                           pa.seg_chunks * C, S_final != nullptr ? 1 : 0);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if (!plan.fuse_scan) {
+            hipLaunchKernelGGL(seg_scan_frag_kernel<NCB>, dim3((kDK * kDV / 4 + 255) / 256, units), dim3(256), 0,
+                               stream, S0, a.U, static_cast<bf16*>(a.Ub), lambda, H, pa.nseg, plan.seg_chunks,
+                               pa.seg_chunks * C, S_final != nullptr ? 1 : 0);
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
     }
     hipLaunchKernelGGL((fwd_bf16_kernel<C, LDK, NCB, false>), dim3(plan.nseg, units), dim3(F8<C, LDK, NCB>::NT), 0,
                        stream, a);

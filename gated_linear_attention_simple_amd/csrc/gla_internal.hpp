@@ -35,6 +35,7 @@ struct FwdArgs {
     void* sbar;        // optional: every chunk's start state, [B*H][nc][DK][DV] in the input dtype
     int nseg, seg_chunks, nc;
     int psub;          // segment states in U per segment boundary (sub-segment prologue), >= 1
+    int fuse_scan;     // 1: U holds the prologue's local states; each segment folds them itself
 };
 
 struct FwdPlan {
@@ -43,6 +44,8 @@ struct FwdPlan {
     int seg_chunks;  // chunks per segment (the last segment may hold fewer)
     int psub;        // bf16 segments: the state-only prologue runs psub sub-segments per segment
     int chain;       // bf16 path: tiled state chain + per-chunk output instead of segments
+    int fuse_scan;   // bf16 segments: no scan launch; each segment folds the (at most
+                     // kFuseMaxStates) local states before it into its start state
     size_t ws_bytes; // segments: B*H*(nseg-1)*dk*dv fp32 (+ as many bf16 on the bf16 path);
                      // chain: B*H*nc*dk*dv bf16 chunk start states
 };
@@ -57,7 +60,12 @@ struct PlanHint {
     int nseg;   // sequence segments, 1 .. kMaxSegments (0: default)
     int chain;  // 0: segment split, 1: tiled chain where it can run (-1: default)
     int psub;   // 1: one prologue workgroup per segment (0: default)
+    int scan;   // 0: a scan launch between the state passes, 1: folded where allowed (-1: default)
 };
+
+// A segment folds the local states before it into its start state itself (no
+// scan launch) when there are at most this many.
+constexpr int kFuseMaxStates = 2;
 
 // Token-major operands of one forward call (pointers and their strides).
 struct FwdIO {
@@ -111,6 +119,7 @@ struct StateArgs {
     const void* sbar;     // fp32 reverse emit pass: the forward snapshots (for <Gbar, Sbar>)
     float* part;          // fp32 reverse emit pass: dlam partials (slot 0)
     int nseg, seg_chunks, nc;
+    int fuse_scan;        // emit passes: U holds the local passes' states, folded here
 };
 
 // bf16 chains (dk = 96, dv = 192, chunk 64 or 128); grid (grid_x, units).
@@ -140,6 +149,7 @@ hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipSt
 
 struct BwdPlan {
     int nc, nseg, seg_chunks;
+    int fuse_scan;      // bf16: the emit passes fold the local states (no scan launches)
     bool saved;         // chunk start states come from the forward (no state snapshot array here)
     size_t snap_bytes;  // per-chunk snapshots: state gradients (and, unless saved, states)
     size_t u_bytes;     // segment states (fp32)

@@ -29,18 +29,24 @@ extern "C" {
  *             chunk), used where it can run (2 .. 64 chunks)
  *   psub      1 = one prologue workgroup per segment (the library may run the
  *             bf16 prologue over half-length sub-segments instead)
+ *   scan      -1 = the library's choice; 0 = a scan launch turns the segments'
+ *             local states into start states; 1 = (bf16, at most 2 local states
+ *             before the last segment) no scan launch: each segment folds them
+ *             into its start state in the scan's order, with the same bits
  * Out-of-range fields give GLA_ERR_INVALID_ARG (size queries: 0).
  */
 typedef struct {
     int segments;
     int chain;
     int psub;
+    int scan;
 } gla_plan;
 
 /*
  * The plan a forward over these sizes runs with hint `hint` (NULL = none):
  * out->segments = segments used, out->chain = 0/1, out->psub = prologue
- * sub-segments per segment (1 or 2).  The backward splits its state chains
+ * sub-segments per segment (1 or 2), out->scan = 1 if the segment scan is
+ * folded into the segments (0 if launched or not needed).  The backward splits its state chains
  * into the same segments.  Errors as gla_fwd_workspace_bytes' sizes, plus a
  * NULL out.
  */

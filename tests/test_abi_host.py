@@ -273,14 +273,16 @@ def test_strides_validated_on_the_host():
 def test_plan_controls_validate_and_resolve():
     lib = gla.load()
     r = lambda **kw: gla.plan_resolve(1, *kw.pop("shape", (8, 2048, 16, 96, 192, 128)), kw or None)
-    assert r() == {"segments": 2, "chain": 0, "psub": 2}                 # the training step's plan
-    assert r(shape=(1, 2048, 16, 96, 192, 128)) == {"segments": 16, "chain": 1, "psub": 1}   # the layer
-    assert r(shape=(1, 65536, 16, 96, 192, 128)) == {"segments": 16, "chain": 0, "psub": 1}  # the 64k prefill
+    assert r() == {"segments": 2, "chain": 0, "psub": 2, "scan": 1}       # the training step's plan
+    assert r(shape=(1, 2048, 16, 96, 192, 128)) == {"segments": 16, "chain": 1, "psub": 1, "scan": 0}   # layer
+    assert r(shape=(1, 65536, 16, 96, 192, 128)) == {"segments": 16, "chain": 0, "psub": 1, "scan": 0}  # 64k
     assert r(chain=0, shape=(1, 2048, 16, 96, 192, 128))["chain"] == 0
-    assert r(psub=1) == {"segments": 2, "chain": 0, "psub": 1}
+    assert r(psub=1) == {"segments": 2, "chain": 0, "psub": 1, "scan": 1}
+    assert r(scan=0)["scan"] == 0
+    assert r(segments=4, scan=1)["scan"] == 0          # six local states before the last segment: a scan
     assert r(segments=8)["segments"] == 8
     assert r(segments=5)["segments"] == 4          # 16 chunks in segments of 4
-    for bad in ({"segments": 17}, {"chain": 2}, {"psub": 2}, {"segments": -1}):
+    for bad in ({"segments": 17}, {"chain": 2}, {"psub": 2}, {"segments": -1}, {"scan": 2}):
         with pytest.raises(gla.GlaError):
             r(**bad)
         assert lib.gla_fwd_workspace_bytes_planned(1, 8, 2048, 16, 96, 192, 128,

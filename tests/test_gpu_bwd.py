@@ -154,7 +154,7 @@ def test_saved_states_training_width(chunk):
     gradients also agree with the recomputing backward's within the bf16 bar."""
     w = gi.workloads()[2]
     plan = gla.plan_resolve(gla.GLA_BF16, 8, 2048, 16, 96, 192, chunk)
-    assert plan == {"segments": 2, "chain": 0, "psub": 2}, plan   # the plan the bench times
+    assert plan == {"segments": 2, "chain": 0, "psub": 2, "scan": 1}, plan   # the plan the bench times
     x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 7 + chunk, 8, 2048, chunk, 0.0)
     g2 = gla.bwd_chunked(x["q"], x["k"], x["v"], x["lam"], x["do"], S0=x["S0"], dS_final=x["dS"], scale=x["scale"],
                          chunk=chunk)
@@ -225,3 +225,33 @@ def test_fwd_bwd_shape_sweep(case):
     for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
         assert_close(f64(got), ref, "bf16", name)
     assert_close(f64(dl), r[3], "bf16", "dlambda", batch_axis=None)
+
+
+@pytest.mark.parametrize("B,T,chunk,saved,plan", [(8, 2048, 128, True, {}), (8, 2048, 128, False, {}),
+                                                  (8, 1000, 64, True, {}), (8, 2048, 32, False, {}),
+                                                  (2, 1000, 64, False, {"segments": 3, "psub": 1})])
+def test_folded_chain_scans_are_bitwise_the_scans(B, T, chunk, saved, plan):
+    """The backward's state passes with the segment scans folded into the emit passes
+    (forward from S0, reverse from dS_T) equal the launched scans bit for bit."""
+    w = gi.workloads()[1]
+    x = gi.fwd_inputs(w, DEV, 2700 + T + chunk + B, B=B, T=T, with_do=True, with_dS=True, s0_var=0.01)
+    _say(f"folded vs launched backward scans B={B} T={T} C={chunk} saved={saved} plan={plan}")
+    args = (x["q"], x["k"], x["v"], x["lam"])
+    kw = dict(S0=x["S0"], dS_final=x["dS"], scale=x["scale"], chunk=chunk)
+    outs = []
+    for sc in (1, 0):
+        p = dict(plan, scan=sc)
+        if saved:
+            _, _, st = gla.fwd_chunked_states(*args, S0=x["S0"], scale=x["scale"], chunk=chunk, plan=p)
+            outs.append(gla.bwd_chunked_states(*args, x["do"], st, plan=p, **kw))
+        else:
+            outs.append(gla.bwd_chunked(*args, x["do"], plan=p, **kw))
+    torch.cuda.synchronize()
+    for a_, b_, name in zip(outs[0], outs[1], ("dq", "dk", "dv", "dlambda", "dS0")):
+        assert torch.equal(a_, b_), f"{name}: folded scans differ from launched scans"
+    if B <= 2:
+        r = oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), f64(x["do"]), S0=f64(x["S0"]),
+                       dS_T=f64(x["dS"]), scale=x["scale"])
+        for got, ref, name in zip(outs[0][:3] + outs[0][4:], (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
+            assert_close(f64(got), ref, "bf16", name)
+        assert_close(f64(outs[0][3]), r[3], "bf16", "dlambda", batch_axis=None)

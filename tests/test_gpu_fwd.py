@@ -259,3 +259,24 @@ def test_page_decay_schedule(chunk, chain):
     w = gi.Workload(w.name + "-page-decay", w.B, w.T, w.H, w.dk, w.dv, chunk, w.dtype,
                     tuple(gi.page_lambdas(w.H)), w.scale)
     _run_and_check(w, seed=95 + chunk, chunk=chunk, s0_var=0.01, plan={"chain": chain})
+
+
+@pytest.mark.parametrize("B,T,chunk,s0,plan", [(8, 2048, 128, None, {}), (8, 1000, 128, 0.01, {}),
+                                               (8, 2048, 64, 0.01, {}), (8, 2048, 32, None, {}),
+                                               (2, 1000, 64, 0.01, {"segments": 3, "psub": 1, "chain": 0})])
+def test_folded_segment_scan_is_bitwise_the_scan(B, T, chunk, s0, plan):
+    """With at most two local states before the last segment the segments fold them into
+    their start states themselves (no scan launch), in the scan kernel's order: outputs
+    and final states equal the launched scan's bit for bit, and meet the oracle."""
+    w = gi.workloads()[1]
+    x = gi.fwd_inputs(w, DEV, 2600 + T + chunk + B, B=B, T=T, s0_var=s0)
+    assert gla.plan_resolve(gla.GLA_BF16, B, T, 16, 96, 192, chunk, plan)["scan"] == 1
+    _say(f"folded vs launched segment scan B={B} T={T} C={chunk} plan={plan}")
+    outs = [gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], scale=x["scale"], chunk=chunk,
+                            plan=dict(plan, scan=sc)) for sc in (1, 0)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]),
+                        S0=None if x["S0"] is None else f64(x["S0"]), scale=x["scale"])
+    assert_close(f64(outs[0][0]), ro, "bf16", "o")
+    assert_close(f64(outs[0][1]), rS, "bf16", "S_final")
