@@ -150,20 +150,25 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
     // of row stride R and width D is read from ptr + r0 R with the range
     // (drl R + (hl + 1) D) elements, which ends after the batch's last unit (0
     // for a batch past the end), and this lane's piece at (dr R + hu D) + lane VEC.
+    // G UPB is a multiple of H, so every batch of this workgroup starts at the
+    // same head m: dr and hu are fixed per thread, and batch b = blockIdx.x + k G
+    // starts at row r0 = rfirst + k (G UPB / H) (no division per batch).
     struct Pos {
         long r0;
         int dr, hu, drl, hl, nu;
     };
-    auto where = [&](long b) {
+    const int m = (int)(((long)blockIdx.x * UPB) % a.H);
+    const long rfirst = (long)blockIdx.x * UPB / a.H, rstep = G * UPB / a.H;
+    const int dr_lane = (m + lu) / a.H, hu_lane = (m + lu) % a.H;
+    auto where = [&](long kb) {
         Pos p;
-        const long u0 = b * UPB;
-        p.nu = batch_units(b);
-        p.r0 = u0 / a.H;
-        const long u = u0 + lu, ul = u0 + (p.nu > 0 ? p.nu - 1 : 0);
-        p.dr = (int)(u / a.H - p.r0);
-        p.hu = (int)(u % a.H);
-        p.drl = (int)(ul / a.H - p.r0);
-        p.hl = (int)(ul % a.H);
+        p.nu = batch_units(blockIdx.x + kb * G);
+        p.r0 = rfirst + kb * rstep;
+        p.dr = dr_lane;
+        p.hu = hu_lane;
+        const int dl = m + (p.nu > 0 ? p.nu - 1 : 0);
+        p.drl = dl / a.H;
+        p.hl = dl - p.drl * a.H;
         return p;
     };
     auto range_of = [&](const Pos& p, int R, int D) { return p.nu > 0 ? (p.drl * R + (p.hl + 1) * D) * ES : 0; };
@@ -174,18 +179,18 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
         const int rg = range_of(p, R, D);
         return ld16(rsrc(static_cast<const E*>(base) + p.r0 * R, rg), off_of(p, R, D, nl, rg));
     };
-    // row loads of batch b: q, k, v, o, g pieces (zeros past the rows' ends)
-    auto load = [&](long b, uint4* r) {
-        const Pos p = where(b);
+    // row loads of this workgroup's batch kb: q, k, v, o, g pieces (zeros past the rows' ends)
+    auto load = [&](long kb, uint4* r) {
+        const Pos p = where(kb);
         r[0] = row_load(p, a.q, a.rq, DK, NKL);
         r[1] = row_load(p, a.k, a.rk, DK, NKL);
         r[2] = row_load(p, a.v, a.rv, DV, NVL);
         r[3] = row_load(p, a.o, a.ro, DV, NVL);
         r[4] = row_load(p, a.g, a.rg, DV, NVL);
     };
-    // one batch: issue the loads of batch b + G into `nxt`, then finish batch b from `cur`
-    auto step = [&](long b, const uint4* cur, uint4* nxt) {
-        load(b + G, nxt);
+    // one batch: issue the loads of batch kb + 1 into `nxt`, then finish batch kb from `cur`
+    auto step = [&](long kb, const uint4* cur, uint4* nxt) {
+        load(kb + 1, nxt);
         __builtin_amdgcn_sched_barrier(0);   // next batch's loads ahead of this batch's arithmetic
         float q[VEC], k[VEC], v[VEC], o[VEC], g[VEC];
         Piece<E>::unpack(cur[0], q);
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
         float y[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) y[e] = g[e] * fast_sigmoid(g[e]) * x[e] * inv * w[e];
-        const Pos p = where(b);                               // (past the end: range 0, store dropped)
+        const Pos p = where(kb);                              // (past the end: range 0, store dropped)
         const int ry = range_of(p, a.ry, DV);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Piece<E>::pack(y)),
                                                rsrc(static_cast<E*>(a.y) + p.r0 * a.ry, ry),
@@ -220,10 +225,10 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
     // two register sets in turn (no copies between them); the loop body is two
     // whole steps, the second of which may be a past-the-end batch
     uint4 ra0[5], ra1[5];
-    load(blockIdx.x, ra0);
-    for (long b = blockIdx.x; b < nb; b += 2 * G) {
-        step(b, ra0, ra1);
-        step(b + G, ra1, ra0);
+    load(0, ra0);
+    for (long kb = 0; blockIdx.x + kb * G < nb; kb += 2) {
+        step(kb, ra0, ra1);
+        step(kb + 1, ra1, ra0);
     }
 }
 
