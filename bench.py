@@ -453,7 +453,7 @@ def _repeat(fn, budget_s, max_reps):
             return reps, el
 
 
-def cpu_baseline_fwd(gi, w, seed, budget_s=6.0):
+def cpu_baseline_fwd(gi, w, seed, budget_s=4.0):
     """fp64 oracle on the Laplace layer's inputs (drawn on the CPU), repeated for ~budget_s."""
     import oracle
 
@@ -467,7 +467,7 @@ def cpu_baseline_fwd(gi, w, seed, budget_s=6.0):
                       f"repetitions in {el:.1f} s, OpenMP over the 16 (batch, head) units"}
 
 
-def cpu_baseline_train(gi, w, seed, budget_s=6.0):
+def cpu_baseline_train(gi, w, seed, budget_s=4.0):
     """fp64 oracle forward + reverse mode on one of the training step's 8 sequences."""
     import oracle
 
@@ -485,7 +485,7 @@ def cpu_baseline_train(gi, w, seed, budget_s=6.0):
                       f"(H=16, T=2048) x {reps} in {el:.1f} s; tokens/s of that sample"}
 
 
-def cpu_baseline_long(gi, w, seed, tokens=8192, budget_s=5.0):
+def cpu_baseline_long(gi, w, seed, tokens=8192, budget_s=3.0):
     """fp64 oracle forward over the first `tokens` tokens of the 64k-token prefill."""
     import oracle
 
@@ -498,7 +498,7 @@ def cpu_baseline_long(gi, w, seed, tokens=8192, budget_s=5.0):
                       f"in {el:.1f} s (the recurrence's cost is linear in T)"}
 
 
-def cpu_baseline_decode(gi, w, seed, budget_s=5.0):
+def cpu_baseline_decode(gi, w, seed, budget_s=3.0):
     import oracle
 
     n = 64

@@ -1025,13 +1025,15 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
 template <int C>
 hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, const FwdIO& io, const float* lambda,
                         const float* S0, float* S_final, void* ws, hipStream_t stream) {
-    // 4 waves, two 16x16 blocks each, over a 32 x 64 tile (the fastest of the
-    // shapes tried; a pass costs ~0.7 us, about half of it LDS time for the
-    // transposed operand reads).  Chunks in flight: as deep as the wave's
-    // memory counter can follow exactly (at most 63 outstanding operations; a
-    // chunk costs PK + PV loads and NJ snapshot stores); even, so the pass
-    // parity is known at compile time in the unrolled loop.
-    constexpr int NVB = 4, NJ = 2;
+    // 8 waves, one 16x16 block each, over a 32 x 64 tile: the fastest of the
+    // shapes measured on gfx950 (Laplace layer 29.8 us against 30.6 for 4 waves
+    // of two blocks, 31.6 for 4 waves over 32 x 32 tiles; a deeper ring of 10 or
+    // 12 chunks was slower).  A pass costs ~0.7 us at 128 tokens and its time
+    // follows the tokens.  Chunks in flight: at most what the wave's memory
+    // counter can follow exactly (at most 63 outstanding operations; a chunk
+    // costs PK + PV loads and NJ snapshot stores); even, so the pass parity is
+    // known at compile time in the unrolled loop.
+    constexpr int NVB = 4, NJ = 1;
     using L = ChainShape<C, NVB, NJ>;
     constexpr int D = C == 128 ? 6 : 12;
     static_assert(D * (L::PK + L::PV + NJ) <= 63, "memory counter");
