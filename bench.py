@@ -853,6 +853,27 @@ def main():
     del lleg
     torch.cuda.empty_cache()
 
+    # ---- the forward by chunk size (the pages' chunk-size trade-off, on MI355X): the
+    # Laplace layer and the training width's forward at C = 32, 64, 128, 256 (256-token
+    # chunks run in the tiled-chain form only; 32 in the segment form only)
+    result["fwd_chunks"] = {}
+    nk = max(K // 2, 10)
+    for name, wi in (("laplace_layer", 1), ("train_width", 2)):
+        wk = ws[wi]
+        row = {}
+        for C in (32, 64, 128, 256):
+            cl = FwdLeg(gla, gi, torch, wk, wi, C)
+            _, g = time_region(torch, cl.stream, cl, nk, W)
+            avg = g / nk
+            cb = FWD_BYTES_PER_TOKEN_HEAD[wk.dtype] * cl.token_heads
+            row[str(C)] = {"avg_call_us": avg * 1e6, "tokens_per_s": cl.tokens / avg,
+                           "hbm_frac": cb / avg / 1e9 / HBM_PEAK_GBS,
+                           "alg_flops_per_call": fwd_flops_per_token_head(C) * cl.token_heads,
+                           "plan": gla.plan_resolve(gla.GLA_BF16, wk.B, wk.T, 16, 96, 192, C)}
+            del cl
+            torch.cuda.empty_cache()
+        result["fwd_chunks"][name] = row
+
     # ---- training-step legs (mixer-train workload, chunk 128 and 64)
     w2 = ws[2]
     t_ms = 0.0

@@ -302,7 +302,7 @@ __global__ void copy_state_kernel(const float* __restrict__ S0, float* __restric
 bool fwd_supported(bool bf16_io, int dk, int dv, int chunk) {
     // fp32 tiles of 128 tokens would need ~250 KB of LDS, so fp32 stops at 64;
     // bf16 MFMA steps contract 32 values, so the dk = 16 shape is fp32 only.
-    return (dk == 96 && dv == 192 && (chunk == 64 || (bf16_io && (chunk == 128 || chunk == 32)))) ||
+    return (dk == 96 && dv == 192 && (chunk == 64 || (bf16_io && (chunk == 128 || chunk == 32 || chunk == 256)))) ||
            (dk == 16 && dv == 32 && chunk == 32 && !bf16_io);
 }
 
@@ -343,6 +343,9 @@ FwdPlan fwd_plan(bool bf16_io, int B, int T, int H, int dk, int dv, int chunk, i
     if (hint && hint->chain == 0) p.chain = 0;
     // (the tiled chain and its output kernel are built for 64- and 128-token chunks)
     if (hint && hint->chain == 1 && bf16_io && chunk >= 64 && p.nc > 1 && p.nc <= kChainMaxChunks) p.chain = 1;
+    // 256-token chunks run in the chain form only: their q, k, v tiles alone
+    // exceed a compute unit's LDS, so the segment kernels do not take them
+    if (bf16_io && chunk == 256 && p.nc > 0) p.chain = 1;
     if (p.chain) p.ws_bytes = (size_t)units * p.nc * dk * dv * 2;  // every chunk's start state, bf16
     // bf16 segments with at most kFuseMaxStates local states before the last segment
     // (e.g. two segments with the sub-segment prologue): no scan launch, each segment

@@ -1,5 +1,6 @@
 // gla_fwd_bf16.hip -- chunked-parallel GLA forward for bf16 q/k/v on gfx950
-// (dk = 96, dv = 192, chunks of 32, 64 or 128 tokens).
+// (dk = 96, dv = 192, chunks of 32, 64 or 128 tokens; 256-token chunks in the
+// tiled-chain form only, see fwd_out256_kernel).
 //
 // Method: Laplace 3B post, section "Challenge 1" (chunked GLA).  For chunk c
 // of C tokens with start state S (positions i, j in [0, C); b_i = lam^(i+1),
@@ -794,6 +795,238 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     }
 }
 
+// Output of one 256-token chunk from its start state (the tiled chain's bf16
+// snapshot), as two workgroups per (chunk, unit): the chunk's 256 x 256
+// decay-masked score matrix does not fit LDS (the q, k, v tiles alone would
+// take ~208 KB), so each workgroup takes 128 query rows.
+//   half 0 (rows 0..127): exactly the 128-token output kernel's work on the
+//            chunk's first 128 tokens (same b_i, D_ij and start state);
+//   half 1 (rows 128..255): b (.) Q1 S plus the intra-chunk term over all 256
+//            keys: the cross block (Q1 K0^T) (.) D, a full 8 x 8 grid of 16x16
+//            score blocks with D_ij = lam^(i-j) for i - j in [1, 255], and
+//            the lower triangle (Q1 K1^T) (.) D as in the 128-token kernel.
+//            The 100 score blocks go to LDS in bf16; then V0 and V1 pass in
+//            turn through the space the keys took, each wave keeping its value
+//            fragments of both halves in registers for the output strips.
+// Grid (2 nc, units): blockIdx.x = half * nc + chunk.
+template <int LDK, int NCB>
+__global__ __launch_bounds__((F8<128, LDK, NCB>::NT), 1) void fwd_out256_kernel(FwdArgs a) {
+    constexpr int C = 256, R = 128;
+    using L = F8<R, LDK, NCB>;
+    constexpr int NT = L::NT, NP = L::NP, LDV = L::LDV, NCG = L::NCG;
+    constexpr int NCROSS = 64, NDIAG = L::NTRI, NBLK = NCROSS + NDIAG;  // half 1's score blocks
+    // half 0: Q | K | V | 36 score blocks;  half 1: Q1 | K0 K1 (then V0, then V1) | 100 score blocks
+    constexpr int SM = R * LDK + 2 * R * LDK + NBLK * 256;
+    static_assert(2 * R * LDK + R * LDV + NDIAG * 256 <= SM && R * LDV <= 2 * R * LDK, "LDS carve-up");
+    __shared__ __align__(16) bf16 sm[SM];
+    __shared__ float pws[C + 2];  // pws[0] = 0, pws[x + 1] = scale * lam^x (x = 0..C)
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, n = lane % 16, g = lane / 16;
+    const int h = wave / NCG, colbase = 16 * NCB * (wave % NCG);
+    const int partner = h == 0 ? wave + NCG : wave - NCG;
+    const int half = blockIdx.x / a.nc, c = blockIdx.x % a.nc, bh = blockIdx.y;
+    const int H = a.H, T = a.T;
+    const int hd = bh % H, b = bh / H;
+    const int t0 = c * C + half * R;            // first token of this workgroup's rows
+    const int ceff = min(R, T - t0);            // its rows (<= 0: none)
+    if (ceff <= 0) return;                      // (whole workgroup)
+    const int tokQ = a.sq.t, tokK = a.sk.t, tokV = a.sv.t, tokO = a.so.t;
+    const bf16* qb = static_cast<const bf16*>(a.q) + b * a.sq.b + (size_t)t0 * tokQ + hd * kDK;
+    const bf16* kb = static_cast<const bf16*>(a.k) + b * a.sk.b + (size_t)(c * C) * tokK + hd * kDK;  // chunk row 0
+    const bf16* vb = static_cast<const bf16*>(a.v) + b * a.sv.b + (size_t)(c * C) * tokV + hd * kDV;
+    bf16* ob = static_cast<bf16*>(a.o) + b * a.so.b + hd * kDV;
+
+    using StageK = RowStage<R, kDK, NT>;
+    using StageV = RowStage<R, kDV, NT>;
+    static_assert(NT % (kDK / 8) == 0 && NT % (kDV / 8) == 0, "row staging");
+    // start state: this wave's half and the partner's, 4 bf16 per block and lane
+    const uint2* sn = reinterpret_cast<const uint2*>(static_cast<const bf16*>(a.Ub) + ((size_t)bh * a.nc + c) * kDK * kDV);
+    uint2 so[3][NCB], sp[3][NCB];
+    auto sop = [&](int p, int cb) -> bf16x8 {
+        const bf16x4 own = __builtin_bit_cast(bf16x4, so[p][cb]);
+        const bf16x4 oth = __builtin_bit_cast(bf16x4, sp[p][cb]);
+        return h == 0 ? __builtin_shufflevector(own, oth, 0, 1, 2, 3, 4, 5, 6, 7)
+                      : __builtin_shufflevector(oth, own, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    const float lam = a.lambda[hd];
+
+    if (half == 0) {
+        // --------------------------------- rows 0..127: the 128-token kernel's work
+        bf16* Qs = sm;
+        bf16* Ks = sm + R * LDK;
+        bf16* Vs = sm + 2 * R * LDK;
+        bf16* As = Vs + R * LDV;
+        constexpr int NS = L::NSLOT;
+        int blk[NS];
+        score_blocks_uniform<R, L::NW>(wave, blk, std::make_integer_sequence<int, NS>{});
+        const int sa = blk[0] >= 0 ? blk[0] >> 4 : 0;
+        int sb = sa;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            if (blk[k] >= 0) sb = blk[k] >> 4;
+        constexpr int NA = score_lead<R, L::NW>();
+        bool use_b[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) use_b[k] = k >= NA && blk[k] >= 0 && (blk[k] >> 4) != sa;
+        StageK tq, tk;
+        StageV tv;
+        tq.load(qb, tokQ, ceff, tid);
+        tk.load(kb, tokK, ceff, tid);
+        tv.load(vb, tokV, ceff, tid);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                so[i][cb] = sn[((wave * 3 + i) * NCB + cb) * 64 + lane];
+                sp[i][cb] = sn[((partner * 3 + i) * NCB + cb) * 64 + lane];
+            }
+        if (tid < R + 2) pws[tid] = tid == 0 ? 0.f : a.scale * pow_int(lam, tid - 1);
+        tq.template store<LDK>(Qs, tid);
+        tk.template store<LDK>(Ks, tid);
+        __syncthreads();  // q, k, decay table
+        score_blocks_to_lds<R, LDK, L::NW, NS>(Qs, Ks, As, pws, blk, sa, sb, use_b, n, g);
+        tv.template store<LDV>(Vs, tid);
+        __syncthreads();  // score blocks, values
+        bf16x8 vf[NCB][NP];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) vf[cb][p] = op_col8(Vs, LDV, 32 * p, colbase + 16 * cb, n, g);
+        if (h == 0) {
+            out_pair<R, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+            out_pair<R, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+        } else {
+            out_pair<R, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+            out_pair<R, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+        }
+        return;
+    }
+
+    // ------------------------------------------------------- rows 128..255
+    bf16* Qs = sm;                  // Q1
+    bf16* Kc = sm + R * LDK;        // K0 (rows 0..127), K1 (rows 128..255); then V0, then V1
+    bf16* As = sm + 3 * R * LDK;    // cross blocks 0..63 (8 ib + jb), then the triangle of K1
+    StageK tq, tk0, tk1;
+    StageV tv;
+    tq.load(qb, tokQ, ceff, tid);
+    tk0.load(kb, tokK, R, tid);
+    tk1.load(kb + (size_t)R * tokK, tokK, ceff, tid);
+    tv.load(vb, tokV, R, tid);  // V0
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            so[i][cb] = sn[((wave * 3 + i) * NCB + cb) * 64 + lane];
+            sp[i][cb] = sn[((partner * 3 + i) * NCB + cb) * 64 + lane];
+        }
+    for (int i = tid; i < C + 2; i += NT) pws[i] = i == 0 ? 0.f : a.scale * pow_int(lam, i - 1);
+    tq.template store<LDK>(Qs, tid);
+    tk0.template store<LDK>(Kc, tid);
+    tk1.template store<LDK>(Kc + R * LDK, tid);
+    __syncthreads();  // q, k, decay table
+    // Score blocks: block e < 64 is cross block (ib, jb) = (e / 8, e % 8) of Q1
+    // against K0, i - j = 128 + 16 (ib - jb) + ...; block 64 + t is the
+    // triangle's block t = ib (ib + 1) / 2 + jb of Q1 against K1.  Wave w takes
+    // blocks w, w + NW, ...; AT[4g + r][n] = q_(16 ib + n) . k_(16 jb + 4g + r).
+    for (int e = wave; e < NBLK; e += L::NW) {
+        int ib, jb, krow, off;
+        if (e < NCROSS) {
+            ib = e / 8;
+            jb = e % 8;
+            krow = 16 * jb;
+            off = R;
+        } else {
+            const int t = e - NCROSS;
+            ib = 0;
+            while ((ib + 1) * (ib + 2) / 2 <= t) ++ib;
+            jb = t - ib * (ib + 1) / 2;
+            krow = R + 16 * jb;
+            off = 0;
+        }
+        f32x4 at = zero4();
+#pragma unroll
+        for (int p = 0; p < kDK / 32; ++p)
+            at = mfma(op_row8(Kc, LDK, krow + n, 32 * p + 8 * g), op_row8(Qs, LDK, 16 * ib + n, 32 * p + 8 * g), at);
+        const int d1 = off + 16 * (ib - jb) + n - 4 * g + 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) at[r] *= pws[max(d1 - r, 0)];
+        *reinterpret_cast<bf16x4*>(As + e * 256 + as_off(n, g >> 1) + 4 * (g & 1)) =
+            bf16x4{to_bf16(at[0]), to_bf16(at[1]), to_bf16(at[2]), to_bf16(at[3])};
+    }
+    StageV tv1;
+    tv1.load(vb + (size_t)R * tokV, tokV, ceff, tid);
+    __syncthreads();  // score blocks done, keys no longer read
+    tv.template store<LDV>(Kc, tid);
+    __syncthreads();
+    bf16x8 vf0[NCB][NP], vf1[NCB][NP];  // vf[cb][p] = V[32p + 8g + e][colbase + 16cb + n]
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) vf0[cb][p] = op_col8(Kc, LDV, 32 * p, colbase + 16 * cb, n, g);
+    __syncthreads();  // V0 fragments read
+    tv1.template store<LDV>(Kc, tid);
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) vf1[cb][p] = op_col8(Kc, LDV, 32 * p, colbase + 16 * cb, n, g);
+
+    // Output strips (the 128-token kernel's split: h = 0 takes strips 0 and 3,
+    // h = 1 strips 1 and 2), O^T = b (.) S^T Q1^T + V0^T A10^T + V1^T A11^T.
+    auto strip = [&](int K) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ib = 2 * K + u;
+            f32x4 OT[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) OT[cb] = zero4();
+#pragma unroll
+            for (int p = 0; p < kDK / 32; ++p) {
+                const bf16x8 q0 = op_row_pair(Qs, LDK, 16 * ib + n, 32 * p + 4 * g);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(sop(p, cb), q0, OT[cb]);
+            }
+            const float bi = pws[R + 16 * ib + n + 2];  // scale * lam^(i+1), i = 128 + 16 ib + n
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) OT[cb][r] *= bi;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int jb = 2 * p + (g >> 1);
+                const bf16x8 aop = *reinterpret_cast<const bf16x8*>(As + (8 * ib + jb) * 256 + as_off(n, g & 1));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf0[cb][p], aop, OT[cb]);
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (2 * p > ib) break;  // pair entirely above the diagonal (uniform)
+                const int jb = 2 * p + (g >> 1);
+                bf16x8 aop = bf16x8{};
+                if (jb <= ib)
+                    aop = *reinterpret_cast<const bf16x8*>(As + (NCROSS + ib * (ib + 1) / 2 + jb) * 256 + as_off(n, g & 1));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) OT[cb] = mfma(vf1[cb][p], aop, OT[cb]);
+            }
+            const int irow = 16 * ib + n;
+            if (irow < ceff) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    store4<bf16>(ob + (size_t)(t0 + irow) * tokO + colbase + cb * 16 + 4 * g, OT[cb]);
+            }
+        }
+    };
+    if (h == 0) {
+        strip(0);
+        strip(3);
+    } else {
+        strip(1);
+        strip(2);
+    }
+}
+
 // ---------------------------------------------------------------- tiled chain
 //
 // Chunk start states for the per-chunk output kernel, by running the state
@@ -829,19 +1062,20 @@ struct ChainShape {
     static constexpr int TK = 32, TV = 16 * NVB;
     static constexpr int NTK = kDK / TK, NTV = kDV / TV, NTILE = NTK * NTV;
     static constexpr int LKT = TK + 16, LVT = TV + 16;      // LDS row strides (elements)
-    static constexpr int NPK = C * (TK / 8), NPV = C * (TV / 8);   // 16-byte pieces per chunk tile
+    static constexpr int R = C < 128 ? C : 128, NS = C / R;  // tokens per pass, passes per chunk
+    static constexpr int NPK = R * (TK / 8), NPV = R * (TV / 8);   // 16-byte pieces per pass tile
     static constexpr int PK = (NPK + NT - 1) / NT, PV = (NPV + NT - 1) / NT;
     static_assert(kDV % TV == 0 && (NJ == 1 || NJ == 2), "tile shape");
 };
 
 template <int C, int NVB, int NJ, int D>
 __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel(ChainArgs a) {
-    static_assert(D % 2 == 0, "pass parity");
     using L = ChainShape<C, NVB, NJ>;
     constexpr int NT = L::NT, TK = L::TK, TV = L::TV, LKT = L::LKT, LVT = L::LVT, PK = L::PK, PV = L::PV;
-    constexpr int NPK = L::NPK, NPV = L::NPV;
-    __shared__ __align__(16) bf16 Kt[3][C * LKT];   // chunk tiles, three buffers
-    __shared__ __align__(16) bf16 Vt[3][C * LVT];
+    constexpr int NPK = L::NPK, NPV = L::NPV, R = L::R, NS = L::NS;
+    static_assert(D % (2 * NS) == 0, "pass and chunk parities");
+    __shared__ __align__(16) bf16 Kt[3][R * LKT];   // pass tiles, three buffers
+    __shared__ __align__(16) bf16 Vt[3][R * LVT];
 
     // Workgroups of one unit share an XCD (dispatch goes round-robin over 8):
     // linear id = 8 * NTILE * (unit / 8) + 8 * tile + unit % 8.
@@ -857,6 +1091,7 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
     const int lane = tid % 64, n = lane % 16, g = lane / 16;
     const int vb = wave % NVB, jlo = NJ == 2 ? 0 : wave / NVB;  // this wave's blocks: rows 16 (jlo + j), columns 16 vb
     const int H = a.H, T = a.T, nc = a.nc;
+    const int nx = (T + R - 1) / R;   // passes
     const int hd = bh % H, b = bh / H;
     const int tokK = a.sk.t, tokV = a.sv.t;
     const bf16* kb = a.k + b * a.sk.b + hd * kDK + dk0;
@@ -879,7 +1114,7 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
     // requested after it.
     uint4 rk[D][PK], rv[D][PV];
     auto load = [&](uint4 (&xk)[PK], uint4 (&xv)[PV], int t) {
-        const int valid = t < T ? min(C, T - t) : 0;
+        const int valid = t < T ? min(R, T - t) : 0;
         const auto rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kb + (size_t)t * tokK), 0,
                                                            __builtin_amdgcn_readfirstlane(valid * tokK * 2), kBufWord3);
         const auto rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(vb_ + (size_t)t * tokV), 0,
@@ -898,18 +1133,23 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
         }
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(rk[d], rv[d], d * C);
+    for (int d = 0; d < D; ++d) load(rk[d], rv[d], d * R);
 
-    // Decay factors: c_j of the key rows this thread stages (a full chunk, a
-    // partial last chunk) and the chunk decays lam^C, lam^(partial length).
+    // Decay factors: c_j of the key rows this thread stages, for each pass of a
+    // chunk (chunk row R s + row), in a full chunk and in a partial last chunk,
+    // and the chunk decays lam^C, lam^(partial length).
     const float lam = a.lambda[hd];
     const int ctail = T % C;
-    float ck[PK][2];
+    float ck[PK][2][NS];
 #pragma unroll
     for (int i = 0; i < PK; ++i) {
         const int row = (tid + NT * i) / (TK / 8);
-        ck[i][0] = pow_int(lam, C - 1 - row);
-        ck[i][1] = row < ctail ? pow_int(lam, ctail - 1 - row) : 0.f;
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+            const int jj = R * sp + row;
+            ck[i][0][sp] = pow_int(lam, C - 1 - jj);
+            ck[i][1][sp] = jj < ctail ? pow_int(lam, ctail - 1 - jj) : 0.f;
+        }
     }
     const float lamC = uniform_f32(pow_int(lam, C)), lamT = uniform_f32(pow_int(lam, ctail));
 
@@ -927,17 +1167,23 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
     }
     bf16x4* snap = reinterpret_cast<bf16x4*>(a.snap + (size_t)bh * nc * kDK * kDV);
 
-    // Chunk x sits in ring slot x % D; staging writes it to LDS buffer x % 3
-    // (keys scaled by c_j), then the slot is refilled with chunk x + D.
+    // Pass x (chunk x / NS, its rows R (x % NS) ..) sits in ring slot x % D;
+    // staging writes it to LDS buffer x % 3 (keys scaled by c_j), then the slot
+    // is refilled with pass x + D.
     auto stage = [&](uint4 (&xk)[PK], uint4 (&xv)[PV], int x) {
-        const bool full = T - x * C >= C;
+        const bool full = T - (x / NS) * C >= C;
+        const int sp = x % NS;
         bf16* kt = Kt[x % 3];
         bf16* vt = Vt[x % 3];
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int p = tid + NT * i, row = p / (TK / 8), kc = p % (TK / 8);
+            float cf = full ? ck[i][0][0] : ck[i][1][0];
+#pragma unroll
+            for (int q = 1; q < NS; ++q)
+                if (sp == q) cf = full ? ck[i][0][q] : ck[i][1][q];
             if (NPK % NT == 0 || p < NPK)
-                *reinterpret_cast<uint4*>(kt + row * LKT + 8 * kc) = scale_bf16x8(xk[i], full ? ck[i][0] : ck[i][1]);
+                *reinterpret_cast<uint4*>(kt + row * LKT + 8 * kc) = scale_bf16x8(xk[i], cf);
         }
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
@@ -945,62 +1191,69 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
             if (NPV % NT == 0 || p < NPV) *reinterpret_cast<uint4*>(vt + row * LVT + 8 * kc) = xv[i];
         }
     };
-    // Operands of chunk x (LDS buffer x % 3): this wave's value and key columns.
-    bf16x8 vop[2][C / 32], kop[2][C / 32][NJ];  // [chunk parity]
+    // Operands of pass x (LDS buffer x % 3): this wave's value and key columns.
+    bf16x8 vop[2][R / 32], kop[2][R / 32][NJ];  // [pass parity]
     auto operands = [&](int par, int x) {
         const bf16* kt = Kt[x % 3];
         const bf16* vt = Vt[x % 3];
 #pragma unroll
-        for (int p = 0; p < C / 32; ++p) {
+        for (int p = 0; p < R / 32; ++p) {
             vop[par][p] = op_col8(vt, LVT, 32 * p, 16 * vb, n, g);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) kop[par][p][j] = op_col8(kt, LKT, 32 * p, 16 * (jlo + j), n, g);
         }
     };
     stage(rk[0], rv[0], 0);
-    load(rk[0], rv[0], D * C);
+    load(rk[0], rv[0], D * R);
     stage(rk[1], rv[1], 1);
-    load(rk[1], rv[1], (D + 1) * C);
+    load(rk[1], rv[1], (D + 1) * R);
     __syncthreads();
     operands(0, 0);
 
-    // Pass c: chunk c's operands are in registers (read a pass earlier), chunk
-    // c + 1 is complete in LDS, chunk c + 2 is staged into the third buffer
-    // (last read two passes ago).  Chunk c's own contribution
-    // Lc = (diag(c) K)^T V is multiplied in pass c; the chain itself,
-    // S <- lam^C S + L(c-1), one fma per element, runs a pass later, so the
-    // chunk's MFMAs never wait for the chain, and LDS reads, LDS writes and
-    // MFMAs of neighbouring chunks overlap.  One barrier per pass.
-    f32x4 Lc[2][NJ];  // [pass parity][block]
-    for (int c0 = 0; c0 < nc; c0 += D) {
+    // Pass x: its operands are in registers (read a pass earlier), pass x + 1
+    // is complete in LDS, pass x + 2 is staged into the third buffer (last read
+    // two passes ago).  Chunk c's own contribution Lc = (diag(c) K)^T V is
+    // multiplied in its NS passes; the chain itself, S <- lam^C S + L(c-1), one
+    // fma per element, runs in chunk c's first pass, so the chunk's MFMAs never
+    // wait for the chain, and LDS reads, LDS writes and MFMAs of neighbouring
+    // passes overlap.  One barrier per pass.  (With NS = 1 a pass is a chunk.)
+    f32x4 Lc[2][NJ];  // [chunk parity][block]
+    for (int x0 = 0; x0 < nx; x0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int c = c0 + d;
-            if (c >= nc) break;
-            const int cur = d & 1, prv = cur ^ 1;  // D is even: parity of c
+            const int x = x0 + d;
+            if (x >= nx) break;
+            const int po = d & 1, pn = po ^ 1;                   // pass parity (compile time)
+            const int sp = d % NS;                               // pass within the chunk
+            const int cur = (d / NS) & 1, prv = cur ^ 1;         // chunk parity (x0 is a multiple of 2 NS)
+            const int c = x / NS;
+            if (sp == 0) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) Lc[cur][j] = zero4();
-#pragma unroll
-            for (int p = 0; p < C / 32; ++p)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) Lc[cur][j] = mfma(kop[cur][p][j], vop[cur][p], Lc[cur][j]);
-            // chain step of the previous chunk: S = start state of chunk c
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if (c >= 1) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[j][r] = fmaf(lamC, S[j][r], Lc[prv][j][r]);  // a full chunk
-                }
-                snap[(size_t)c * (kDK * kDV / 4) + spos[j]] =
-                    bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
+                for (int j = 0; j < NJ; ++j) Lc[cur][j] = zero4();
             }
-            operands(prv, c + 1);
-            // chunk c + 2 staged, its slot refilled; issued on every pass (past
+#pragma unroll
+            for (int p = 0; p < R / 32; ++p)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) Lc[cur][j] = mfma(kop[po][p][j], vop[po][p], Lc[cur][j]);
+            if (sp == 0) {
+                // chain step of the previous chunk: S = start state of chunk c
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    if (c >= 1) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) S[j][r] = fmaf(lamC, S[j][r], Lc[prv][j][r]);  // a full chunk
+                    }
+                    snap[(size_t)c * (kDK * kDV / 4) + spos[j]] =
+                        bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
+                }
+            }
+            operands(pn, x + 1);
+            // pass x + 2 staged, its slot refilled; issued on every pass (past
             // the end: zeros, no reads), so the waits for the ring stay exact
             const int d2 = (d + 2) % D;  // compile-time once unrolled
-            stage(rk[d2], rv[d2], c + 2);
-            load(rk[d2], rv[d2], (c + 2 + D) * C);
-            __syncthreads();  // chunk c + 2 staged; chunk c + 1's operands read
+            stage(rk[d2], rv[d2], x + 2);
+            load(rk[d2], rv[d2], (x + 2 + D) * R);
+            __syncthreads();  // pass x + 2 staged; pass x + 1's operands read
         }
     }
     {
@@ -1035,7 +1288,7 @@ hipError_t launch_chain(const FwdPlan& plan, int B, int T, int H, int ncbo, cons
     // known at compile time in the unrolled loop.
     constexpr int NVB = 4, NJ = 1;
     using L = ChainShape<C, NVB, NJ>;
-    constexpr int D = C == 128 ? 6 : 12;
+    constexpr int D = C == 256 ? 8 : C == 128 ? 6 : 12;  // (256: 128-token passes, two per chunk)
     static_assert(D * (L::PK + L::PV + NJ) <= 63, "memory counter");
     ChainArgs c{};
     c.T = T;
@@ -1127,6 +1380,33 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
     return hipGetLastError();
 }
 
+// 256-token chunks: the tiled chain (two 128-token passes per chunk), then two
+// output workgroups per (chunk, unit).
+hipError_t launch_c256(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, const float* lambda,
+                       const float* S0, float scale, float* S_final, void* ws, hipStream_t stream) {
+    constexpr int LDK = 104, NCB = 2;
+    hipError_t err = launch_chain<256>(plan, B, T, H, NCB, io, lambda, S0, S_final, ws, stream);
+    if (err != hipSuccess) return err;
+    FwdArgs a{};
+    a.T = T;
+    a.H = H;
+    a.q = io.q;
+    a.k = io.k;
+    a.v = io.v;
+    a.sq = io.sq;
+    a.sk = io.sk;
+    a.sv = io.sv;
+    a.so = io.so;
+    a.lambda = lambda;
+    a.scale = scale;
+    a.o = io.o;
+    a.Ub = ws;
+    a.nc = plan.nc;
+    hipLaunchKernelGGL((fwd_out256_kernel<LDK, NCB>), dim3(2 * plan.nc, (unsigned)B * H), dim3(F8<128, LDK, NCB>::NT),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, const FwdIO& io, const float* lambda,
@@ -1138,6 +1418,8 @@ hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, 
         return launch_c<64, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
     if (chunk == 32 && !plan.chain)
         return launch_c<32, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
+    if (chunk == 256 && plan.chain && !sbar)
+        return launch_c256(plan, B, T, H, io, lambda, S0, scale, S_final, ws, stream);
     return hipErrorInvalidValue;
 }
 

@@ -26,7 +26,8 @@ extern "C" {
  *             every segment from its start state)
  *   chain     bf16 forward: 0 = the segment split above; 1 = the tiled state
  *             chain (every chunk's start state, then one output workgroup per
- *             chunk), used where it can run (2 .. 64 chunks)
+ *             chunk), used where it can run (2 .. 64 chunks); 256-token chunks
+ *             always run in the chain form (two output workgroups per chunk)
  *   psub      1 = one prologue workgroup per segment (the library may run the
  *             bf16 prologue over half-length sub-segments instead)
  *   scan      -1 = the library's choice; 0 = a scan launch turns the segments'

@@ -55,8 +55,9 @@ def test_fwd_rejects_bad_arguments_before_touching_the_device():
     assert fwd(T=-1) == E.GLA_ERR_INVALID_ARG
     assert fwd(H=0) == E.GLA_ERR_INVALID_ARG
     assert fwd(dk=64) == E.GLA_ERR_UNSUPPORTED
-    assert fwd(C=256) == E.GLA_ERR_UNSUPPORTED                  # 256-row tiles exceed the LDS
+    assert fwd(C=512) == E.GLA_ERR_UNSUPPORTED
     assert fwd(C=96) == E.GLA_ERR_UNSUPPORTED
+    assert fwd(dtype=0, C=256) == E.GLA_ERR_UNSUPPORTED          # 256-token chunks: bf16 forward only
     assert fwd(dtype=0, C=128) == E.GLA_ERR_UNSUPPORTED          # fp32 stops at chunk 64
     assert fwd(dtype=1, dk=16, dv=32, C=32) == E.GLA_ERR_UNSUPPORTED
     assert fwd(q=None) == E.GLA_ERR_INVALID_ARG
@@ -201,6 +202,7 @@ def test_saved_state_entry_points_validate():
                                           ws, wsb, None)
 
     assert f(dtype=0) == gla.GLA_ERR_UNSUPPORTED           # fp32 96/192: no backward, so no saved states
+    assert f(C=256) == gla.GLA_ERR_UNSUPPORTED             # no backward at 256-token chunks either
     assert f(states=None) == gla.GLA_ERR_INVALID_ARG
     assert f(states=MIS) == gla.GLA_ERR_INVALID_ARG
     assert f(ws=None) == gla.GLA_ERR_WORKSPACE
@@ -232,6 +234,7 @@ def test_bwd_rejects_bad_arguments_before_touching_the_device():
     assert bwd(dk=64) == E.GLA_ERR_UNSUPPORTED
     assert bwd(dtype=0) == E.GLA_ERR_UNSUPPORTED                  # fp32 backward: tiny shape only
     assert bwd(dtype=0, dk=16, dv=32, C=64) == E.GLA_ERR_UNSUPPORTED
+    assert bwd(C=256) == E.GLA_ERR_UNSUPPORTED                    # 256-token chunks: forward only
     assert bwd(do=None) == E.GLA_ERR_INVALID_ARG
     assert bwd(dv_=MIS) == E.GLA_ERR_INVALID_ARG
     assert bwd(dl=MIS) == E.GLA_ERR_INVALID_ARG
@@ -282,6 +285,10 @@ def test_plan_controls_validate_and_resolve():
     assert r(segments=4, scan=1)["scan"] == 0          # six local states before the last segment: a scan
     assert r(segments=8)["segments"] == 8
     assert r(segments=5)["segments"] == 4          # 16 chunks in segments of 4
+    # 256-token chunks run in the chain form whatever the hint (their tiles exceed LDS)
+    assert r(shape=(8, 2048, 16, 96, 192, 256))["chain"] == 1
+    assert r(chain=0, shape=(1, 300, 16, 96, 192, 256))["chain"] == 1
+    assert lib.gla_fwd_workspace_bytes(1, 2, 1000, 16, 96, 192, 256) == 2 * 16 * 4 * 96 * 192 * 2
     for bad in ({"segments": 17}, {"chain": 2}, {"psub": 2}, {"segments": -1}, {"scan": 2}):
         with pytest.raises(gla.GlaError):
             r(**bad)
@@ -304,7 +311,7 @@ def test_noalloc_forward_limits_checked_on_the_host():
         return lib.gla_fwd_chunked_noalloc(dtype, B, T, H, 96, 192, C, q, P, P, P, None, 1.0, o, None, None, None)
 
     assert n(dtype=9) == gla.GLA_ERR_INVALID_ARG
-    assert n(C=256) == gla.GLA_ERR_UNSUPPORTED
+    assert n(C=512) == gla.GLA_ERR_UNSUPPORTED
     assert n(q=None) == gla.GLA_ERR_INVALID_ARG
     assert n(o=MIS) == gla.GLA_ERR_INVALID_ARG
     # B=6, H=20, T=2048: four segments, 39.8 MB of workspace > 32 MiB

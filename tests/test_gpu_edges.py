@@ -54,6 +54,8 @@ FWD_CASES = {
     "layer_segments": (1, 1, 2048, 128, None, 0.01, "segments"),
     "ragged_c64": (1, 2, 1000, 64, None, 0.01, None),
     "ragged_c32": (1, 2, 1000, 32, None, 0.01, None),
+    "layer_c256": (1, 1, 2048, 256, None, 0.01, None),
+    "ragged_c256": (1, 2, 1000, 256, None, 0.01, None),
     "train_width": (2, 8, 2048, 128, None, 0.0, None),
     "fp32_tiny": (0, 2, 250, 32, None, 0.5, None),
     "fp32_wide_c64": (1, 2, 300, 64, "f32", 0.01, None),

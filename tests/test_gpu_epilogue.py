@@ -237,7 +237,8 @@ def test_decode_epilogue_full_width_sampled():
 
 
 @pytest.mark.parametrize("B,T,chunk,chain", [(1, 2048, 128, 1), (1, 2048, 128, 0), (1, 300, 128, 1),
-                                             (1, 300, 128, 0), (2, 700, 128, None), (1, 2048, 64, None)])
+                                             (1, 300, 128, 0), (2, 700, 128, None), (1, 2048, 64, None),
+                                             (2, 700, 256, None)])
 @pytest.mark.parametrize("aug", [True, False])
 def test_forward_epilogue_matches_oracle(B, T, chunk, chain, aug):
     """gla_fwd_chunked_epilogue: fused into the output kernel on tiled-chain plans

@@ -57,10 +57,21 @@ def test_laplace_layer_config():
     _run_and_check(gi.workloads()[1], seed=1)
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 32])
+@pytest.mark.parametrize("chunk", [128, 64, 32, 256])
 @pytest.mark.parametrize("T", [1, 100, 300, 1000])
 def test_bf16_ragged_with_state(chunk, T):
     _run_and_check(gi.workloads()[1], seed=100 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
+
+
+@pytest.mark.parametrize("B,T,s0", [(1, 2048, None), (1, 2048, 0.01), (3, 513, 0.01), (2, 200, None),
+                                    (1, 128, 0.01), (1, 129, None), (2, 256, 0.01), (1, 257, None),
+                                    (1, 384, 0.01), (1, 4096, None)])
+def test_chunk256(B, T, s0):
+    """256-token chunks (the tiled chain in two 128-token passes per chunk, then one
+    output workgroup per 128 query rows, the second with the cross-half score blocks):
+    the Laplace layer, and lengths that end inside the first or the second half of a
+    chunk or on its boundaries."""
+    _run_and_check(gi.workloads()[1], seed=900 + T + B, B=B, T=T, chunk=256, s0_var=s0)
 
 
 def test_fp32_laplace_shape_chunk64():

@@ -50,6 +50,7 @@ FWD_CASES = {
     "layer_segments": (1, 1, 2048, 128, 0.01, {"chain": 0}),
     "ragged_c64": (1, 2, 1000, 64, 0.01, None),
     "ragged_c32": (1, 2, 1000, 32, 0.01, None),
+    "ragged_c256": (1, 2, 1000, 256, 0.01, None),
     "train_width": (2, 8, 2048, 128, None, None),
     "fp32_wide_c64": (1, 2, 300, 64, 0.01, None),
     "fp32_tiny": (0, 3, 250, 32, 0.5, None),

@@ -34,8 +34,9 @@ def _noalloc(x, chunk, o, S):
 
 
 # largest first: the training width (two segments, 28.3 MB of scratch), the Laplace layer
-# (tiled chain, 9.4 MB), a ragged two-sequence case at chunk 64 (three segments)
-CALLS = [(2, 8, 2048, 128, 0.0), (1, 1, 2048, 128, 0.01), (1, 2, 700, 64, 0.01)]
+# (tiled chain, 9.4 MB), a ragged two-sequence case at chunk 64 (three segments), and
+# 256-token chunks (tiled chain, 2.4 MB)
+CALLS = [(2, 8, 2048, 128, 0.0), (1, 1, 2048, 128, 0.01), (1, 2, 700, 64, 0.01), (1, 2, 500, 256, 0.01)]
 
 
 def test_noalloc_forward_matches_the_workspace_forward():
