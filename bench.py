@@ -874,11 +874,11 @@ def main():
             torch.cuda.empty_cache()
         result["fwd_chunks"][name] = row
 
-    # ---- training-step legs (mixer-train workload, chunk 128 and 64)
+    # ---- training-step legs (mixer-train workload, chunks 128, 64, 32 and 256)
     w2 = ws[2]
     t_ms = 0.0
     result["train"] = {}
-    for C in (() if args.no_train else (128, 64, 32)):
+    for C in (() if args.no_train else (128, 64, 32, 256)):
         tleg = TrainLeg(gla, gi, torch, w2, 2, C)
         t_wall, t_gpu = time_region(torch, tleg.stream, tleg, K, W)
         t_avg = t_gpu / K

@@ -608,7 +608,7 @@ __global__ void bwd_empty_kernel(const float* __restrict__ dST, float* __restric
 // ---------------------------------------------------------------- host side
 
 bool bwd_supported(bool bf16_io, int dk, int dv, int chunk) {
-    return bf16_io ? (dk == 96 && dv == 192 && (chunk == 128 || chunk == 64 || chunk == 32))
+    return bf16_io ? (dk == 96 && dv == 192 && (chunk == 128 || chunk == 64 || chunk == 32 || chunk == 256))
                    : (dk == 16 && dv == 32 && chunk == 32);
 }
 
@@ -749,6 +749,7 @@ static hipError_t launch_bwd_t(const BwdPlan& plan, int B, int T, int H, const B
     ga.dv = io.dv;
     ga.part = part;
     ga.nc = plan.nc;
+    ga.units = (int)units;
     using GS = GradShape<E, DK, DV, C>;
     if constexpr (BF) {
         if ((err = launch_grad_bf16(C, ga, units, stream)) != hipSuccess) return err;
@@ -777,6 +778,9 @@ hipError_t launch_bwd(bool bf16_io, const BwdPlan& plan, int B, int T, int H, in
         return hipGetLastError();
     }
     if (plan.saved != (sbar_in != nullptr)) return hipErrorInvalidValue;
+    if (bf16_io && dk == 96 && dv == 192 && chunk == 256)
+        return launch_bwd_t<bf16, 96, 192, 256>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
+                                                stream);
     if (bf16_io && dk == 96 && dv == 192 && chunk == 128)
         return launch_bwd_t<bf16, 96, 192, 128>(plan, B, T, H, io, lambda, S0, scale, dST, dlambda, dS0, sbar_in, ws,
                                                 stream);

@@ -808,6 +808,8 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
 //            The 100 score blocks go to LDS in bf16; then V0 and V1 pass in
 //            turn through the space the keys took, each wave keeping its value
 //            fragments of both halves in registers for the output strips.
+// With a.sbar, the half-0 workgroup also stores the chunk's start state
+// (row-major, bf16) for the backward.
 // Grid (2 nc, units): blockIdx.x = half * nc + chunk.
 template <int LDK, int NCB>
 __global__ __launch_bounds__((F8<128, LDK, NCB>::NT), 1) void fwd_out256_kernel(FwdArgs a) {
@@ -900,6 +902,20 @@ __global__ __launch_bounds__((F8<128, LDK, NCB>::NT), 1) void fwd_out256_kernel(
         } else {
             out_pair<R, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
             out_pair<R, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+        }
+        if (a.sbar) {
+            // the chunk's start state for the backward, row-major: this wave's
+            // half (16-row blocks 2i + h), columns colbase + 16 cb + n
+            bf16* sbo = static_cast<bf16*>(a.sbar) + ((size_t)bh * a.nc + c) * kDK * kDV;
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const bf16x4 s4 = __builtin_bit_cast(bf16x4, so[i][cb]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sbo[(size_t)(16 * (2 * i + h) + 4 * g + r) * kDV + colbase + 16 * cb + n] = s4[r];
+                }
         }
         return;
     }
@@ -1383,7 +1399,7 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
 // 256-token chunks: the tiled chain (two 128-token passes per chunk), then two
 // output workgroups per (chunk, unit).
 hipError_t launch_c256(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, const float* lambda,
-                       const float* S0, float scale, float* S_final, void* ws, hipStream_t stream) {
+                       const float* S0, float scale, float* S_final, void* sbar, void* ws, hipStream_t stream) {
     constexpr int LDK = 104, NCB = 2;
     hipError_t err = launch_chain<256>(plan, B, T, H, NCB, io, lambda, S0, S_final, ws, stream);
     if (err != hipSuccess) return err;
@@ -1401,6 +1417,7 @@ hipError_t launch_c256(const FwdPlan& plan, int B, int T, int H, const FwdIO& io
     a.scale = scale;
     a.o = io.o;
     a.Ub = ws;
+    a.sbar = sbar;
     a.nc = plan.nc;
     hipLaunchKernelGGL((fwd_out256_kernel<LDK, NCB>), dim3(2 * plan.nc, (unsigned)B * H), dim3(F8<128, LDK, NCB>::NT),
                        0, stream, a);
@@ -1418,8 +1435,8 @@ hipError_t launch_fwd_bf16(const FwdPlan& plan, int B, int T, int H, int chunk, 
         return launch_c<64, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
     if (chunk == 32 && !plan.chain)
         return launch_c<32, 104, 2>(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, nullptr, stream);
-    if (chunk == 256 && plan.chain && !sbar)
-        return launch_c256(plan, B, T, H, io, lambda, S0, scale, S_final, ws, stream);
+    if (chunk == 256 && plan.chain)
+        return launch_c256(plan, B, T, H, io, lambda, S0, scale, S_final, sbar, ws, stream);
     return hipErrorInvalidValue;
 }
 

@@ -122,7 +122,7 @@ struct StateArgs {
     int fuse_scan;        // emit passes: U holds the local passes' states, folded here
 };
 
-// bf16 chains (dk = 96, dv = 192, chunk 64 or 128); grid (grid_x, units).
+// bf16 chains (dk = 96, dv = 192, chunk 32, 64, 128 or 256); grid (grid_x, units).
 hipError_t launch_chain_bf16(int chunk, bool rev, bool emit, const StateArgs& s, unsigned grid_x, unsigned units,
                              hipStream_t stream);
 
@@ -142,9 +142,10 @@ struct GradArgs {
     void* dv;
     float* part;       // [BH][NC][kNPart]
     int nc;
+    int units;         // B * H
 };
 
-// bf16 gradient kernel (dk = 96, dv = 192, chunk 64 or 128): dQ, dK and dV of a chunk.
+// bf16 gradient kernels (dk = 96, dv = 192, chunk 32, 64, 128 or 256): dQ, dK and dV of a chunk.
 hipError_t launch_grad_bf16(int chunk, const GradArgs& ga, unsigned units, hipStream_t stream);
 
 struct BwdPlan {

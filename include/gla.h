@@ -29,8 +29,8 @@
  *   or GLA_BF16 (bfloat16).  States, lambda and every accumulation are fp32.
  *   bf16 outputs are rounded to nearest even.
  * - Supported shapes (instantiated kernels), (dk, dv, chunk):
- *     bf16: (96, 192, 128), (96, 192, 64), (96, 192, 32), and for the forward alone
- *     (96, 192, 256);   fp32: (96, 192, 64) forward, (16, 32, 32);
+ *     bf16: (96, 192, 256), (96, 192, 128), (96, 192, 64), (96, 192, 32);
+ *     fp32: (96, 192, 64) forward only, (16, 32, 32);
  *     decode, either dtype: (dk, dv) = (96, 192) or (16, 32).
  *   Anything else returns GLA_ERR_UNSUPPORTED.  T need not be a multiple of
  *   chunk (the last chunk is partial).

@@ -57,7 +57,7 @@ def test_fwd_rejects_bad_arguments_before_touching_the_device():
     assert fwd(dk=64) == E.GLA_ERR_UNSUPPORTED
     assert fwd(C=512) == E.GLA_ERR_UNSUPPORTED
     assert fwd(C=96) == E.GLA_ERR_UNSUPPORTED
-    assert fwd(dtype=0, C=256) == E.GLA_ERR_UNSUPPORTED          # 256-token chunks: bf16 forward only
+    assert fwd(dtype=0, C=256) == E.GLA_ERR_UNSUPPORTED          # 256-token chunks: bf16 only
     assert fwd(dtype=0, C=128) == E.GLA_ERR_UNSUPPORTED          # fp32 stops at chunk 64
     assert fwd(dtype=1, dk=16, dv=32, C=32) == E.GLA_ERR_UNSUPPORTED
     assert fwd(q=None) == E.GLA_ERR_INVALID_ARG
@@ -202,7 +202,7 @@ def test_saved_state_entry_points_validate():
                                           ws, wsb, None)
 
     assert f(dtype=0) == gla.GLA_ERR_UNSUPPORTED           # fp32 96/192: no backward, so no saved states
-    assert f(C=256) == gla.GLA_ERR_UNSUPPORTED             # no backward at 256-token chunks either
+    assert f(C=512) == gla.GLA_ERR_UNSUPPORTED
     assert f(states=None) == gla.GLA_ERR_INVALID_ARG
     assert f(states=MIS) == gla.GLA_ERR_INVALID_ARG
     assert f(ws=None) == gla.GLA_ERR_WORKSPACE
@@ -234,7 +234,8 @@ def test_bwd_rejects_bad_arguments_before_touching_the_device():
     assert bwd(dk=64) == E.GLA_ERR_UNSUPPORTED
     assert bwd(dtype=0) == E.GLA_ERR_UNSUPPORTED                  # fp32 backward: tiny shape only
     assert bwd(dtype=0, dk=16, dv=32, C=64) == E.GLA_ERR_UNSUPPORTED
-    assert bwd(C=256) == E.GLA_ERR_UNSUPPORTED                    # 256-token chunks: forward only
+    assert bwd(C=512) == E.GLA_ERR_UNSUPPORTED
+    assert bwd(dtype=0, dk=16, dv=32, C=256) == E.GLA_ERR_UNSUPPORTED   # 256-token chunks: bf16 only
     assert bwd(do=None) == E.GLA_ERR_INVALID_ARG
     assert bwd(dv_=MIS) == E.GLA_ERR_INVALID_ARG
     assert bwd(dl=MIS) == E.GLA_ERR_INVALID_ARG

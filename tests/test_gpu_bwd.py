@@ -50,13 +50,13 @@ def test_tiny_fp32_ragged_with_states(T):
     _run(gi.workloads()[0], seed=60 + T, B=2, T=T, s0_var=0.5)
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 32])
+@pytest.mark.parametrize("chunk", [128, 64, 32, 256])
 @pytest.mark.parametrize("T", [1, 100, 300, 1000])
 def test_bf16_ragged_with_states(chunk, T):
     _run(gi.workloads()[1], seed=70 + T + chunk, B=2, T=T, chunk=chunk, s0_var=0.01)
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 32])
+@pytest.mark.parametrize("chunk", [128, 64, 32, 256])
 @pytest.mark.parametrize("T", [40, 2048])
 def test_single_partial_chunk_and_full_length(chunk, T):
     """T = 40: one partial chunk with no second query half (chunks 128, 64), one full
@@ -69,9 +69,9 @@ def test_bf16_segment_split(nseg):
     _run(gi.workloads()[1], seed=90 + nseg, B=1, T=1000, chunk=64, s0_var=0.01, plan={"segments": nseg})
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 32])
+@pytest.mark.parametrize("chunk", [128, 64, 32, 256])
 def test_train_step_config(chunk):
-    """B=8, H=16, T=2048, dk=96, dv=192, bf16, do ~ N(0,1); C=128, 64 and 32."""
+    """B=8, H=16, T=2048, dk=96, dv=192, bf16, do ~ N(0,1); C=128, 64, 32 and 256."""
     _run(gi.workloads()[2], seed=2, chunk=chunk, with_dS=False)
 
 
@@ -119,7 +119,9 @@ def _states_case(w, seed, B, T, chunk, s0_var, chain=None):
 
 @pytest.mark.parametrize("wi,B,T,chunk,chain", [(1, 2, 700, 128, None), (1, 2, 700, 64, None),
                                                 (1, 1, 2048, 128, 1), (1, 1, 2048, 128, 0),
-                                                (1, 1, 300, 128, 1), (0, 2, 200, 32, None)])
+                                                (1, 1, 300, 128, 1), (0, 2, 200, 32, None),
+                                                (1, 2, 1000, 256, None), (1, 1, 2048, 256, None),
+                                                (1, 3, 200, 256, None)])
 def test_saved_states_and_backward_match_oracle(wi, B, T, chunk, chain):
     """gla_fwd_chunked_states writes the state before every chunk (checked against the
     oracle's state after each prefix of whole chunks), and gla_bwd_chunked_states'
@@ -171,7 +173,26 @@ def test_saved_states_training_width(chunk):
     assert_close(f64(dl), r[3], "bf16", "dlambda", batch_axis=None)
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 32])
+def test_saved_states_training_width_c256():
+    """The bench's 256-token training leg exactly: the forward in the tiled-chain form
+    (256-token chunks run only so) storing every chunk's start state, the backward's
+    chains over two sequence segments and the four-workgroup gradient kernel; every
+    sequence's o, dq, dk, dv and dS0 and dlambda against the oracle."""
+    w = gi.workloads()[2]
+    plan = gla.plan_resolve(gla.GLA_BF16, 8, 2048, 16, 96, 192, 256)
+    assert plan["chain"] == 1, plan
+    x, o, S, states, (dq, dk, dv, dl, dS0) = _states_case(w, 263, 8, 2048, 256, 0.0)
+    ro, rS = oracle.fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), scale=x["scale"])
+    assert_close(f64(o), ro, "bf16", "o")
+    assert_close(f64(S), rS, "bf16", "S_final")
+    r = oracle.bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["lam"]), f64(x["do"]), dS_T=f64(x["dS"]),
+                   scale=x["scale"])
+    for got, ref, name in zip((dq, dk, dv, dS0), (r[0], r[1], r[2], r[4]), ("dq", "dk", "dv", "dS0")):
+        assert_close(f64(got), ref, "bf16", name)
+    assert_close(f64(dl), r[3], "bf16", "dlambda", batch_axis=None)
+
+
+@pytest.mark.parametrize("chunk", [128, 64, 32, 256])
 def test_bwd_batch_position_invariant(chunk):
     """Each (batch, head) unit's gradients are computed alone: permuting the batch
     permutes dq, dk, dv and dS0 bit for bit (saved-state pair and recomputing form);

@@ -86,6 +86,8 @@ BWD_CASES = {
     "c64_saved": (1, 2, 1500, 64, "saved"),
     "c32": (1, 2, 700, 32, "recompute"),
     "c32_saved": (1, 2, 1000, 32, "saved"),
+    "c256": (1, 2, 1000, 256, "recompute"),
+    "c256_saved": (1, 2, 1000, 256, "saved"),
     "fp32_tiny": (0, 2, 200, 32, "recompute"),
 }
 

@@ -85,7 +85,8 @@ def test_forward_reads_fused_projection(case):
 
 
 BWD_CASES = {"c128": (1, 2, 1000, 128, False), "c64_saved": (1, 2, 700, 64, True), "train_c128": (2, 8, 2048, 128, True),
-             "c32_saved": (1, 2, 900, 32, True), "fp32_tiny": (0, 2, 200, 32, False)}
+             "c32_saved": (1, 2, 900, 32, True), "c256_saved": (1, 2, 1000, 256, True),
+             "fp32_tiny": (0, 2, 200, 32, False)}
 
 
 @pytest.mark.parametrize("case", sorted(BWD_CASES))
