@@ -596,7 +596,20 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     const int lane = tid % 64, n = lane % 16, g = lane / 16;
     const int h = wave / NCG, colbase = 16 * NCB * (wave % NCG);
     const int partner = h == 0 ? wave + NCG : wave - NCG;
-    const int c = blockIdx.x, bh = blockIdx.y;
+    // (chunk, unit) from the dispatch order (workgroup i runs on XCD i mod 8).
+    // With out_xcd, every chunk of unit u runs on XCD u mod 8, where the tiled
+    // chain walked that unit, so its k, v and chunk start states come from that
+    // XCD's L2 (the launcher sets it when those fit there); else chunk-major.
+    int c, bh;
+    if (a.out_xcd) {
+        const int jx = blockIdx.x / 8;
+        bh = (jx / a.nc) * 8 + blockIdx.x % 8;
+        c = jx % a.nc;
+    } else {
+        c = blockIdx.x % a.nc;
+        bh = blockIdx.x / a.nc;
+    }
+    if (bh >= a.units) return;  // (whole workgroup, before any barrier)
     const int H = a.H, T = a.T;
     const int hd = bh % H, b = bh / H;
     const int t0 = c * C, ceff = min(C, T - t0);
@@ -1362,12 +1375,18 @@ hipError_t launch_c(const FwdPlan& plan, int B, int T, int H, const FwdIO& io, c
         a.U = nullptr;
         a.Ub = ws;
         a.S_final = nullptr;
+        // one workgroup per (chunk, unit); units in groups of 8 (one per XCD)
+        // when an XCD's units' k and v (T (dk + dv) bf16 each) fit its 4 MB L2
+        // with room to spare
+        a.units = (int)units;
+        a.out_xcd = (size_t)((units + 7) / 8) * T * (kDK + kDV) * 2 <= (size_t)3 << 20;
+        const unsigned ogrid = (unsigned)plan.nc * (a.out_xcd ? (units + 7) / 8 * 8 : units);
         if (ep)
-            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, true>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT),
-                               0, stream, a, *ep);
+            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, true>), dim3(ogrid), dim3(F8<C, LDK, NCB>::NT), 0, stream,
+                               a, *ep);
         else
-            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, false>), dim3(plan.nc, units), dim3(F8<C, LDK, NCB>::NT),
-                               0, stream, a, EpilogueArgs{});
+            hipLaunchKernelGGL((fwd_out_kernel<C, LDK, NCB, false>), dim3(ogrid), dim3(F8<C, LDK, NCB>::NT), 0,
+                               stream, a, EpilogueArgs{});
         return hipGetLastError();
       }
     }

@@ -36,6 +36,8 @@ struct FwdArgs {
     int nseg, seg_chunks, nc;
     int psub;          // segment states in U per segment boundary (sub-segment prologue), >= 1
     int fuse_scan;     // 1: U holds the prologue's local states; each segment folds them itself
+    int units;         // B * H (the per-chunk output kernel's grid)
+    int out_xcd;       // output kernel: all chunks of a unit on one XCD (else chunk-major)
 };
 
 struct FwdPlan {
