@@ -281,6 +281,10 @@ def test_plan_controls_validate_and_resolve():
     assert r(shape=(1, 2048, 16, 96, 192, 128)) == {"segments": 16, "chain": 1, "psub": 1, "scan": 0}   # layer
     assert r(shape=(1, 65536, 16, 96, 192, 128)) == {"segments": 16, "chain": 0, "psub": 1, "scan": 0}  # 64k
     assert r(chain=0, shape=(1, 2048, 16, 96, 192, 128))["chain"] == 0
+    # a requested chain runs up to 64 chunks; a longer sequence keeps the segment form
+    assert r(chain=1, shape=(1, 8192, 16, 96, 192, 128))["chain"] == 1
+    assert r(chain=1, shape=(1, 8193, 16, 96, 192, 128))["chain"] == 0
+    assert r(chain=1, shape=(1, 4096, 16, 96, 192, 64))["chain"] == 1
     assert r(psub=1) == {"segments": 2, "chain": 0, "psub": 1, "scan": 1}
     assert r(scan=0)["scan"] == 0
     assert r(segments=4, scan=1)["scan"] == 0          # six local states before the last segment: a scan

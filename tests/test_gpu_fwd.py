@@ -98,6 +98,16 @@ def test_bf16_plans(chunk, mode):
                    plan=PLANS[mode])
 
 
+@pytest.mark.parametrize("chunk,T", [(128, 8192), (64, 4096), (128, 8100)])
+def test_chain_at_its_longest(chunk, T):
+    """The tiled chain at the most chunks it runs (64; a longer sequence keeps the
+    segment form), S0 given: its snapshot workspace at full size, and at 8,192
+    tokens the output kernel's chunk-major order (the unit's k and v exceed an
+    XCD's L2 share); 8,100 tokens end in a partial chunk."""
+    assert gla.plan_resolve(gla.GLA_BF16, 1, T, 16, 96, 192, chunk, {"chain": 1})["chain"] == 1
+    _run_and_check(gi.workloads()[1], seed=5150 + chunk + T, B=1, T=T, chunk=chunk, s0_var=0.01, plan={"chain": 1})
+
+
 @pytest.mark.parametrize("chunk,T,s0", [(128, 2048, None), (64, 1000, None), (128, 700, 0.01), (64, 700, 0.01)])
 @pytest.mark.parametrize("want_final", [True, False])
 def test_chain_matches_one_chunk_segments_bitwise(chunk, T, s0, want_final):
