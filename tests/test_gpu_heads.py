@@ -177,3 +177,91 @@ def test_forward_epilogue_heads(H, plan):
                          e["tier"])
     assert_close(f64(y), ry, "bf16", "y")
     assert_close(f64(S), rS, "bf16", "S_final")
+
+
+# ---------------------------------------------------------------- head permutation
+# Each (batch, head) unit is computed on its own with its own lambda, whatever its
+# place in the launch (its XCD group, its slot in an epilogue batch): permuting the
+# heads of every input together with lambda (and the epilogue's per-head parameters)
+# permutes every output bit for bit.
+
+PERM = [5, 0, 11, 3, 14, 9, 1, 7, 15, 2, 12, 6, 10, 4, 13, 8]
+
+
+def _perm_heads(t, axis):
+    return None if t is None else t.index_select(axis, torch.tensor(PERM, device=t.device)).contiguous()
+
+
+@pytest.mark.parametrize("chunk,plan", [(128, {"chain": 1}), (128, {"chain": 0}), (64, None), (256, None),
+                                        (32, None)])
+def test_head_permutation_forward(chunk, plan):
+    w = _wl(16, chunk, B=2, T=500)
+    x = gi.fwd_inputs(w, DEV, 7500 + chunk, s0_var=0.01)
+    _say(f"fwd head permutation C={chunk} plan={plan}")
+    kw = dict(scale=x["scale"], chunk=chunk, plan=plan)
+    o, S = gla.fwd_chunked(x["q"], x["k"], x["v"], x["lam"], S0=x["S0"], **kw)
+    op, Sp = gla.fwd_chunked(_perm_heads(x["q"], 2), _perm_heads(x["k"], 2), _perm_heads(x["v"], 2),
+                             _perm_heads(x["lam"], 0), S0=_perm_heads(x["S0"], 1), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(op, _perm_heads(o, 2)), "o"
+    assert torch.equal(Sp, _perm_heads(S, 1)), "S_final"
+
+
+@pytest.mark.parametrize("chunk,form", [(128, "saved"), (128, "recompute"), (64, "saved"), (256, "recompute"),
+                                        (32, "recompute")])
+def test_head_permutation_backward(chunk, form):
+    w = _wl(16, chunk, B=2, T=500)
+    x = gi.fwd_inputs(w, DEV, 7600 + chunk, with_do=True, with_dS=True, s0_var=0.01)
+    _say(f"bwd head permutation C={chunk} {form}")
+
+    def run(q, k, v, lam, d_o, S0, dS):
+        if form == "saved":
+            _, _, st = gla.fwd_chunked_states(q, k, v, lam, S0=S0, scale=x["scale"], chunk=chunk)
+            return gla.bwd_chunked_states(q, k, v, lam, d_o, st, S0=S0, dS_final=dS, scale=x["scale"], chunk=chunk)
+        return gla.bwd_chunked(q, k, v, lam, d_o, S0=S0, dS_final=dS, scale=x["scale"], chunk=chunk)
+
+    base = run(x["q"], x["k"], x["v"], x["lam"], x["do"], x["S0"], x["dS"])
+    perm = run(*(_perm_heads(x[n], 2) for n in ("q", "k", "v")), _perm_heads(x["lam"], 0), _perm_heads(x["do"], 2),
+               _perm_heads(x["S0"], 1), _perm_heads(x["dS"], 1))
+    torch.cuda.synchronize()
+    for got, ref, axis, name in zip(perm, base, (2, 2, 2, 0, 1), ("dq", "dk", "dv", "dlambda", "dS0")):
+        assert torch.equal(got, _perm_heads(ref, axis)), name
+
+
+def test_head_permutation_decode_and_epilogue():
+    """Decode (plain and with the fused epilogue) and the forward with the fused
+    epilogue: heads permuted with lambda, the gate weights a_h and the tier map."""
+    N = 9
+    w = gi.Workload("heads-perm", N, 1, 16, 96, 192, 0, "bf16", tuple(_lams(16)), 96 ** -0.5, 0.5, 1)
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
+    S = gi.decode_state(w, DEV, seed=77, layer=0)
+    d = gi.decode_token_inputs(w, DEV, seed=77, layer=0, step=0)
+    e = gi.epilogue_inputs(w, DEV, 77, (N,))
+    tier_p = [e["tier"][h] for h in PERM]
+    _say("decode / epilogue head permutation N=9")
+    Sa, Sb = S.clone(), _perm_heads(S, 1)
+    o = gla.decode_step(d["q"], d["k"], d["v"], lam, Sa, scale=w.scale)
+    op = gla.decode_step(*(_perm_heads(d[n], 1) for n in ("q", "k", "v")), _perm_heads(lam, 0), Sb, scale=w.scale)
+    Se, Sf = S.clone(), _perm_heads(S, 1)
+    y = gla.decode_step_epilogue(d["q"], d["k"], d["v"], e["g"], lam, Se, e["norm_w"], e["tier"],
+                                 aug_a=e["aug_a"], scale=w.scale)
+    yp = gla.decode_step_epilogue(*(_perm_heads(d[n], 1) for n in ("q", "k", "v")), _perm_heads(e["g"], 1),
+                                  _perm_heads(lam, 0), Sf, e["norm_w"], tier_p, aug_a=_perm_heads(e["aug_a"], 0),
+                                  scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(op, _perm_heads(o, 1)) and torch.equal(Sb, _perm_heads(Sa, 1)), "decode"
+    assert torch.equal(yp, _perm_heads(y, 1)) and torch.equal(Sf, _perm_heads(Se, 1)), "decode with epilogue"
+
+    wf = _wl(16, B=1, T=700)
+    x = gi.fwd_inputs(wf, DEV, 7700, s0_var=0.01)
+    ef = gi.epilogue_inputs(wf, DEV, 7700, (1, 700))
+    for plan in ({"chain": 1}, {"chain": 0}):
+        yf, Sf_ = gla.fwd_chunked_epilogue(x["q"], x["k"], x["v"], x["lam"], ef["g"], ef["norm_w"], ef["tier"],
+                                           aug_a=ef["aug_a"], S0=x["S0"], scale=x["scale"], chunk=128, plan=plan)
+        yfp, Sfp = gla.fwd_chunked_epilogue(*(_perm_heads(x[n], 2) for n in ("q", "k", "v")), _perm_heads(x["lam"], 0),
+                                            _perm_heads(ef["g"], 2), ef["norm_w"], [ef["tier"][h] for h in PERM],
+                                            aug_a=_perm_heads(ef["aug_a"], 0), S0=_perm_heads(x["S0"], 1),
+                                            scale=x["scale"], chunk=128, plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(yfp, _perm_heads(yf, 2)), f"forward with epilogue y, plan {plan}"
+        assert torch.equal(Sfp, _perm_heads(Sf_, 1)), f"forward with epilogue S_final, plan {plan}"
