@@ -79,6 +79,43 @@ def test_decode_full_width_sampled():
     torch.cuda.empty_cache()
 
 
+def test_decode_serving_run_64_steps_sampled_pairs():
+    """The whole serving workload as the decode benchmark runs it: the 24-layer pool of
+    1,280 sequences (36.2 GB fp32), 64 steps of one launch per layer.  A seeded sample of
+    64 (layer, sequence) pairs, all 16 heads each, follows the oracle from the regenerated
+    initial pages through every step: the outputs at each step, the pages at steps 16, 32,
+    48 and 64."""
+    w = gi.workloads()[4]
+    L, N, STEPS = w.decode_layers, w.B, 64
+    lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
+    pool = torch.empty((L, N, w.H, w.dk, w.dv), dtype=torch.float32, device=DEV)
+    for layer in range(L):
+        gi.decode_state(w, DEV, seed=4, layer=layer, out=pool[layer])
+    rng = np.random.default_rng(404)
+    flat = np.sort(rng.choice(L * N, 64, replace=False))
+    rows = {layer: flat[flat // N == layer] % N for layer in range(L)}
+    rows = {layer: r for layer, r in rows.items() if len(r)}
+    Sref = {layer: f64(pool[layer][r]) for layer, r in rows.items()}
+    _say(f"decode serving run: {L} layers x {N} sequences x {STEPS} steps, pairs in {len(rows)} layers")
+    for step in range(STEPS):
+        outs = {}
+        for layer in range(L):
+            d = gi.decode_token_inputs(w, DEV, seed=4, layer=layer, step=step)
+            o = gla.decode_step(d["q"], d["k"], d["v"], lam, pool[layer], scale=w.scale)
+            if layer in rows:
+                r = torch.as_tensor(rows[layer], device=DEV)
+                outs[layer] = (f64(o[r]), f64(d["q"][r]), f64(d["k"][r]), f64(d["v"][r]))
+        for layer, (o, q, k, v) in outs.items():
+            ro, Sref[layer] = oracle.decode(q, k, v, f64(lam), Sref[layer], scale=w.scale)
+            assert_close(o, ro, "bf16", f"o layer {layer} step {step}")
+        if step % 16 == 15:
+            torch.cuda.synchronize()
+            for layer, r in rows.items():
+                assert_close(f64(pool[layer][r]), Sref[layer], "bf16", f"pages layer {layer} step {step}")
+    del pool
+    torch.cuda.empty_cache()
+
+
 def test_decode_batch_position_invariant():
     w = gi.workloads()[4]
     lam = torch.tensor(w.lambdas, dtype=torch.float32, device=DEV)
