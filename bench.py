@@ -179,6 +179,44 @@ class FwdLeg:
             raise RuntimeError(f"gla_fwd_chunked: {self.gla.status_str(st)}")
 
 
+class SplitLeg:
+    """A single-sequence prefill as two gla_fwd_chunked calls of T/2 tokens each, the
+    first one's final state the second one's initial state (the split a sequence-parallel
+    prefill would make); pre-marshalled on the inputs and outputs of a FwdLeg (B = 1, so
+    each half of every token-major tensor is contiguous)."""
+
+    def __init__(self, leg, gla, torch, chunk):
+        x = leg.x
+        B, T, H, dk = x["q"].shape
+        dv = x["v"].shape[3]
+        assert B == 1 and T % 2 == 0
+        half = T // 2
+        dev = x["q"].device
+        dt = gla.GLA_BF16 if x["q"].dtype == torch.bfloat16 else gla.GLA_F32
+        es = x["q"].element_size()
+        need = gla.fwd_workspace_bytes(dt, 1, half, H, dk, dv, chunk)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        self.S1 = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
+        self.stream = leg.stream
+        self.tokens = T
+        p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        off = lambda t, d: ctypes.c_void_p(t.data_ptr() + half * H * d * es)
+        sc = ctypes.c_float(x["scale"])
+        self.fn = gla.load().gla_fwd_chunked
+        tail = (p(self.ws), ctypes.c_size_t(need))
+        self.first = (dt, 1, half, H, dk, dv, chunk, p(x["q"]), p(x["k"]), p(x["v"]), p(x["lam"]), p(x["S0"]),
+                      sc, p(leg.o), p(self.S1), None) + tail
+        self.second = (dt, 1, half, H, dk, dv, chunk, off(x["q"], dk), off(x["k"], dk), off(x["v"], dv),
+                       p(x["lam"]), p(self.S1), sc, off(leg.o, dv), p(leg.S), None) + tail
+        self.gla = gla
+
+    def __call__(self):
+        for args in (self.first, self.second):
+            st = self.fn(*args, ctypes.c_void_p(self.stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"gla_fwd_chunked: {self.gla.status_str(st)}")
+
+
 class TrainLeg:
     """Pre-marshalled forward + backward (dq, dk, dv, dlambda) on the mixer-train workload:
     the forward saving every chunk's start state and the backward reading them
@@ -850,7 +888,16 @@ def main():
                      "alg_bytes_per_launch": l_bytes,
                      "alg_flops_per_launch": l_flops, "mfma_tflops": l_flops / l_avg / 1e12,
                      "mfma_frac": l_flops / l_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS}}
-    del lleg
+    # the same prefill split in two halves carrying the state
+    sleg = SplitLeg(lleg, gla, torch, args.chunk)
+    s_wall, s_gpu = time_region(torch, sleg.stream, sleg, max(K // 4, 8), W)
+    s_avg = s_gpu / max(K // 4, 8)
+    result["long_prefill"]["split_2x%d" % (w3.T // 2)] = {
+        "calls": "two gla_fwd_chunked calls of %d tokens, the state carried between them" % (w3.T // 2),
+        "avg_pair_us": s_avg * 1e6, "tokens_per_s": sleg.tokens / s_avg,
+        "plan_per_half": gla.plan_resolve(gla.GLA_BF16, 1, w3.T // 2, 16, 96, 192, args.chunk),
+        "hbm_frac": l_bytes / s_avg / 1e9 / HBM_PEAK_GBS}
+    del sleg, lleg
     torch.cuda.empty_cache()
 
     # ---- the forward by chunk size (the pages' chunk-size trade-off, on MI355X): the
