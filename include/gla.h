@@ -32,8 +32,10 @@
  *     bf16: (96, 192, 256), (96, 192, 128), (96, 192, 64), (96, 192, 32);
  *     fp32: (96, 192, 64) forward only, (16, 32, 32);
  *     decode, either dtype: (dk, dv) = (96, 192) or (16, 32).
- *   Anything else returns GLA_ERR_UNSUPPORTED.  T need not be a multiple of
- *   chunk (the last chunk is partial).
+ *   Anything else returns GLA_ERR_UNSUPPORTED, and so does a chunked forward
+ *   or backward with B*H above 65,535 (the units take one 16-bit grid
+ *   dimension; a larger batch is split by the caller).  T need not be a
+ *   multiple of chunk (the last chunk is partial).
  * - Validation is host-only and finishes before any HIP call: on any error
  *   nothing is enqueued and no output is touched.  Pointers must be 16-byte
  *   aligned.  Every computing entry point returns a gla_status.  lambda in
@@ -345,7 +347,7 @@ gla_status gla_decode_step_epilogue(gla_dtype dtype, int N, int H, int dk, int d
  * Supported: K == 4, D a multiple of 8 (D <= 2^20).  T == 0 passes the window
  * through.  One kernel launch, no workspace.
  * Errors: a NULL/misaligned required pointer, negative sizes -> GLA_ERR_INVALID_ARG;
- * another K or D -> GLA_ERR_UNSUPPORTED.
+ * another K or D, B > 65,535 or T > 2,097,120 -> GLA_ERR_UNSUPPORTED.
  */
 gla_status gla_conv1d_silu(gla_dtype dtype, int B, int T, int D, int K,
                            const void* x, const float* w, const float* bias,
@@ -359,7 +361,8 @@ gla_status gla_conv1d_silu(gla_dtype dtype, int B, int T, int D, int K,
  *          windows [P][K][D] with row n using window slots[n] (device int32 [N]);
  *          a slot outside [0, P) is a padding row: zero output, no window touched.
  * Each row is computed on its own (bit-identical whatever batch it is in).
- * Errors and support: as gla_conv1d_silu; P < 0 with slots -> GLA_ERR_INVALID_ARG.
+ * Errors and support: as gla_conv1d_silu (N in place of B); P < 0 with slots ->
+ * GLA_ERR_INVALID_ARG.
  */
 gla_status gla_conv1d_silu_decode(gla_dtype dtype, int N, int D, int K,
                                   const void* x, const float* w, const float* bias,

@@ -178,6 +178,8 @@ def test_conv_rejects_bad_arguments():
     assert c(wo=MIS) == gla.GLA_ERR_INVALID_ARG
     assert c(B=0, x=None) == gla.GLA_OK
     assert c(T=0, x=None, y=None) == gla.GLA_OK          # nothing to write
+    assert c(B=65536, T=1, D=8) == gla.GLA_ERR_UNSUPPORTED            # grid limits
+    assert c(B=1, T=2_097_121, D=8) == gla.GLA_ERR_UNSUPPORTED
 
     def d(dtype=1, N=3, D=3072, K=4, x=P, w=P, win=P, Pn=0, slots=None, y=P):
         return lib.gla_conv1d_silu_decode(dtype, N, D, K, x, w, None, win, Pn, slots, y, None)
@@ -189,6 +191,7 @@ def test_conv_rejects_bad_arguments():
     assert d(slots=MIS, Pn=4) == gla.GLA_ERR_INVALID_ARG
     assert d(y=None) == gla.GLA_ERR_INVALID_ARG
     assert d(N=0, x=None) == gla.GLA_OK
+    assert d(N=65536, D=8) == gla.GLA_ERR_UNSUPPORTED
 
 
 def test_saved_state_entry_points_validate():
