@@ -536,6 +536,34 @@ def cpu_baseline_long(gi, w, seed, tokens=8192, budget_s=3.0):
                       f"in {el:.1f} s (the recurrence's cost is linear in T)"}
 
 
+def cpu_baseline_epilogue(gi, w, seed, budget_s=2.0):
+    """fp64 oracle mixer epilogue over the Laplace layer's 2,048 rows (inputs drawn on the CPU)."""
+    import oracle
+
+    x = gi.fwd_inputs(w, "cpu", seed)
+    e = gi.epilogue_inputs(w, "cpu", seed, (w.B, w.T))
+    f = lambda t: t.double().numpy()
+    q, k, v, g, a, nw = f(x["q"]), f(x["k"]), f(x["v"]), f(e["g"]), f(e["aug_a"]), f(e["norm_w"])
+    reps, el = _repeat(lambda: oracle.epilogue(q, k, v, v, g, a, nw, e["tier"]), budget_s, 200)
+    rows = w.B * w.T
+    return {"value": reps * rows / el, "unit": "rows/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"fp64 epilogue (gate, tier RMSNorm, SiLU gate) of the {rows} rows x 16 heads of the "
+                      f"Laplace layer x {reps} in {el:.1f} s"}
+
+
+def cpu_baseline_conv(gi, seed, budget_s=2.0):
+    """fp64 oracle depth-wise conv + SiLU over one 2,048-token sequence of width 3,072."""
+    import oracle
+
+    c = gi.conv_inputs(1, 2048, 3072, "bf16", "cpu", seed=seed)
+    f = lambda t: t.double().numpy()
+    x, wt, b, win = f(c["x"]), f(c["w"]), f(c["bias"]), f(c["win"])
+    reps, el = _repeat(lambda: oracle.conv1d(x, wt, b, win), budget_s, 200)
+    return {"value": reps * 2048 / el, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"fp64 conv (width 4) + SiLU of 1 of the 8 sequences (T=2048, D=3072) x {reps} in "
+                      f"{el:.1f} s; tokens/s of that sample"}
+
+
 def cpu_baseline_decode(gi, w, seed, budget_s=3.0):
     import oracle
 
@@ -1070,6 +1098,9 @@ def main():
             result["train"]["cpu_baseline"] = cpu_baseline_train(gi, w2, 2)
         if not args.no_decode:
             result["decode"]["cpu_baseline"] = cpu_baseline_decode(gi, ws[4], 4)
+        result["epilogue"]["cpu_baseline"] = cpu_baseline_epilogue(gi, w1, 7)
+        if "conv" in result:
+            result["conv"]["cpu_baseline"] = cpu_baseline_conv(gi, 5)
     print(json.dumps(result), flush=True)
 
 
