@@ -156,11 +156,16 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
 
         if constexpr (EMIT) {
             // Copy the snapshot out as 16-byte row pieces (96 rows x 24 pieces).
-            bf16* snap = static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV;
+            // (non-temporal buffer stores: the training step 369.5 -> 368.2 us at C = 128,
+            // 431.0 -> 427.6 at 64, the same bits)
+            const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV, 0, kDK * kDV * 2, kBufWord3);
 #pragma unroll
             for (int k = 0; k < NSP; ++k) {
                 const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
-                *reinterpret_cast<bf16x8*>(snap + row * kDV + col) = *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col)), rs,
+                    (row * kDV + col) * 2, 0, kCpolNT);
             }
         }
 
@@ -225,12 +230,14 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
             if constexpr (EMIT) {
                 if (sp == 0) {
                     // Copy the snapshot out as 16-byte row pieces (96 rows x 24 pieces).
-                    bf16* snap = static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV;
+                    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+                        static_cast<bf16*>(a.snap) + ((size_t)bh * a.nc + c) * kDK * kDV, 0, kDK * kDV * 2, kBufWord3);
 #pragma unroll
                     for (int k = 0; k < NSP; ++k) {
                         const int pc = tid + k * kNT, row = pc / (kDV / 8), col = (pc % (kDV / 8)) * 8;
-                        *reinterpret_cast<bf16x8*>(snap + row * kDV + col) =
-                            *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(Sb + row * LDV + col)), rs,
+                            (row * kDV + col) * 2, 0, kCpolNT);
                     }
                 }
             }

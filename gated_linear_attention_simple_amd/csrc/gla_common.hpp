@@ -21,6 +21,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }

@@ -1194,7 +1194,9 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
             spos[j] = ((wo * 3 + i) * a.ncbo + cb) * 64 + lane;
         }
     }
-    bf16x4* snap = reinterpret_cast<bf16x4*>(a.snap + (size_t)bh * nc * kDK * kDV);
+    // (written with non-temporal buffer stores, one resource per chunk's snapshot: 24.97
+    // against 25.59 us per Laplace-layer call with plain stores, the same bits)
+    bf16* const snap = a.snap + (size_t)bh * nc * kDK * kDV;
 
     // Pass x (chunk x / NS, its rows R (x % NS) ..) sits in ring slot x % D;
     // staging writes it to LDS buffer x % 3 (keys scaled by c_j), then the slot
@@ -1283,8 +1285,11 @@ __global__ __launch_bounds__((ChainShape<C, NVB, NJ>::NT)) void fwd_chain_kernel
 #pragma unroll
                         for (int r = 0; r < 4; ++r) S[j][r] = fmaf(lamC, S[j][r], Lc[prv][j][r]);  // a full chunk
                     }
-                    snap[(size_t)c * (kDK * kDV / 4) + spos[j]] =
-                        bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]), to_bf16(S[j][3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(u32x2, bf16x4{to_bf16(S[j][0]), to_bf16(S[j][1]), to_bf16(S[j][2]),
+                                                         to_bf16(S[j][3])}),
+                        __builtin_amdgcn_make_buffer_rsrc(snap + (size_t)c * kDK * kDV, 0, kDK * kDV * 2, kBufWord3),
+                        spos[j] * 8, 0, kCpolNT);
                 }
             }
             __syncthreads();  // pass x + 2 staged; pass x + 1's operands read

@@ -156,6 +156,8 @@ __device__ __forceinline__ uint4 scale_bf16x8(uint4 raw, float c) {
 
 // Buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9-family parts.
 constexpr int kBufWord3 = 0x00020000;
+// Cache-policy operand of the buffer intrinsics on gfx950: non-temporal (nt).
+constexpr int kCpolNT = 2;
 
 // Stages a ROWS x D bf16 tile like TileStage, with buffer loads: the tile base
 // and its byte range live in one scalar resource and each piece needs only a
