@@ -50,7 +50,6 @@ __device__ __forceinline__ float group_sum(float x) {
 
 constexpr int lanes_for(int n) { return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
 constexpr int kEpiThreads = 256;
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte piece <-> VEC floats
 template <typename E> struct Piece;
@@ -217,9 +216,10 @@ __global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(EpilogueArgs a) {
         for (int e = 0; e < VEC; ++e) y[e] = g[e] * fast_sigmoid(g[e]) * x[e] * inv * w[e];
         const Pos p = where(kb);                              // (past the end: range 0, store dropped)
         const int ry = range_of(p, a.ry, DV);
+        // (y leaves with non-temporal stores: 97.8 -> 93.6 us at the training width)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Piece<E>::pack(y)),
                                                rsrc(static_cast<E*>(a.y) + p.r0 * a.ry, ry),
-                                               off_of(p, a.ry, DV, NVL, ry), 0, 0);
+                                               off_of(p, a.ry, DV, NVL, ry), 0, kCpolNT);
     };
 
     // two register sets in turn (no copies between them); the loop body is two
