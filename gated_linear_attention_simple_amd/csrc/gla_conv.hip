@@ -88,10 +88,12 @@ __device__ __forceinline__ void ld_f32(__amdgpu_buffer_rsrc_t r, int e, float* f
 #pragma unroll
     for (int i = 0; i < VEC / 4; ++i) CPiece<float>::unpack(cld16(r, (e + 4 * i) * 4), f + 4 * i);
 }
-template <int VEC>
+template <int VEC, int CPOL = 0>
 __device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, int e, const float* f) {
 #pragma unroll
-    for (int i = 0; i < VEC / 4; ++i) cst16(r, (e + 4 * i) * 4, CPiece<float>::pack(f + 4 * i));
+    for (int i = 0; i < VEC / 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(cu32x4, CPiece<float>::pack(f + 4 * i)), r,
+                                               (e + 4 * i) * 4, 0, CPOL);
 }
 
 // Per-thread filter: taps w[c][j] and bias of the thread's VEC channels.
@@ -239,9 +241,10 @@ __global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvArgs a) {
     for (int c = 0; c < VEC; ++c) yv[c] = tp.out(c, h[0][c], h[1][c], h[2][c], xt[c]);
     cst16(ry, c0 * ES, CPiece<E>::pack(yv));
     // the window drops its oldest input: slots 0..K-2 <- old slots 1..K-1, slot K-1 <- x_n
+    // (non-temporal stores: 25.2 -> 24.7 us for 1,280 rows; non-temporal loads were slower)
 #pragma unroll
-    for (int s = 0; s < kConvK - 1; ++s) st_f32<VEC>(rwin, (int)(s * D + c0), h[s]);
-    st_f32<VEC>(rwin, (int)((kConvK - 1) * D + c0), xt);
+    for (int s = 0; s < kConvK - 1; ++s) st_f32<VEC, kCpolNT>(rwin, (int)(s * D + c0), h[s]);
+    st_f32<VEC, kCpolNT>(rwin, (int)((kConvK - 1) * D + c0), xt);
 }
 
 }  // namespace
