@@ -719,12 +719,36 @@ __global__ __launch_bounds__((F8<C, LDK, NCB>::NT), 1) void fwd_out_kernel(FwdAr
     };
     if constexpr (!EPI) {
         if constexpr (C == 128) {
+            // o staged row-major in the value tile (free once every wave holds its
+            // value fragments), then written as whole 384-byte rows with non-temporal
+            // stores (23.39 against 24.94 us per Laplace-layer call with each lane's
+            // 8-byte pieces stored directly; the same bits)
+            __syncthreads();   // every wave's value fragments are read
+            bf16* Os = Vs;
+            auto stage = [&](int, int irow, const f32x4(&OT)[NCB]) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    *reinterpret_cast<bf16x4*>(Os + irow * LDV + colbase + 16 * cb + 4 * g) =
+                        bf16x4{to_bf16(OT[cb][0]), to_bf16(OT[cb][1]), to_bf16(OT[cb][2]), to_bf16(OT[cb][3])};
+            };
             if (h == 0) {
-                out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
-                out_pair<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                out_strip<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, n, g, stage);
+                out_strip<C, LDK, NCB, 3>(Qs, As, sop, vf, pws, n, g, stage);
             } else {
-                out_pair<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
-                out_pair<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
+                out_strip<C, LDK, NCB, 1>(Qs, As, sop, vf, pws, n, g, stage);
+                out_strip<C, LDK, NCB, 2>(Qs, As, sop, vf, pws, n, g, stage);
+            }
+            __syncthreads();   // o complete in LDS
+            const auto ro = __builtin_amdgcn_make_buffer_rsrc(ob + (size_t)t0 * tokO, 0,
+                                                              __builtin_amdgcn_readfirstlane(ceff * (int)tokO * 2), kBufWord3);
+            constexpr int KCO = kDV / 8;   // 16-byte pieces per row
+#pragma unroll
+            for (int k = 0; k < (C * KCO + NT - 1) / NT; ++k) {
+                const int pc = tid + k * NT;
+                if ((C * KCO) % NT != 0 && pc >= C * KCO) break;
+                const int row = pc / KCO, col = (pc % KCO) * 8;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, *reinterpret_cast<const bf16x8*>(Os + row * LDV + col)),
+                                                       ro, (row * (int)tokO + col) * 2, 0, kCpolNT);
             }
         } else {
             if (h == 0) out_pair<C, LDK, NCB, 0>(Qs, As, sop, vf, pws, ob, tokO, t0, ceff, colbase, n, g);
