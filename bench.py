@@ -778,7 +778,7 @@ def ingest_counters(csvs):
 
 
 COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 170 rocprofv3 --pmc {counters} -f csv "
-               "-d gpurun_out/pmc/{name} -o pmc -- python3 bench.py --counters")
+               "-d $R/gpurun_out/pmc/{name} -o pmc -- python3 $R/bench.py --counters")
 GROUP_DESC = {"train": "training step, B=8 H=16 T=2048 C=128 (saved-state pair)",
               "fwd": "Laplace-layer forward, B=1 H=16 T=2048 C=128",
               "long": "64k-token prefill, B=1 H=16 T=65536 C=128, S0 given",
@@ -791,7 +791,8 @@ def write_counter_summary(out):
              "Commands (one run per counter set, the sets of bench.COUNTER_PASSES):", ""]
     for name, cs in COUNTER_PASSES.items():
         lines.append("    " + COUNTER_CMD.format(counters=" ".join(cs), name=name))
-    lines += ["", "then `python bench.py --ingest-counters gpurun_out/pmc/{fetch,write,sq_mfma,sq_wait}/"
+    lines += ["", "with R the repository root; then `python bench.py --ingest-counters "
+                  "gpurun_out/pmc/{fetch,write,sq_mfma,sq_wait}/"
                   "pmc_counter_collection.csv`.", "",
               "HBM bytes: FETCH_SIZE x %.3f + WRITE_SIZE x %.3f (the factors that make the 256 MiB marker "
               "copies read and write 256 MiB). Utilisations: counter / (dispatch time x %.1f GHz x units) with "
@@ -823,7 +824,9 @@ def ingest_ktrace(stats_csv):
     rows = list(csv.DictReader(open(stats_csv)))
     lines = ["# Kernel time per kernel (rocprofv3 --kernel-trace --stats of a bench run)", "",
              "    cd /tmp && export TMPDIR=/tmp && timeout -s KILL 200 rocprofv3 --kernel-trace --stats -f csv "
-             "-d gpurun_out/pmc/ktrace -o kt -- python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline", "",
+             "-d $R/gpurun_out/pmc/ktrace -o kt -- python3 $R/bench.py --steps 10 --warmup 3 --no-cpu-baseline", "",
+             "with R the repository root; then `python bench.py --ingest-ktrace "
+             "gpurun_out/pmc/ktrace/kt_kernel_stats.csv`.", "",
              "(source digest %s; every leg of the bench, so a kernel's average mixes the workloads that "
              "launch it: fwd_bf16_kernel<128, ...> runs in the training step's forward and in the 64k prefill)"
              % src_digest(), "", "| kernel | calls | average us | min us | max us | share of GPU time % |",
