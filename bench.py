@@ -470,6 +470,44 @@ def time_decode(torch, leg, K, W):
     return time_region(torch, leg.stream, one_step, K, W)
 
 
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def _dpm_current(text):
+    """The active level of a pp_dpm_* sysfs table ('1: 2400Mhz *' -> '2400Mhz')."""
+    for line in (text or "").splitlines():
+        if line.rstrip().endswith("*"):
+            return line.split(":", 1)[-1].replace("*", "").strip()
+    return None
+
+
+def machine_info(torch):
+    """ROCm / HIP versions, the device, and its current engine and memory clock levels
+    (from the driver's sysfs tables; null where the box does not expose them)."""
+    import glob
+
+    info = {"rocm": _read("/opt/rocm/.info/version"), "torch": torch.__version__,
+            "hip_runtime": getattr(torch.version, "hip", None)}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info.update({"device": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+                     "hbm_gib": round(p.total_memory / 2 ** 30, 1)})
+    except Exception:  # noqa: BLE001  (no device: report what is known)
+        pass
+    sclk = mclk = None
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        if _read(os.path.join(dev, "vendor")) == "0x1002":
+            sclk = sclk or _dpm_current(_read(os.path.join(dev, "pp_dpm_sclk")))
+            mclk = mclk or _dpm_current(_read(os.path.join(dev, "pp_dpm_mclk")))
+    info.update({"sclk": sclk, "mclk": mclk})
+    return info
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -1094,6 +1132,7 @@ def main():
     del fe
     torch.cuda.empty_cache()
 
+    result["env"] = machine_info(torch)   # clocks read right after the timed legs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_fwd(gi, w1, 1)
         result["long_prefill"]["cpu_baseline"] = cpu_baseline_long(gi, ws[3], 3)

@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (CPU only): the one-GPU contract, the algorithmic work counts
-the roofline figures divide by, the parsing of rocprofv3 output, and the rule that stored
+the roofline figures divide by, the parsing of rocprofv3 output and of clock tables, and the rule that stored
 counter traffic is reported only for the kernel sources it was taken on."""
 import json
 import os
@@ -92,3 +92,20 @@ def test_stored_traffic_only_for_the_sources_it_was_taken_on(tmp_path, monkeypat
     with open(root / "gated_linear_attention_simple_amd" / "csrc" / "gla_grad_bf16.hip", "a") as f:
         f.write("\n// changed\n")
     assert bench.stored_traffic("grad", 1.0) is None
+
+
+def test_clock_level_parsing():
+    """The active level of a pp_dpm_* table is the line marked '*'; none marked: None."""
+    assert bench._dpm_current("0: 500Mhz\n1: 1800Mhz *\n2: 2400Mhz\n") == "1800Mhz"
+    assert bench._dpm_current("0: 900Mhz\n1: 1300Mhz\n") is None
+    assert bench._dpm_current(None) is None
+
+
+def test_machine_info_without_a_device():
+    """On a host with no GPU the record still has every field (unknown ones null)."""
+    import torch
+
+    info = bench.machine_info(torch)
+    for key in ("rocm", "torch", "hip_runtime", "sclk", "mclk"):
+        assert key in info
+    json.dumps(info)
