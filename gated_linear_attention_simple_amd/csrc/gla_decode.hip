@@ -39,8 +39,8 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
     constexpr int RPT = DK / RG;         // rows per thread
     static_assert(DK % RG == 0, "rows must split evenly");
 
-    __shared__ float qs[DK];
-    __shared__ float ks[DK];
+    __shared__ float qs[DK + 1];   // (slot DK: written by the threads past DK, never read)
+    __shared__ float ks[DK + 1];
     __shared__ f32x4 part[RG][NCG];
     __shared__ float red[NT / 64 + 1];    // epilogue: gate logit, per-wave sums of squares
 
@@ -59,19 +59,30 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
         page = (size_t)slot * H + h;
     }
 
-    for (int i = t; i < DK; i += NT) {
-        qs[i] = to_f32(q[(size_t)unit * DK + i]);
-        ks[i] = to_f32(k[(size_t)unit * DK + i]);
-    }
-    const float lam = lambda[h];
-    float vc[4];
+    // q and k are requested first and staged once they arrive, while the state
+    // loads issued between them are still in flight (the memory counter is in
+    // order, so the staging waits only for the two loads ahead of the state).
+    // (Every thread loads an element and stores it, threads past DK the first one
+    // into a spare slot, so no branch holds the loads back behind the state's.)
+    static_assert(DK <= NT, "one q, k element per thread");
+    const int tq = t < DK ? t : 0;
+    const E qv = q[(size_t)unit * DK + tq];
+    const E kv = k[(size_t)unit * DK + tq];
+    E vr[4];   // (converted after the state loads are issued: a conversion here would wait)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[(size_t)unit * DV + cg * 4 + e]);
-
+    for (int e = 0; e < 4; ++e) vr[e] = v[(size_t)unit * DV + cg * 4 + e];
+    __builtin_amdgcn_sched_barrier(0);   // q, k, v issued ahead of the state loads
     f32x4* Sp = reinterpret_cast<f32x4*>(S + page * DK * DV);
     f32x4 st[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + i * RG) * NCG + cg);
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the staging waits
+    qs[t < DK ? t : DK] = to_f32(qv);
+    ks[t < DK ? t : DK] = to_f32(kv);
+    float vc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vc[e] = to_f32(vr[e]);
+    const float lam = lambda[h];
     __syncthreads();
 
     f32x4 acc = zero4();
