@@ -51,8 +51,25 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     const int hd = bh % H, b = bh / H;
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nc, c_begin + a.seg_chunks);
-    const float lam = a.lambda[hd];
 
+    // The first pass's tiles are requested before anything else (decay tables,
+    // start state, folded local states), which is then set up while they fly.
+    const int tokX = a.sx.t, tokY = a.sy.t;
+    const bf16* xb = static_cast<const bf16*>(a.x) + b * a.sx.b + hd * kDK;
+    const bf16* yb = static_cast<const bf16*>(a.y) + b * a.sy.b + hd * kDV;
+    RowStage<R, kDK, kNT> tx;
+    RowStage<R, kDV, kNT> ty;
+    const int nchunks = c_end - c_begin;
+    auto chunk_of = [&](int ci) { return REV ? c_end - 1 - ci : c_begin + ci; };
+    // pass (ci, sp): tokens c C + sp R .. of chunk c = chunk_of(ci)
+    auto load_pass = [&](int c, int sp, int tid) {
+        const int t = c * C + sp * R;
+        tx.load(xb + (size_t)t * tokX, tokX, T - t, tid);
+        ty.load(yb + (size_t)t * tokY, tokY, T - t, tid);
+    };
+    if (nchunks > 0) load_pass(chunk_of(0), 0, tid);
+
+    const float lam = a.lambda[hd];
     const int ctail = T % C;  // length of a partial last chunk (0: none)
     for (int j = tid; j < C; j += kNT) {
         if constexpr (REV) {
@@ -66,10 +83,6 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
     }
     const float lamC = uniform_f32(pow_int(lam, C));
     const float lamTail = uniform_f32(pow_int(lam, ctail));
-
-    const int tokX = a.sx.t, tokY = a.sy.t;
-    const bf16* xb = static_cast<const bf16*>(a.x) + b * a.sx.b + hd * kDK;
-    const bf16* yb = static_cast<const bf16*>(a.y) + b * a.sy.b + hd * kDV;
 
     // Sacc[i][cb][r] = S[16 (2i + h) + 4g + r][colbase + 16 cb + n]
     f32x4 Sacc[3][kNCB];
@@ -110,17 +123,6 @@ __global__ __launch_bounds__(kNT, 1) void chain_bf16_kernel(StateArgs a) {
         }
     }
 
-    RowStage<R, kDK, kNT> tx;
-    RowStage<R, kDV, kNT> ty;
-    const int nchunks = c_end - c_begin;
-    auto chunk_of = [&](int ci) { return REV ? c_end - 1 - ci : c_begin + ci; };
-    // pass (ci, sp): tokens c C + sp R .. of chunk c = chunk_of(ci)
-    auto load_pass = [&](int c, int sp, int tid) {
-        const int t = c * C + sp * R;
-        tx.load(xb + (size_t)t * tokX, tokX, T - t, tid);
-        ty.load(yb + (size_t)t * tokY, tokY, T - t, tid);
-    };
-    if (nchunks > 0) load_pass(chunk_of(0), 0, tid);
     constexpr int NSP = kDK * (kDV / 8) / kNT;   // snapshot pieces per thread
     static_assert(kDK * (kDV / 8) % kNT == 0, "snapshot pieces per thread");
 
