@@ -261,8 +261,14 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         td.template store<kLDV>(Ds, tid);
         __syncthreads();
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
+        // Waves 4..7 carry about twice the work of waves 0..3 here (a dQ block and a
+        // key block each); with the issue priority of their SIMD they no longer
+        // trail the lighter partner wave into the barrier (the training step at
+        // C = 128 -2.2 us in alternating runs of the two builds).
+        if (wave >= 4) __builtin_amdgcn_s_setprio(1);
         if (wave >= 4) query_block(HALF, wave - 4);
         key_terms(HALF);
+        __builtin_amdgcn_s_setprio(0);
     } else {
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
     }
