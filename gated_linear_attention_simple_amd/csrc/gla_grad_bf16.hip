@@ -247,12 +247,18 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         }
     };
 
-    // A: queries 0 .. HALF-1 (waves past the chunk's key or query blocks idle)
+    // A: queries 0 .. HALF-1 (waves past the chunk's key or query blocks idle).
+    // With one query half (C <= 64) this is the whole intra-chunk work, and the
+    // dQ waves 4..7 get their SIMD's issue priority (the training step -2.3 us at
+    // C = 64, -1.2 at 32 in alternating runs; no gain at 128, not used there).
+    if constexpr (C < 128)
+        if (wave >= 4) __builtin_amdgcn_s_setprio(1);
     if (wave < 4) {
         if (wave < NKB) key_terms(0);
     } else if (wave - 4 < NQB) {
         query_block(0, wave - 4);
     }
+    if constexpr (C < 128) __builtin_amdgcn_s_setprio(0);
     // B: queries 64..127 (Gbar requested for C meanwhile)
     BufStage<kDK, kDV, kFNT> tg;
     if (C > HALF && HALF < ceff) {
