@@ -134,6 +134,13 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         tq.template store<kLDK>(Qs, tid);
         td.template store<kLDV>(Ds, tid);
     }
+    // Gbar: at C = 64 (one query half, one workgroup per CU) requested now, to
+    // arrive during the intra-chunk terms (the training step -7.0 us); at 128 at
+    // the start of the second half; at 32, where two workgroups share a CU and
+    // registers are short, after the intra-chunk terms (+1.7 us if requested now).
+    BufStage<kDK, kDV, kFNT> tg;
+    constexpr bool kGbarEarly = C == 64;
+    if constexpr (kGbarEarly) tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
     // the second half's queries and output gradients, in registers meanwhile
     if (HALF < ceff) {
         tq.load(qb + (size_t)HALF * tokQ, tokQ, ceff - HALF, tid);
@@ -260,7 +267,6 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     }
     if constexpr (C < 128) __builtin_amdgcn_s_setprio(0);
     // B: queries 64..127 (Gbar requested for C meanwhile)
-    BufStage<kDK, kDV, kFNT> tg;
     if (C > HALF && HALF < ceff) {
         __syncthreads();  // half 0 reads are done
         tq.template store<kLDK>(Qs, tid);
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         if (wave >= 4) query_block(HALF, wave - 4);
         key_terms(HALF);
         __builtin_amdgcn_s_setprio(0);
-    } else {
+    } else if constexpr (!kGbarEarly) {
         tg.load(static_cast<const bf16*>(a.gbar) + snap, kDV, kDK, tid);
     }
     // <Gbar, Sbar> (dlam through lam^ceff): this thread's Gbar pieces against
