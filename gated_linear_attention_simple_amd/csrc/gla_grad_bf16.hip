@@ -257,7 +257,8 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
     // A: queries 0 .. HALF-1 (waves past the chunk's key or query blocks idle).
     // With one query half (C <= 64) this is the whole intra-chunk work, and the
     // dQ waves 4..7 get their SIMD's issue priority (the training step -2.3 us at
-    // C = 64, -1.2 at 32 in alternating runs; no gain at 128, not used there).
+    // C = 64, -1.2 at 32 against the same kernel without it; no gain at 128, not
+    // used there).
     if constexpr (C < 128)
         if (wave >= 4) __builtin_amdgcn_s_setprio(1);
     if (wave < 4) {
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         // Waves 4..7 carry about twice the work of waves 0..3 here (a dQ block and a
         // key block each); with the issue priority of their SIMD they no longer
         // trail the lighter partner wave into the barrier (the training step at
-        // C = 128 -2.2 us in alternating runs of the two builds).
+        // C = 128: -2.2 us against the same kernel without it, timed alternately).
         if (wave >= 4) __builtin_amdgcn_s_setprio(1);
         if (wave >= 4) query_block(HALF, wave - 4);
         key_terms(HALF);
