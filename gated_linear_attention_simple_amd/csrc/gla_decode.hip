@@ -59,9 +59,9 @@ __global__ __launch_bounds__((DV / 4) * RG) void decode_kernel(
         page = (size_t)slot * H + h;
     }
 
-    // q and k are requested first and staged once they arrive, while the state
-    // loads issued between them are still in flight (the memory counter is in
-    // order, so the staging waits only for the two loads ahead of the state).
+    // q, k and v are requested first, then the state; q and k are staged once they
+    // arrive while the state loads are still in flight (the memory counter is in
+    // order, so the staging waits only for the loads issued ahead of the state).
     // (Every thread loads an element and stores it, threads past DK the first one
     // into a spare slot, so no branch holds the loads back behind the state's.)
     static_assert(DK <= NT, "one q, k element per thread");

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kFNT, 1) void grad_fused_bf16(GradArgs a) {
         td.template store<kLDV>(Ds, tid);
     }
     // Gbar: at C = 64 (one query half, one workgroup per CU) requested now, to
-    // arrive during the intra-chunk terms (the training step -7.0 us); at 128 at
+    // arrive during the intra-chunk terms (the training step -6.5 us); at 128 at
     // the start of the second half; at 32, where two workgroups share a CU and
     // registers are short, after the intra-chunk terms (+1.7 us if requested now).
     BufStage<kDK, kDV, kFNT> tg;
